@@ -1,0 +1,210 @@
+/*
+ * int8w_oracle.c -- plain, slow CPU oracle for 8-bit affine group-quantized
+ * weight-only linear layers.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library under test links, loads or
+ * calls this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code, header, table or helper with the HIP
+ * path.
+ *
+ * Source: the rustdoc page "MlxInt8Weight" (metrale_gpu_runtime::mlx_int8),
+ * struct description and the field/method sections cited at each function.
+ *
+ * Conventions (each one is a reading of the page; the page gives no formula):
+ *   - packed is uint32 [N, K/4]; code k of row n is byte (k % 4) of word
+ *     packed[n, k/4], little-endian (byte 0 = bits 0..7), unsigned 0..255.
+ *   - scales, biases are BF16 bit patterns [N, K/gs].
+ *   - The weight is affine: w = q * scale + bias, evaluated in fp32
+ *     (one fp32 multiply, one fp32 add; the product is exact because both
+ *     factors carry at most 8 significant bits).
+ *   - dequantize_to rounds that fp32 value to BF16, round-to-nearest-even.
+ *   - Dot products accumulate in fp64, ascending k, one output at a time.
+ *   - silu(g) = g / (1 + exp(-g)), evaluated in fp64.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (no fast-math).
+ * OpenMP splits only the independent output rows; every sum is sequential, so
+ * results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- BF16 <-> fp32, written from the IEEE-754 binary32 / bfloat16 layouts ---- */
+
+/* A BF16 value is the upper 16 bits of a binary32 value; widening is exact. */
+float orc_bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* Round a binary32 value to BF16, nearest, ties to even.  The 16 dropped bits
+ * are compared with one half unit in the last kept place (0x8000); above half
+ * rounds up, below rounds down, exactly half rounds to the even neighbour.  A
+ * carry out of the mantissa moves into the exponent, which is the correct
+ * next representable value (and gives infinity past the largest finite BF16).
+ * NaN stays NaN (quiet bit set, sign kept); infinities pass through. */
+uint16_t orc_f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  uint32_t exp_bits = (u >> 23) & 0xFFu;
+  uint32_t man_bits = u & 0x7FFFFFu;
+  if (exp_bits == 0xFFu && man_bits != 0) return (uint16_t)((u >> 16) | 0x0040u);
+  uint32_t upper = u >> 16;
+  uint32_t dropped = u & 0xFFFFu;
+  if (dropped > 0x8000u || (dropped == 0x8000u && (upper & 1u))) upper += 1u;
+  return (uint16_t)upper;
+}
+
+void orc_f32_to_bf16_rne_array(const uint32_t *in_bits, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) {
+    float f;
+    memcpy(&f, &in_bits[i], sizeof f);
+    out[i] = orc_f32_to_bf16_rne(f);
+  }
+}
+
+/* ---- weight encoding: page "MlxInt8Weight", field sections packed/scales/biases ---- */
+
+/* Code k of one packed row: byte k%4 of word k/4, least significant byte first. */
+static uint32_t code_at(const uint32_t *row_words, int64_t k) {
+  return (row_words[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+}
+
+void orc_unpack(const uint32_t *packed, int64_t n_words, uint8_t *codes) {
+  for (int64_t i = 0; i < n_words; ++i)
+    for (int64_t j = 0; j < 4; ++j) codes[4 * i + j] = (uint8_t)code_at(packed + i, j);
+}
+
+/* fp32 affine value of one weight: q * scale + bias, one fp32 multiply and one
+ * fp32 add (the struct description calls the weight "8-bit affine"; the scales
+ * and biases sections give one BF16 pair per group of group_size codes). */
+static float affine_f32(uint32_t q, uint16_t s_bits, uint16_t b_bits) {
+  float s = orc_bf16_to_f32(s_bits);
+  float b = orc_bf16_to_f32(b_bits);
+  float prod = (float)q * s;
+  float w = prod + b;
+  return w;
+}
+
+/* One full fp32 row of the weight. */
+static void weight_row_f32(const uint32_t *packed, const uint16_t *scales, const uint16_t *biases,
+                           int64_t K, int64_t gs, int64_t n, float *w_row) {
+  const int64_t G = K / gs;
+  const uint32_t *words = packed + n * (K / 4);
+  for (int64_t k = 0; k < K; ++k) {
+    int64_t g = k / gs;
+    w_row[k] = affine_f32(code_at(words, k), scales[n * G + g], biases[n * G + g]);
+  }
+}
+
+/* All fp32 affine weights [N, K]. */
+void orc_weight_f32(const uint32_t *packed, const uint16_t *scales, const uint16_t *biases,
+                    int64_t N, int64_t K, int64_t gs, float *w32) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) weight_row_f32(packed, scales, biases, K, gs, n, w32 + n * K);
+}
+
+/* dequantize_to: the full weight as BF16, row-major [N, K]
+ * (page "MlxInt8Weight", method dequantize_to). */
+void orc_dequantize_to(const uint32_t *packed, const uint16_t *scales, const uint16_t *biases,
+                       int64_t N, int64_t K, int64_t gs, uint16_t *out) {
+#pragma omp parallel
+  {
+    float *w_row = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+      weight_row_f32(packed, scales, biases, K, gs, n, w_row);
+      for (int64_t k = 0; k < K; ++k) out[n * K + k] = orc_f32_to_bf16_rne(w_row[k]);
+    }
+    free(w_row);
+  }
+}
+
+/* ---- products: page "MlxInt8Weight", methods gemv, gemv_silu_gate(_resid), gemm ---- */
+
+/* Y[i, n] = sum_k w[n, k] * a[i, k] for fp64 activations a [m, K]; also
+ * Aabs[i, n] = sum_k |w[n, k] * a[i, k]|.  Sums run in ascending k in fp64. */
+void orc_matmul_act_f64(const uint32_t *packed, const uint16_t *scales, const uint16_t *biases,
+                        int64_t N, int64_t K, int64_t gs, const double *a, int64_t m, double *Y,
+                        double *Aabs) {
+#pragma omp parallel
+  {
+    float *w_row = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+      weight_row_f32(packed, scales, biases, K, gs, n, w_row);
+      for (int64_t i = 0; i < m; ++i) {
+        const double *ai = a + i * K;
+        double sum = 0.0, sum_abs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          double t = (double)w_row[k] * ai[k];
+          sum += t;
+          sum_abs += fabs(t);
+        }
+        Y[i * N + n] = sum;
+        if (Aabs) Aabs[i * N + n] = sum_abs;
+      }
+    }
+    free(w_row);
+  }
+}
+
+/* gemm: Y = X W^T with X BF16 [m, K] (method gemm). */
+void orc_gemm(const uint32_t *packed, const uint16_t *scales, const uint16_t *biases, int64_t N,
+              int64_t K, int64_t gs, const uint16_t *X, int64_t m, double *Y, double *Aabs) {
+  double *a = (double *)malloc((size_t)(m * K > 0 ? m * K : 1) * sizeof(double));
+  for (int64_t j = 0; j < m * K; ++j) a[j] = (double)orc_bf16_to_f32(X[j]);
+  orc_matmul_act_f64(packed, scales, biases, N, K, gs, a, m, Y, Aabs);
+  free(a);
+}
+
+/* gemv: y = W x with x BF16 [K] (method gemv). */
+void orc_gemv(const uint32_t *packed, const uint16_t *scales, const uint16_t *biases, int64_t N,
+              int64_t K, int64_t gs, const uint16_t *x, double *y, double *Aabs) {
+  orc_gemm(packed, scales, biases, N, K, gs, x, 1, y, Aabs);
+}
+
+/* silu(g) = g * sigmoid(g) = g / (1 + exp(-g)), fp64.  For g -> -inf the
+ * quotient tends to -0, which is the limit of silu there. */
+static double silu_f64(double g) { return g / (1.0 + exp(-g)); }
+
+/* The gated activation silu(gate[k]) * up[k], fp64, never rounded to BF16
+ * (method gemv_silu_gate: the product is not written out). */
+void orc_silu_gate_act(const uint16_t *gate, const uint16_t *up, int64_t K, double *a) {
+  for (int64_t k = 0; k < K; ++k)
+    a[k] = silu_f64((double)orc_bf16_to_f32(gate[k])) * (double)orc_bf16_to_f32(up[k]);
+}
+
+/* gemv_silu_gate: y = W (silu(gate) * up). */
+void orc_gemv_silu_gate(const uint32_t *packed, const uint16_t *scales, const uint16_t *biases,
+                        int64_t N, int64_t K, int64_t gs, const uint16_t *gate, const uint16_t *up,
+                        double *y, double *Aabs) {
+  double *a = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+  orc_silu_gate_act(gate, up, K, a);
+  orc_matmul_act_f64(packed, scales, biases, N, K, gs, a, 1, y, Aabs);
+  free(a);
+}
+
+/* gemv_silu_gate_resid: y[n] = x_resid[n] + sum_k W[n,k] (silu(gate[k]) up[k]).
+ * Aabs excludes the residual term. */
+void orc_gemv_silu_gate_resid(const uint32_t *packed, const uint16_t *scales,
+                              const uint16_t *biases, int64_t N, int64_t K, int64_t gs,
+                              const uint16_t *gate, const uint16_t *up, const uint16_t *x_resid,
+                              double *y, double *Aabs) {
+  orc_gemv_silu_gate(packed, scales, biases, N, K, gs, gate, up, y, Aabs);
+  for (int64_t n = 0; n < N; ++n) y[n] = (double)orc_bf16_to_f32(x_resid[n]) + y[n];
+}
+
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,434 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each test ties one oracle function to a library routine (torch's BF16
+conversion and silu), to exact rational arithmetic (fractions.Fraction), to a
+closed form or invariant, or to a hand-computed example stored under
+tests/golden/.  The functions follow the rustdoc page "MlxInt8Weight"
+(metrale_gpu_runtime::mlx_int8): struct description, the packed / scales /
+biases field sections and the methods dequantize_to, gemv, gemv_silu_gate,
+gemv_silu_gate_resid and gemm.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from weight_only_quantized_int8_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers (test side)
+
+def frac_of_bf16(bits: int) -> Fraction:
+    """Exact value of a finite BF16 bit pattern, from the binary16-brain layout."""
+    sign = -1 if bits & 0x8000 else 1
+    e = (bits >> 7) & 0xFF
+    m = bits & 0x7F
+    assert e != 0xFF
+    if e == 0:
+        return sign * Fraction(m, 1 << 7) * Fraction(1, 1 << 126)
+    return sign * (1 + Fraction(m, 128)) * (Fraction(2) ** (e - 127))
+
+
+def frac_of_f32(bits: int) -> Fraction:
+    sign = -1 if bits & 0x80000000 else 1
+    e = (bits >> 23) & 0xFF
+    m = bits & 0x7FFFFF
+    assert e != 0xFF
+    if e == 0:
+        return sign * Fraction(m, 1 << 23) * Fraction(1, 1 << 126)
+    return sign * (1 + Fraction(m, 1 << 23)) * (Fraction(2) ** (e - 127))
+
+
+def rne_bf16_of_fraction(v: Fraction, negative_zero: bool = False) -> int:
+    """Nearest BF16 to an exact rational, ties to the even significand."""
+    if v == 0:
+        return 0x8000 if negative_zero else 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1)
+    if e < -126:  # subnormal range: fixed spacing 2^-133
+        ulp = Fraction(1, 1 << 133)
+        base = 0
+    else:
+        ulp = Fraction(2) ** (e - 7)
+        base = ((e + 127) << 7) - 128
+    m = a / ulp
+    lo = m.numerator // m.denominator
+    rem = m - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo & 1):
+        lo += 1
+    bits = base + lo
+    if bits >= 0x7F80:
+        bits = 0x7F80
+    return sign | bits
+
+
+def load_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def weight_from_codes(codes: np.ndarray, s_bits: np.ndarray, b_bits: np.ndarray):
+    """Pack uint8 codes [N,K] little-endian into uint32 words (test-side, NumPy view)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    N, K = codes.shape
+    packed = codes.view("<u4").reshape(N, K // 4).astype(np.uint32)
+    return packed, np.asarray(s_bits, dtype=np.uint16), np.asarray(b_bits, dtype=np.uint16)
+
+
+def config_weight(seed, N, K, gs):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = synth.gen_weight(rng, N, K, gs)
+    return w, rng
+
+
+# ---------------------------------------------------------------- BF16 conversion
+
+def test_bf16_widen_matches_torch():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    got = oracle.bf16_to_f32(bits)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    for b in (0x3F80, 0xC100, 0x3BA4, 0x0001, 0x8080):
+        assert Fraction(float(oracle._load().orc_bf16_to_f32(b))) == frac_of_bf16(b)
+
+
+@pytest.mark.slow
+def test_rne_exhaustive_against_torch():
+    """Every one of the 2^32 fp32 bit patterns: oracle RNE == torch's CPU RNE (NaN: both NaN, sign kept)."""
+    chunk = 1 << 26
+    for start in range(0, 1 << 32, chunk):
+        u = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+        got = oracle.f32_to_bf16(u.view(np.float32))
+        ref = torch.from_numpy(u.view(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        is_nan = ((u >> 23) & 0xFF == 0xFF) & (u & 0x7FFFFF != 0)
+        ok = (got == ref) | is_nan
+        assert ok.all(), f"first mismatch at 0x{int(u[~ok][0]):08X}"
+        g_nan = got[is_nan]
+        assert ((g_nan & 0x7F80) == 0x7F80).all() and ((g_nan & 0x7F) != 0).all()
+        assert np.array_equal(g_nan & 0x8000, (u[is_nan] >> 16).astype(np.uint16) & 0x8000)
+
+
+def test_rne_against_exact_rationals():
+    """Random finite fp32 patterns and constructed ties: oracle RNE == nearest-even by Fraction."""
+    rng = np.random.default_rng(7)
+    u = rng.integers(0, 1 << 32, size=4000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 1 << 16, size=2000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    u = np.concatenate([u, ties, np.array([0x7F7FFFFF, 0x7F7F8000, 0x00008000, 0x80018000], np.uint32)])
+    u = u[((u >> 23) & 0xFF) != 0xFF]
+    got = oracle.f32_to_bf16(u.view(np.float32))
+    for bits, g in zip(u.tolist(), got.tolist()):
+        want = rne_bf16_of_fraction(frac_of_f32(bits), negative_zero=bool(bits & 0x80000000))
+        assert g == want, f"f32 0x{bits:08X}: oracle 0x{g:04X}, exact nearest-even 0x{want:04X}"
+
+
+# ---------------------------------------------------------------- unpacking
+
+def test_unpack_byte_order():
+    codes = oracle.unpack(np.array([0x04030201, 0xFF00807F], dtype=np.uint32))
+    assert codes.tolist() == [1, 2, 3, 4, 127, 128, 0, 255]
+
+
+def test_unpack_matches_numpy_little_endian_view():
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 256, size=(8, 64), dtype=np.uint8)
+    packed = codes.view("<u4")
+    assert np.array_equal(oracle.unpack(packed), codes)
+
+
+# ---------------------------------------------------------------- affine dequantization
+
+def test_dequant_golden_examples():
+    for s_hex, b_hex, q, want_hex, *_ in load_table("dequant_examples.txt"):
+        s, b, q, want = int(s_hex, 16), int(b_hex, 16), int(q), int(want_hex, 16)
+        exact = q * frac_of_bf16(s) + frac_of_bf16(b)
+        assert rne_bf16_of_fraction(exact) == want, "fixture row disagrees with exact arithmetic"
+        codes = np.full((1, 32), q, dtype=np.uint8)
+        packed, sc, bi = weight_from_codes(codes, [[s]], [[b]])
+        out = oracle.dequantize_to(packed, sc, bi, 32)
+        assert (out == want).all(), f"q={q}: oracle 0x{int(out[0, 0]):04X}, want 0x{want:04X}"
+
+
+def test_dequant_endpoints_bias_and_full_scale():
+    """q=0 gives the bias exactly; q=255 gives RNE(255*scale + bias)."""
+    w, _ = config_weight(11, 16, 256, 64)
+    codes = np.zeros((16, 256), np.uint8)
+    codes[:, 128:] = 255
+    packed, sc, bi = weight_from_codes(codes, w.scales, w.biases)
+    out = oracle.dequantize_to(packed, sc, bi, 64)
+    for n in range(16):
+        for g in range(4):
+            s, b = int(w.scales[n, g]), int(w.biases[n, g])
+            blk = out[n, g * 64:(g + 1) * 64]
+            if g < 2:
+                assert (blk == b).all()
+            else:
+                assert (blk == rne_bf16_of_fraction(255 * frac_of_bf16(s) + frac_of_bf16(b))).all()
+
+
+def test_affine_fp32_is_exact_under_workload_distribution():
+    """For workload-distributed (scale, bias) and all 256 codes the fp32 affine value is the exact rational."""
+    # Exact rationals on a small set ...
+    w, _ = config_weight(5, 48, 256, 64)
+    codes = np.tile(np.arange(256, dtype=np.uint8), (48, 1))
+    sc = np.repeat(w.scales[:, :1], 4, axis=1)
+    bi = np.repeat(w.biases[:, :1], 4, axis=1)
+    packed, sc, bi = weight_from_codes(codes, sc, bi)
+    w32 = oracle.weight_f32(packed, sc, bi, 64)
+    for n in range(48):
+        s, b = frac_of_bf16(int(sc[n, 0])), frac_of_bf16(int(bi[n, 0]))
+        for q in range(256):
+            assert Fraction(float(w32[n, q])) == q * s + b
+    # ... and an error-free transformation (TwoSum) on 10^4 random (scale, bias) pairs.
+    R = 10000
+    w, _ = config_weight(6, R, 64, 64)
+    codes = np.tile(np.arange(256, dtype=np.uint8), (R, 1))
+    sc = np.repeat(w.scales[:, :1], 4, axis=1)
+    bi = np.repeat(w.biases[:, :1], 4, axis=1)
+    packed, sc, bi = weight_from_codes(codes, sc, bi)
+    w32 = oracle.weight_f32(packed, sc, bi, 64).astype(np.float64)
+    p = np.arange(256, dtype=np.float64)[None, :] * oracle.bf16_to_f32(sc[:, :1]).astype(np.float64)
+    b = np.broadcast_to(oracle.bf16_to_f32(bi[:, :1]).astype(np.float64), p.shape)
+    s = p + b
+    bv = s - p
+    err = (p - (s - bv)) + (b - bv)  # TwoSum: s + err == p + b exactly
+    assert (err == 0).all() and (s == w32).all()
+
+
+def test_dequant_random_against_exact_rationals():
+    w, _ = config_weight(21, 6, 128, 32)
+    out = oracle.dequantize_to(w.packed, w.scales, w.biases, 32)
+    codes = w.packed.view(np.uint8).reshape(6, 128)
+    for n in range(6):
+        for k in range(128):
+            g = k // 32
+            exact = int(codes[n, k]) * frac_of_bf16(int(w.scales[n, g])) + frac_of_bf16(int(w.biases[n, g]))
+            assert int(out[n, k]) == rne_bf16_of_fraction(exact)
+
+
+def test_dequant_group_index_uses_group_size():
+    """Per-group parameters apply to exactly group_size consecutive codes, row by row."""
+    N, K, gs = 3, 256, 64
+    codes = np.full((N, K), 1, np.uint8)
+    sc = np.zeros((N, K // gs), np.uint16)
+    bi = np.zeros((N, K // gs), np.uint16)
+    for n in range(N):
+        for g in range(K // gs):
+            sc[n, g] = 0x3F80  # 1.0
+            bi[n, g] = int(rne_bf16_of_fraction(Fraction(10 * n + g)))
+    packed, sc, bi = weight_from_codes(codes, sc, bi)
+    w32 = oracle.weight_f32(packed, sc, bi, gs)
+    for n in range(N):
+        for k in range(K):
+            assert w32[n, k] == 1 + 10 * n + k // gs
+
+
+# ---------------------------------------------------------------- gemv
+
+def test_gemv_golden_436():
+    (_, _, y_exact, _, y_bf16), = [r for r in load_table("product_examples.txt") if r[0] == "gemv_436"]
+    codes = np.arange(64, dtype=np.uint8)[None, :]
+    packed, sc, bi = weight_from_codes(codes, [[0x3F00, 0x3E80]], [[0xC100, 0x4000]])
+    y, A = oracle.gemv(packed, sc, bi, 32, np.full(64, 0x3F80, np.uint16))
+    assert y[0] == float(y_exact)
+    assert rne_bf16_of_fraction(Fraction(y[0])) == int(y_bf16, 16)
+
+
+def test_gemv_identity_reproduces_x():
+    K = 64
+    codes = np.full((K, K), 128, np.uint8)
+    np.fill_diagonal(codes, 129)
+    packed, sc, bi = weight_from_codes(codes, np.full((K, 2), 0x3F80), np.full((K, 2), 0xC300))
+    rng = np.random.default_rng(1)
+    x = synth.gen_act(rng, K)
+    y, A = oracle.gemv(packed, sc, bi, 32, x)
+    assert np.array_equal(y, oracle.bf16_to_f32(x).astype(np.float64))
+    assert np.array_equal(oracle.f32_to_bf16(y.astype(np.float32)), x)
+
+
+@pytest.mark.parametrize("c", [0, 77, 255])
+def test_gemv_closed_form_constant_codes(c):
+    """All codes equal c: y[n] = sum_g (c*s_g + b_g) * sum_{k in g} x_k."""
+    N, K, gs = 5, 256, 64
+    w, rng = config_weight(31 + c, N, K, gs)
+    packed, sc, bi = weight_from_codes(np.full((N, K), c, np.uint8), w.scales, w.biases)
+    x = synth.gen_act(rng, K)
+    y, _ = oracle.gemv(packed, sc, bi, gs, x)
+    xs = [frac_of_bf16(int(v)) for v in x]
+    for n in range(N):
+        want = Fraction(0)
+        for g in range(K // gs):
+            wg = c * frac_of_bf16(int(sc[n, g])) + frac_of_bf16(int(bi[n, g]))
+            want += wg * sum(xs[g * gs:(g + 1) * gs], Fraction(0))
+        assert abs(Fraction(y[n]) - want) <= abs(want) * Fraction(1, 10**12) + Fraction(1, 10**12)
+
+
+def test_gemv_linearity():
+    N, K, gs = 32, 512, 64
+    w, rng = config_weight(41, N, K, gs)
+    x1 = oracle.bf16_to_f32(synth.gen_act(rng, K)).astype(np.float64)
+    x2 = oracle.bf16_to_f32(synth.gen_act(rng, K)).astype(np.float64)
+    y1, A1 = oracle.matmul_act(w.packed, w.scales, w.biases, gs, x1)
+    y2, A2 = oracle.matmul_act(w.packed, w.scales, w.biases, gs, x2)
+    y3, _ = oracle.matmul_act(w.packed, w.scales, w.biases, gs, 2.0 * x1 - 3.0 * x2)
+    assert np.allclose(y3, 2.0 * y1 - 3.0 * y2, rtol=0, atol=1e-12 * (2 * A1 + 3 * A2).max())
+
+
+def test_gemv_bruteforce_exact():
+    for N, K, gs in [(1, 32, 32), (3, 64, 32), (4, 128, 64), (2, 128, 128)]:
+        w, rng = config_weight(100 + K + N, N, K, gs)
+        x = synth.gen_act(rng, K)
+        y, A = oracle.gemv(w.packed, w.scales, w.biases, gs, x)
+        codes = w.packed.view(np.uint8).reshape(N, K)
+        for n in range(N):
+            exact = Fraction(0)
+            exact_abs = Fraction(0)
+            for k in range(K):
+                g = k // gs
+                wk = int(codes[n, k]) * frac_of_bf16(int(w.scales[n, g])) + frac_of_bf16(int(w.biases[n, g]))
+                t = wk * frac_of_bf16(int(x[k]))
+                exact += t
+                exact_abs += abs(t)
+            assert abs(Fraction(y[n]) - exact) <= exact_abs * Fraction(1, 10**13)
+            assert abs(Fraction(A[n]) - exact_abs) <= exact_abs * Fraction(1, 10**13)
+
+
+# ---------------------------------------------------------------- gemm
+
+def test_gemm_m1_equals_gemv_and_rows_independent():
+    N, K, gs = 24, 256, 64
+    w, rng = config_weight(51, N, K, gs)
+    X = synth.gen_act(rng, (5, K))
+    Y, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
+    for i in range(5):
+        y, a = oracle.gemv(w.packed, w.scales, w.biases, gs, X[i])
+        assert np.array_equal(Y[i], y) and np.array_equal(A[i], a)
+    perm = np.array([3, 0, 4, 1, 2])
+    Yp, _ = oracle.gemm(w.packed, w.scales, w.biases, gs, X[perm])
+    assert np.array_equal(Yp, Y[perm])
+
+
+def test_gemm_one_hot_rows_give_weight_columns():
+    """X[i] = e_j: Y[i, :] is column j of the fp32 weight, and its BF16 rounding is column j of dequantize_to."""
+    N, K, gs = 16, 128, 32
+    w, _ = config_weight(61, N, K, gs)
+    cols = [0, 1, 31, 32, 77, 127]
+    X = np.zeros((len(cols), K), np.uint16)
+    for i, j in enumerate(cols):
+        X[i, j] = 0x3F80
+    Y, _ = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
+    deq = oracle.dequantize_to(w.packed, w.scales, w.biases, gs)
+    codes = w.packed.view(np.uint8).reshape(N, K)
+    for i, j in enumerate(cols):
+        assert np.array_equal(oracle.f32_to_bf16(Y[i].astype(np.float32)), deq[:, j])
+        for n in range(N):
+            g = j // gs
+            assert Fraction(Y[i, n]) == int(codes[n, j]) * frac_of_bf16(int(w.scales[n, g])) + frac_of_bf16(
+                int(w.biases[n, g]))
+
+
+def test_gemm_empty_m():
+    w, _ = config_weight(62, 8, 64, 32)
+    Y, A = oracle.gemm(w.packed, w.scales, w.biases, 32, np.zeros((0, 64), np.uint16))
+    assert Y.shape == (0, 8)
+
+
+# ---------------------------------------------------------------- silu gate (+ residual)
+
+def test_silu_gate_act_against_torch_silu():
+    rng = np.random.default_rng(9)
+    g = synth.gen_act(rng, 4096)
+    g[:6] = [0x0000, 0x8000, 0x41A0, 0xC1A0, 0x4479, 0xC479]  # 0, -0, 20, -20, 996, -996
+    u = synth.gen_act(rng, 4096)
+    a = oracle.silu_gate_act(g, u)
+    gt = torch.from_numpy(oracle.bf16_to_f32(g).astype(np.float64))
+    ut = torch.from_numpy(oracle.bf16_to_f32(u).astype(np.float64))
+    ref = (torch.nn.functional.silu(gt) * ut).numpy()
+    assert np.allclose(a, ref, rtol=1e-14, atol=1e-300)
+
+
+def test_silu_odd_part_identity():
+    """silu(g) - silu(-g) = g for every g (sigmoid(g) + sigmoid(-g) = 1); silu(0) = 0."""
+    rng = np.random.default_rng(10)
+    g = synth.gen_act(rng, 2048)
+    ones = np.full(2048, 0x3F80, np.uint16)
+    a_pos = oracle.silu_gate_act(g, ones)
+    a_neg = oracle.silu_gate_act(g ^ np.uint16(0x8000), ones)
+    gv = oracle.bf16_to_f32(g).astype(np.float64)
+    assert np.allclose(a_pos - a_neg, gv, rtol=1e-14, atol=1e-15)
+    assert oracle.silu_gate_act(np.zeros(1, np.uint16), ones[:1])[0] == 0.0
+
+
+def test_silu_gate_golden_examples():
+    table = {r[0]: r for r in load_table("product_examples.txt")}
+    codes = np.full((1, 32), 129, np.uint8)
+    packed, sc, bi = weight_from_codes(codes, [[0x3F80]], [[0xC300]])
+    one = np.full(32, 0x3F80, np.uint16)
+    y, _ = oracle.gemv_silu_gate(packed, sc, bi, 32, one, one)
+    _, _, approx, _, hexv = table["silu_32"]
+    assert abs(y[0] - float(approx)) < 1e-8
+    assert rne_bf16_of_fraction(Fraction(y[0])) == int(hexv, 16)
+    y, _ = oracle.gemv_silu_gate_resid(packed, sc, bi, 32, one, one, np.array([0x3F80], np.uint16))
+    _, _, approx, _, hexv = table["silu_resid_32"]
+    assert abs(y[0] - float(approx)) < 1e-8
+    assert rne_bf16_of_fraction(Fraction(y[0])) == int(hexv, 16)
+
+
+def test_silu_gate_zero_gate_or_up_gives_zero_and_resid_passthrough():
+    N, K, gs = 64, 512, 64
+    w, rng = config_weight(71, N, K, gs)
+    g = synth.gen_act(rng, K)
+    u = synth.gen_act(rng, K)
+    r = synth.gen_act(rng, N)
+    z = np.zeros(K, np.uint16)
+    assert (oracle.gemv_silu_gate(w.packed, w.scales, w.biases, gs, z, u)[0] == 0).all()
+    assert (oracle.gemv_silu_gate(w.packed, w.scales, w.biases, gs, g, z)[0] == 0).all()
+    y, _ = oracle.gemv_silu_gate_resid(w.packed, w.scales, w.biases, gs, z, u, r)
+    assert np.array_equal(oracle.f32_to_bf16(y.astype(np.float32)), r)
+
+
+def test_silu_gate_equals_gemv_of_gated_activation_and_resid_adds_once():
+    N, K, gs = 32, 256, 32
+    w, rng = config_weight(81, N, K, gs)
+    g = synth.gen_act(rng, K)
+    u = synth.gen_act(rng, K)
+    r = synth.gen_act(rng, N)
+    gt = torch.from_numpy(oracle.bf16_to_f32(g).astype(np.float64))
+    ut = torch.from_numpy(oracle.bf16_to_f32(u).astype(np.float64))
+    a_lib = (torch.nn.functional.silu(gt) * ut).numpy()
+    y_ref, A_ref = oracle.matmul_act(w.packed, w.scales, w.biases, gs, a_lib)
+    y, A = oracle.gemv_silu_gate(w.packed, w.scales, w.biases, gs, g, u)
+    assert np.allclose(y, y_ref[0], rtol=1e-13, atol=1e-13 * A.max())
+    yr, Ar = oracle.gemv_silu_gate_resid(w.packed, w.scales, w.biases, gs, g, u, r)
+    assert np.allclose(yr - oracle.bf16_to_f32(r), y, rtol=0, atol=1e-13 * A.max())
+    assert np.array_equal(Ar, A)
+
+
+# ---------------------------------------------------------------- acceptance rule
+
+def test_tolerance_accepts_rounded_oracle_and_rejects_perturbed():
+    N, K, gs = 128, 1024, 64
+    w, rng = config_weight(91, N, K, gs)
+    x = synth.gen_act(rng, K)
+    y, A = oracle.gemv(w.packed, w.scales, w.biases, gs, x)
+    yb = oracle.f32_to_bf16(y.astype(np.float32))
+    assert oracle.within_tolerance(yb, y, A).all()
+    bad = oracle.f32_to_bf16((y + 0.05 * A).astype(np.float32))
+    assert not oracle.within_tolerance(bad, y, A).any()
+    nan = yb.copy()
+    nan[3] = 0x7FC0
+    assert not oracle.within_tolerance(nan, y, A)[3]

@@ -1,0 +1,71 @@
+"""Seeded synthetic inputs for the 8-bit affine weight-only linear layers.
+
+This module draws random numbers and rounds them to BF16 with torch's own CPU
+conversion; it holds none of the layers' arithmetic (no unpacking, no affine
+dequantization, no products).  Both the CPU oracle's tests and the GPU path's
+tests and benchmark take their inputs from here, so the two sides see the same
+bytes.
+
+Value distributions (the decode/prefill workloads of these layers):
+  codes   uint8 uniform on [0, 255], packed 4 per uint32, code k in byte k%4;
+  scales  BF16 of fp32 uniform[0.002, 0.01];
+  biases  BF16 of fp32 (-128 * scale_bf16 * (1 + U(-0.05, 0.05)));
+  x, gate, up, x_resid: BF16 of fp32 N(0, 1).
+Generator: NumPy PCG64, seed = 1000 * workload_index + shape_index, draws in
+the fixed order codes, scales, bias jitter, then activations.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+
+def to_bf16_bits(values_f32: np.ndarray) -> np.ndarray:
+    """fp32 -> BF16 bit patterns (uint16) via torch's CPU round-to-nearest-even."""
+    t = torch.from_numpy(np.ascontiguousarray(values_f32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+@dataclass
+class WeightArrays:
+    packed: np.ndarray   # uint32 [N, K/4]
+    scales: np.ndarray   # uint16 (BF16 bits) [N, K/gs]
+    biases: np.ndarray   # uint16 (BF16 bits) [N, K/gs]
+    out_features: int
+    in_features: int
+    group_size: int
+
+
+def make_seed(workload_index: int, shape_index: int) -> int:
+    return 1000 * int(workload_index) + int(shape_index)
+
+
+def gen_weight(rng: np.random.Generator, N: int, K: int, group_size: int) -> WeightArrays:
+    if K % 4 or K % group_size:
+        raise ValueError("in_features must be a multiple of 4 and of group_size")
+    G = K // group_size
+    codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    packed = np.ascontiguousarray(codes).view("<u4").reshape(N, K // 4).astype(np.uint32, copy=False)
+    s32 = rng.uniform(0.002, 0.01, size=(N, G)).astype(np.float32)
+    scales = to_bf16_bits(s32)
+    jitter = rng.uniform(-0.05, 0.05, size=(N, G)).astype(np.float32)
+    s_back = torch.from_numpy(scales.view(np.int16)).view(torch.bfloat16).float().numpy()
+    b32 = (np.float32(-128.0) * s_back * (np.float32(1.0) + jitter)).astype(np.float32)
+    biases = to_bf16_bits(b32)
+    return WeightArrays(packed, scales, biases, N, K, group_size)
+
+
+def gen_act(rng: np.random.Generator, shape) -> np.ndarray:
+    """BF16 bits of N(0,1) samples."""
+    return to_bf16_bits(rng.standard_normal(size=shape).astype(np.float32))
+
+
+def gen_case(workload_index: int, shape_index: int, N: int, K: int, group_size: int,
+             act_shapes: dict[str, tuple]) -> tuple[WeightArrays, dict[str, np.ndarray]]:
+    """One weight plus named activations, in the fixed draw order."""
+    rng = np.random.Generator(np.random.PCG64(make_seed(workload_index, shape_index)))
+    w = gen_weight(rng, N, K, group_size)
+    acts = {name: gen_act(rng, shape) for name, shape in act_shapes.items()}
+    return w, acts
