@@ -1,0 +1,119 @@
+/*
+ * int8w.h -- C-ABI of the MI355X (gfx950) library for 8-bit affine
+ * group-quantized weight-only linear layers (libint8w.so).
+ *
+ * Source of the operations: the rustdoc page "MlxInt8Weight"
+ * (metrale_gpu_runtime::mlx_int8): the struct description (one "8-bit affine"
+ * linear weight resident on the GPU, no Drop), the field sections packed /
+ * scales / biases, and the methods load (validation rules), dequantize_to,
+ * gemv, gemv_silu_gate, gemv_silu_gate_resid, gemm and release (ownership).
+ *
+ * Weight encoding (the page's field sections; byte order, signedness and the
+ * dequantization formula are this library's readings of them):
+ *   packed  uint32 [out_features, in_features/4], row-major; code k of row n
+ *           is byte (k % 4) of word packed[n*in_features/4 + k/4], least
+ *           significant byte first; codes are unsigned, 0..255.
+ *   scales  BF16 bit patterns [out_features, in_features/group_size], row-major.
+ *   biases  BF16 bit patterns, same shape.
+ *   w[n,k]  = q[n,k] * scales[n, k/group_size] + biases[n, k/group_size],
+ *           an fp32 value (the product is exact, the sum rounds once).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is a DEVICE pointer (HIP global memory); BF16 data are
+ *     passed as uint16_t bit patterns.
+ *   - The library never allocates, frees or retains caller memory.  All
+ *     buffers are borrowed for the duration of the queued GPU work; the caller
+ *     owns them and frees them once (the page's release method).
+ *   - `stream` is a hipStream_t cast to uint64_t (0 = the null stream).  Calls
+ *     validate on the host, enqueue the kernel(s) and return without waiting.
+ *     Faults during execution surface at the caller's next synchronisation.
+ *   - Return value: INT8W_OK, or a negative INT8W_ERR_* code; on any error
+ *     nothing has been enqueued, and int8w_last_error() describes it.
+ *   - Alignment: packed, x, gate, up, X and the dequantize_to output must be
+ *     16-byte aligned; scales, biases, y, x_resid and Y 2-byte aligned.
+ *   - Outputs must not overlap any input, except y == x_resid exactly
+ *     (in-place residual: each output element reads only its own residual).
+ *   - Results are deterministic: the same call on the same data gives the
+ *     same bits (no atomics in any reduction).
+ *   - The library is stateless and re-entrant apart from the thread-local
+ *     last-error string.
+ */
+#ifndef INT8W_H
+#define INT8W_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A borrowed view of one quantized weight (the page's MlxInt8Weight struct). */
+typedef struct int8w_weight {
+  const uint32_t *packed; /* [out_features, in_features/4] code words (device) */
+  const uint16_t *scales; /* [out_features, in_features/group_size] BF16 (device) */
+  const uint16_t *biases; /* [out_features, in_features/group_size] BF16 (device) */
+  uint32_t out_features;  /* N >= 1 */
+  uint32_t in_features;   /* K >= group_size, K % group_size == 0 */
+  uint32_t group_size;    /* 32, 64 or 128 */
+} int8w_weight;
+
+enum {
+  INT8W_OK = 0,
+  INT8W_ERR_NULL = -1,        /* a required pointer is NULL */
+  INT8W_ERR_SHAPE = -2,       /* zero dimension, in_features % group_size != 0, size overflow */
+  INT8W_ERR_UNSUPPORTED = -3, /* group_size not in {32, 64, 128} */
+  INT8W_ERR_ALIGN = -4,       /* a pointer violates the alignment rule above */
+  INT8W_ERR_ALIAS = -5,       /* an output overlaps an input */
+  INT8W_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+};
+
+/* Check a weight view the way the page's load method checks its tensors: all
+ * three buffers present, in_features divisible by group_size (hence by 4, the
+ * codes per word), the per-group shape implied.  Also checks group_size is
+ * supported and the pointers are aligned.  Touches no device memory. */
+int int8w_validate(const int8w_weight *w);
+
+/* Bytes of the quantized storage: N*K codes + 2*2*N*(K/group_size) for the
+ * BF16 scales and biases; 0 for an invalid shape. */
+uint64_t int8w_storage_bytes(uint32_t out_features, uint32_t in_features, uint32_t group_size);
+
+/* dequantize_to: write the full dequantised weight as BF16 to `out`, row-major
+ * [out_features, in_features]; out[n*K + k] = RNE_bf16(w[n,k]) (round to
+ * nearest, ties to even).  `out` must hold out_features*in_features*2 bytes;
+ * exactly that many are written. */
+int int8_dequantize_to(const int8w_weight *w, uint16_t *out, uint64_t stream);
+
+/* gemv: y = W x.  x is BF16 [in_features]; y is BF16 with at least
+ * out_features elements, of which exactly out_features are written:
+ * y[n] = RNE_bf16(sum_k w[n,k] * x[k]), accumulated in fp32. */
+int int8_gemv(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint64_t stream);
+
+/* gemv_silu_gate: y = W (silu(gate) * up) in one launch, silu(g) = g/(1+e^-g).
+ * gate and up are BF16 [in_features]; the product silu(gate)*up is formed in
+ * fp32 on chip and never written to memory.  y as for int8_gemv. */
+int int8_gemv_silu_gate(const int8w_weight *w, const uint16_t *gate, const uint16_t *up, uint16_t *y,
+                        uint64_t stream);
+
+/* gemv_silu_gate_resid: the above plus a residual, in one launch:
+ * y[n] = RNE_bf16(x_resid[n] + sum_k w[n,k] * silu(gate[k]) * up[k]), the
+ * residual added in fp32 before the single rounding.  x_resid is BF16
+ * [out_features]; y may be x_resid itself. */
+int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const uint16_t *up,
+                              const uint16_t *x_resid, uint16_t *y, uint64_t stream);
+
+/* gemm: Y = X W^T.  X is BF16 [m, in_features] and Y BF16 [m, out_features],
+ * both contiguous row-major.  Y[i,n] = RNE_bf16(sum_k w[n,k] * X[i,k]) with fp32
+ * accumulation; for m > 64 the weight enters the matrix cores as
+ * RNE_bf16(w[n,k]) (the dequantize_to value).  m == 0 enqueues nothing and
+ * returns INT8W_OK. */
+int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, uint64_t stream);
+
+/* Human-readable description of the calling thread's most recent error
+ * ("" if none).  The pointer stays valid until the thread's next call. */
+const char *int8w_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT8W_H */

@@ -1,0 +1,159 @@
+"""The C-ABI boundary on the CPU: the library loads, exports what include/int8w.h
+declares, and rejects every invalid call before launching anything.
+
+No test here passes a call that validates (it would launch a kernel); each
+one checks a status code and the last-error text.  Rules follow the rustdoc
+page "MlxInt8Weight", method load (2-D U32 weight, BF16 scales/biases of
+shape [out_features, in_features/group_size], group_size divides
+in_features) plus the library's own alignment and aliasing rules.
+"""
+import os
+import re
+
+import pytest
+
+from weight_only_quantized_int8_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "int8w.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(int8w?_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert header_functions() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load_library()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    nm = os.popen(f"nm -D --defined-only {B.library_path()}").read()
+    for name in header_functions():
+        assert re.search(rf"\bT {name}$", nm, flags=re.M), f"{name} is not an exported text symbol"
+
+
+def test_storage_bytes():
+    assert B.storage_bytes(14336, 4096, 64) == 14336 * 4096 + 4 * 14336 * 64
+    assert B.storage_bytes(8192, 28672, 128) == 8192 * 28672 + 4 * 8192 * 224
+    assert B.storage_bytes(4, 64, 48) == 0
+    assert B.storage_bytes(0, 64, 32) == 0
+
+
+A16 = 1 << 20  # fake, 16-byte aligned "device" addresses: never dereferenced by these tests
+
+
+def desc(N=64, K=256, gs=64, packed=A16, scales=2 * A16, biases=3 * A16):
+    return B.WeightDesc(packed, scales, biases, N, K, gs)
+
+
+def err(rc):
+    assert rc != B.INT8W_OK
+    return rc, B.load_library().int8w_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(packed=0), B.INT8W_ERR_NULL, "missing a tensor"),
+    (dict(scales=0), B.INT8W_ERR_NULL, "missing a tensor"),
+    (dict(biases=0), B.INT8W_ERR_NULL, "missing a tensor"),
+    (dict(N=0), B.INT8W_ERR_SHAPE, "zero dimension"),
+    (dict(K=0), B.INT8W_ERR_SHAPE, "zero dimension"),
+    (dict(gs=0), B.INT8W_ERR_SHAPE, "zero dimension"),
+    (dict(K=96, gs=64), B.INT8W_ERR_SHAPE, "does not divide"),
+    (dict(K=48, gs=48), B.INT8W_ERR_UNSUPPORTED, "not supported"),
+    (dict(K=256, gs=256), B.INT8W_ERR_UNSUPPORTED, "not supported"),
+    (dict(K=32, gs=16), B.INT8W_ERR_UNSUPPORTED, "not supported"),
+    (dict(packed=A16 + 4), B.INT8W_ERR_ALIGN, "packed"),
+    (dict(scales=2 * A16 + 1), B.INT8W_ERR_ALIGN, "scales/biases"),
+    (dict(N=1 << 20, K=1 << 20, gs=64), B.INT8W_ERR_SHAPE, "too large"),
+])
+def test_validate_rejects(kw, code, text):
+    rc, msg = err(B.int8w_validate(desc(**kw)))
+    assert rc == code and text in msg
+    # every entry point applies the same weight checks before anything else
+    for call in (lambda d: B.int8_dequantize_to(d, 4 * A16, 0),
+                 lambda d: B.int8_gemv(d, 4 * A16, 5 * A16, 0),
+                 lambda d: B.int8_gemv_silu_gate(d, 4 * A16, 5 * A16, 6 * A16, 0),
+                 lambda d: B.int8_gemv_silu_gate_resid(d, 4 * A16, 5 * A16, 6 * A16, 7 * A16, 0),
+                 lambda d: B.int8_gemm(d, 4 * A16, 5 * A16, 3, 0)):
+        assert err(call(desc(**kw)))[0] == code
+
+
+def test_validate_accepts_and_clears_error():
+    B.int8w_validate(desc(gs=48, K=96))
+    assert B.int8w_validate(desc()) == B.INT8W_OK
+    assert B.load_library().int8w_last_error() == b""
+    for gs in (32, 64, 128):
+        assert B.int8w_validate(desc(K=4 * gs, gs=gs)) == B.INT8W_OK
+
+
+def test_null_activation_and_output_pointers():
+    d = desc()
+    assert err(B.int8_dequantize_to(d, 0, 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8_gemv(d, 0, 5 * A16, 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8_gemv(d, 4 * A16, 0, 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8_gemv_silu_gate(d, 0, 5 * A16, 6 * A16, 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8_gemv_silu_gate(d, 4 * A16, 0, 6 * A16, 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8_gemv_silu_gate_resid(d, 4 * A16, 5 * A16, 0, 7 * A16, 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8_gemm(d, 0, 5 * A16, 2, 0))[0] == B.INT8W_ERR_NULL
+
+
+def test_alignment_of_activations_and_outputs():
+    d = desc()
+    assert err(B.int8_dequantize_to(d, 4 * A16 + 2, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8_gemv(d, 4 * A16 + 8, 5 * A16, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8_gemv(d, 4 * A16, 5 * A16 + 1, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8_gemv_silu_gate(d, 4 * A16 + 4, 5 * A16, 6 * A16, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8_gemv_silu_gate_resid(d, 4 * A16, 5 * A16, 6 * A16 + 1, 7 * A16, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8_gemm(d, 4 * A16 + 2, 5 * A16, 2, 0))[0] == B.INT8W_ERR_ALIGN
+
+
+def test_outputs_may_not_overlap_inputs():
+    N, K, gs = 64, 256, 64
+    d = desc(N, K, gs)
+    # y inside packed, scales, biases
+    for base in (A16 + 64, 2 * A16 + 2, 3 * A16 + 126):
+        assert err(B.int8_gemv(d, 4 * A16, base, 0))[0] == B.INT8W_ERR_ALIAS
+    # y overlapping x by one element at either end
+    assert err(B.int8_gemv(d, 4 * A16, 4 * A16 + 2 * K - 2, 0))[0] == B.INT8W_ERR_ALIAS
+    assert err(B.int8_gemv(d, 4 * A16 + 16, 4 * A16 + 16 - 2 * N + 2, 0))[0] == B.INT8W_ERR_ALIAS
+    # dequantize_to output over the codes
+    assert err(B.int8_dequantize_to(d, A16, 0))[0] == B.INT8W_ERR_ALIAS
+    # gated: y over gate or up; y partially over x_resid
+    assert err(B.int8_gemv_silu_gate(d, 4 * A16, 5 * A16, 4 * A16 + 32, 0))[0] == B.INT8W_ERR_ALIAS
+    assert err(B.int8_gemv_silu_gate(d, 4 * A16, 5 * A16, 5 * A16, 0))[0] == B.INT8W_ERR_ALIAS
+    rc, msg = err(B.int8_gemv_silu_gate_resid(d, 4 * A16, 5 * A16, 6 * A16, 6 * A16 + 2, 0))
+    assert rc == B.INT8W_ERR_ALIAS and "x_resid" in msg
+    # gemm: Y over X
+    assert err(B.int8_gemm(d, 4 * A16, 4 * A16 + 2 * K * 3 - 2, 3, 0))[0] == B.INT8W_ERR_ALIAS
+    # adjacent but not overlapping is only refused for another reason (none here) -> would launch; not called
+
+
+def test_gemm_m_zero_is_a_no_op():
+    assert B.int8_gemm(desc(), 0, 0, 0, 0) == B.INT8W_OK
+
+
+def test_gemm_rows_times_width_limit():
+    rc, msg = err(B.int8_gemm(desc(N=64, K=1 << 16, gs=64), 4 * A16, 1 << 40, 1 << 17, 0))
+    assert rc == B.INT8W_ERR_SHAPE and "rows" in msg
+
+
+def test_wrapper_applies_load_rules_on_tensors():
+    torch = pytest.importorskip("torch")
+    p = torch.zeros((4, 16), dtype=torch.int32)
+    s = torch.zeros((4, 2), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="2-D 32-bit"):
+        B.Int8Weight(p.float(), s, s, 32)
+    with pytest.raises(ValueError, match="2-D 32-bit"):
+        B.Int8Weight(p.reshape(-1), s, s, 32)
+    with pytest.raises(ValueError, match="bfloat16"):
+        B.Int8Weight(p, s.float(), s, 32)
+    with pytest.raises(ValueError, match=r"\[4, 2\]"):
+        B.Int8Weight(p, s[:, :1], s[:, :1], 32)
+    with pytest.raises(ValueError, match="does not divide"):
+        B.Int8Weight(p, s, s, 48)
+    with pytest.raises(ValueError, match="one GPU"):
+        B.Int8Weight(p, s, s, 32)  # CPU tensors are refused before any call

@@ -1,0 +1,310 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on seeded inputs.
+
+Dequantization must match bit for bit; products must satisfy
+|y - y_ref| <= 8e-3 |y_ref| + 2e-3 sum_k |w x| elementwise and be finite.
+Operations follow the rustdoc page "MlxInt8Weight" (methods dequantize_to,
+gemv, gemv_silu_gate, gemv_silu_gate_resid, gemm).  Shapes are the decode and
+prefill workloads (Llama-3-8B / 70B-shaped matrices) plus ragged and
+degenerate ones; inputs come from weight_only_quantized_int8_amd.synth.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_close, bits_to_dev, dev_to_bits, make_weight, upload
+from weight_only_quantized_int8_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ dequantize_to
+
+DEQUANT_SHAPES = [
+    (256, 512, 64),     # single-GEMV workload weight
+    (37, 96, 32),       # ragged rows, K a multiple of 32 but not of 64
+    (1, 32, 32),        # one row, one group
+    (300, 4160, 64),    # 260 runs per row
+    (129, 1024, 128),
+    (4096, 4096, 64),
+]
+
+
+@pytest.mark.parametrize("N,K,gs", DEQUANT_SHAPES)
+def test_dequantize_bit_exact(N, K, gs):
+    log(f"dequant N={N} K={K} gs={gs}")
+    w, _ = make_weight(10_000 + N + K + gs, N, K, gs)
+    W = upload(w)
+    out = W.dequantize_to()
+    _sync()
+    ref = oracle.dequantize_to(w.packed, w.scales, w.biases, gs)
+    got = dev_to_bits(out)
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} mismatches"
+
+
+def test_dequantize_bit_exact_70b_shape():
+    N, K, gs = 28672, 8192, 128
+    log(f"dequant N={N} K={K} gs={gs}")
+    w, _ = make_weight(4000, N, K, gs)
+    W = upload(w)
+    out = W.dequantize_to()
+    _sync()
+    ref = oracle.dequantize_to(w.packed, w.scales, w.biases, gs)
+    got = dev_to_bits(out)
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} mismatches"
+
+
+def test_dequantize_writes_exactly_n_times_k():
+    N, K, gs = 33, 64, 32
+    w, _ = make_weight(7, N, K, gs)
+    W = upload(w)
+    buf = torch.full((N * K + 64,), 1.5, dtype=torch.bfloat16, device="cuda")
+    W.dequantize_to(buf)
+    _sync()
+    tail = buf[N * K:].float().cpu()
+    assert (tail == 1.5).all()
+    assert np.array_equal(dev_to_bits(buf[:N * K]).reshape(N, K), oracle.dequantize_to(w.packed, w.scales, w.biases, gs))
+
+
+# ------------------------------------------------------------------ gemv
+
+GEMV_SHAPES = [
+    (256, 512, 64),       # single-GEMV workload
+    (14336, 4096, 64),    # 8B gate/up
+    (4096, 4096, 64),     # 8B q/o
+    (1024, 4096, 64),     # 8B k/v
+    (1000, 4096, 64),     # ragged rows
+    (33, 96, 32),         # ragged everything
+    (7, 20480, 128),      # K over one LDS tile (two tiles)
+    (3000, 40960, 32),    # three LDS tiles, many rows
+    (1, 32, 32),          # degenerate: one row, one group
+]
+
+
+@pytest.mark.parametrize("N,K,gs", GEMV_SHAPES)
+def test_gemv(N, K, gs):
+    log(f"gemv N={N} K={K} gs={gs}")
+    w, rng = make_weight(20_000 + N + K + gs, N, K, gs)
+    x = synth.gen_act(rng, K)
+    W = upload(w)
+    y = W.gemv(bits_to_dev(x))
+    _sync()
+    y_ref, A = oracle.gemv(w.packed, w.scales, w.biases, gs, x)
+    assert_close(dev_to_bits(y), y_ref, A, f"gemv {N}x{K} gs{gs}")
+
+
+GATED_SHAPES = [
+    (256, 512, 64),
+    (4096, 14336, 64),    # 8B down projection
+    (8192, 28672, 128),   # 70B down projection
+    (1000, 3072, 32),
+    (33, 96, 32),
+    (5, 36864, 64),       # K over one LDS tile
+]
+
+
+@pytest.mark.parametrize("N,K,gs", GATED_SHAPES)
+def test_gemv_silu_gate(N, K, gs):
+    log(f"silu_gate N={N} K={K} gs={gs}")
+    w, rng = make_weight(30_000 + N + K + gs, N, K, gs)
+    g = synth.gen_act(rng, K)
+    u = synth.gen_act(rng, K)
+    W = upload(w)
+    y = W.gemv_silu_gate(bits_to_dev(g), bits_to_dev(u))
+    _sync()
+    y_ref, A = oracle.gemv_silu_gate(w.packed, w.scales, w.biases, gs, g, u)
+    assert_close(dev_to_bits(y), y_ref, A, f"silu_gate {N}x{K} gs{gs}")
+
+
+@pytest.mark.parametrize("N,K,gs", GATED_SHAPES)
+def test_gemv_silu_gate_resid(N, K, gs):
+    log(f"silu_gate_resid N={N} K={K} gs={gs}")
+    w, rng = make_weight(40_000 + N + K + gs, N, K, gs)
+    g = synth.gen_act(rng, K)
+    u = synth.gen_act(rng, K)
+    r = synth.gen_act(rng, N)
+    W = upload(w)
+    y = W.gemv_silu_gate_resid(bits_to_dev(g), bits_to_dev(u), bits_to_dev(r))
+    _sync()
+    y_ref, A = oracle.gemv_silu_gate_resid(w.packed, w.scales, w.biases, gs, g, u, r)
+    assert_close(dev_to_bits(y), y_ref, A, f"silu_gate_resid {N}x{K} gs{gs}")
+
+
+def test_silu_gate_resid_in_place_and_zero_gate_passthrough():
+    N, K, gs = 4096, 14336, 64
+    w, rng = make_weight(41_000, N, K, gs)
+    g = synth.gen_act(rng, K)
+    u = synth.gen_act(rng, K)
+    r = synth.gen_act(rng, N)
+    W = upload(w)
+    # gate == 0 -> silu(0) = 0 -> y == x_resid exactly
+    y0 = W.gemv_silu_gate_resid(bits_to_dev(np.zeros(K, np.uint16)), bits_to_dev(u), bits_to_dev(r))
+    _sync()
+    assert np.array_equal(dev_to_bits(y0), r)
+    # in place: y is x_resid itself
+    buf = bits_to_dev(r)
+    W.gemv_silu_gate_resid(bits_to_dev(g), bits_to_dev(u), buf, y=buf)
+    _sync()
+    y_ref, A = oracle.gemv_silu_gate_resid(w.packed, w.scales, w.biases, gs, g, u, r)
+    assert_close(dev_to_bits(buf), y_ref, A, "in-place residual")
+    y_sep = W.gemv_silu_gate_resid(bits_to_dev(g), bits_to_dev(u), bits_to_dev(r))
+    _sync()
+    assert np.array_equal(dev_to_bits(buf), dev_to_bits(y_sep))
+
+
+# ------------------------------------------------------------------ gemm
+
+SMALLM_SHAPES = [(14336, 4096), (4096, 14336)]
+
+
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("N,K", SMALLM_SHAPES)
+@pytest.mark.parametrize("m", [2, 4, 8, 16])
+def test_gemm_small_batch_decode(m, N, K, gs):
+    log(f"gemm m={m} N={N} K={K} gs={gs}")
+    w, rng = make_weight(2000 + m * 10 + gs + N, N, K, gs)
+    X = synth.gen_act(rng, (m, K))
+    W = upload(w)
+    Y = W.gemm(bits_to_dev(X))
+    _sync()
+    Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
+    assert_close(dev_to_bits(Y), Y_ref, A, f"gemm m={m} {N}x{K} gs{gs}")
+
+
+@pytest.mark.parametrize("m,N,K,gs", [
+    (1, 14336, 4096, 64),
+    (3, 1000, 4096, 64),
+    (5, 37, 96, 32),
+    (16, 100, 160, 32),
+    (7, 33, 384, 128),
+    (16, 1, 64, 64),
+])
+def test_gemm_small_m_ragged(m, N, K, gs):
+    log(f"gemm ragged m={m} N={N} K={K} gs={gs}")
+    w, rng = make_weight(2500 + m + N + K, N, K, gs)
+    X = synth.gen_act(rng, (m, K))
+    W = upload(w)
+    Y = W.gemm(bits_to_dev(X))
+    _sync()
+    Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
+    assert_close(dev_to_bits(Y), Y_ref, A, f"gemm m={m} {N}x{K} gs{gs}")
+
+
+@pytest.mark.parametrize("m,N,K,gs", [
+    (17, 200, 512, 64),
+    (64, 128, 256, 64),
+    (129, 130, 96, 32),
+    (300, 1024, 2048, 128),
+    (257, 333, 4096, 64),
+])
+def test_gemm_prefill_small(m, N, K, gs):
+    log(f"gemm prefill m={m} N={N} K={K} gs={gs}")
+    w, rng = make_weight(3000 + m + N + K, N, K, gs)
+    X = synth.gen_act(rng, (m, K))
+    W = upload(w)
+    Y = W.gemm(bits_to_dev(X))
+    _sync()
+    Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
+    assert_close(dev_to_bits(Y), Y_ref, A, f"gemm m={m} {N}x{K} gs{gs}")
+
+
+@pytest.mark.parametrize("m", [512, 2048])
+@pytest.mark.parametrize("N,K", SMALLM_SHAPES)
+def test_gemm_prefill_full_size_sampled_rows(m, N, K):
+    gs = 64
+    log(f"gemm prefill m={m} N={N} K={K} gs={gs}")
+    w, rng = make_weight(3_500 + m + N, N, K, gs)
+    X = synth.gen_act(rng, (m, K))
+    W = upload(w)
+    Y = W.gemm(bits_to_dev(X))
+    _sync()
+    Yb = dev_to_bits(Y)
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(m + N).choice(m, 30, replace=False)]))
+    Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X[rows])
+    assert_close(Yb[rows], Y_ref, A, f"gemm m={m} {N}x{K} rows {rows.tolist()[:6]}...")
+    assert np.isfinite(oracle.bf16_to_f32(Yb)).all()
+
+
+def test_gemm_m1_is_gemv_bit_exact():
+    N, K, gs = 4096, 4096, 64
+    w, rng = make_weight(5000, N, K, gs)
+    x = synth.gen_act(rng, K)
+    W = upload(w)
+    xd = bits_to_dev(x)
+    y = W.gemv(xd)
+    Y = W.gemm(xd.reshape(1, K))
+    _sync()
+    assert np.array_equal(dev_to_bits(y), dev_to_bits(Y)[0])
+
+
+@pytest.mark.parametrize("m", [1, 4, 32])
+def test_gemm_one_hot_rows_give_dequantized_columns(m):
+    """X[i] = e_j: Y[i, :] equals column j of dequantize_to bit for bit."""
+    N, K, gs = 512, 1024, 64
+    w, _ = make_weight(6000 + m, N, K, gs)
+    cols = np.random.default_rng(m).choice(K, m, replace=False)
+    X = np.zeros((m, K), np.uint16)
+    X[np.arange(m), cols] = 0x3F80
+    W = upload(w)
+    Y = W.gemm(bits_to_dev(X))
+    D = W.dequantize_to()
+    _sync()
+    Yb, Db = dev_to_bits(Y), dev_to_bits(D)
+    for i, j in enumerate(cols):
+        assert np.array_equal(Yb[i], Db[:, j]), f"row {i} (column {j})"
+
+
+def test_gemm_m0_is_a_no_op():
+    w, _ = make_weight(6500, 64, 128, 32)
+    W = upload(w)
+    Y = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    assert W.gemm(torch.empty((0, 128), dtype=torch.bfloat16, device="cuda"), Y).shape == (0, 64)
+
+
+# ------------------------------------------------------------------ determinism and constant weights
+
+def test_every_entry_point_is_deterministic():
+    N, K, gs = 4096, 14336, 64
+    w, rng = make_weight(7000, N, K, gs)
+    g = bits_to_dev(synth.gen_act(rng, K))
+    u = bits_to_dev(synth.gen_act(rng, K))
+    r = bits_to_dev(synth.gen_act(rng, N))
+    X4 = bits_to_dev(synth.gen_act(rng, (4, K)))
+    X600 = bits_to_dev(synth.gen_act(rng, (600, K)))
+    W = upload(w)
+    calls = {
+        "gemv": lambda: W.gemv(g),
+        "silu_gate": lambda: W.gemv_silu_gate(g, u),
+        "silu_gate_resid": lambda: W.gemv_silu_gate_resid(g, u, r),
+        "gemm4": lambda: W.gemm(X4),
+        "gemm600": lambda: W.gemm(X600),
+    }
+    for name, f in calls.items():
+        a = dev_to_bits(f())
+        b = dev_to_bits(f())
+        assert np.array_equal(a, b), name
+
+
+@pytest.mark.parametrize("c", [0, 255])
+def test_constant_codes_closed_form(c):
+    """All codes = c: y[n] = sum_g (c s_g + b_g) sum_{k in g} x_k (computed by the oracle on the same bytes)."""
+    N, K, gs = 2048, 4096, 64
+    w, rng = make_weight(8000 + c, N, K, gs)
+    w.packed[:] = np.uint32(c * 0x01010101)
+    x = synth.gen_act(rng, K)
+    W = upload(w)
+    y = W.gemv(bits_to_dev(x))
+    Y = W.gemm(bits_to_dev(np.stack([x, x, x])))
+    _sync()
+    y_ref, A = oracle.gemv(w.packed, w.scales, w.biases, gs, x)
+    assert_close(dev_to_bits(y), y_ref, A, f"gemv codes={c}")
+    for i in range(3):
+        assert_close(dev_to_bits(Y)[i], y_ref, A, f"gemm codes={c} row {i}")

@@ -1,0 +1,246 @@
+"""Thin ctypes binding of libint8w.so (include/int8w.h).
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  If the
+library has not been built, loading it raises -- there is no fallback.
+
+The checks in :class:`Int8Weight` follow the rustdoc page "MlxInt8Weight",
+method load: the weight must be a 2-D 32-bit tensor, scales and biases BF16
+of shape [out_features, in_features / group_size], and group_size must divide
+in_features.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libint8w.so")
+
+INT8W_OK = 0
+INT8W_ERR_NULL = -1
+INT8W_ERR_SHAPE = -2
+INT8W_ERR_UNSUPPORTED = -3
+INT8W_ERR_ALIGN = -4
+INT8W_ERR_ALIAS = -5
+INT8W_ERR_HIP = -6
+ERROR_NAMES = {
+    INT8W_ERR_NULL: "INT8W_ERR_NULL",
+    INT8W_ERR_SHAPE: "INT8W_ERR_SHAPE",
+    INT8W_ERR_UNSUPPORTED: "INT8W_ERR_UNSUPPORTED",
+    INT8W_ERR_ALIGN: "INT8W_ERR_ALIGN",
+    INT8W_ERR_ALIAS: "INT8W_ERR_ALIAS",
+    INT8W_ERR_HIP: "INT8W_ERR_HIP",
+}
+
+EXPORTED = (
+    "int8w_validate", "int8w_storage_bytes", "int8_dequantize_to", "int8_gemv", "int8_gemv_silu_gate",
+    "int8_gemv_silu_gate_resid", "int8_gemm", "int8w_last_error",
+)
+
+
+class Int8wError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {message}")
+        self.code = code
+        self.message = message
+
+
+class WeightDesc(ctypes.Structure):
+    """Mirror of ``int8w_weight`` (include/int8w.h)."""
+    _fields_ = [
+        ("packed", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("biases", ctypes.c_void_p),
+        ("out_features", ctypes.c_uint32),
+        ("in_features", ctypes.c_uint32),
+        ("group_size", ctypes.c_uint32),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -m weight_only_quantized_int8_amd.build` "
+            "(the HIP library is required: there is no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    W = ctypes.POINTER(WeightDesc)
+    u64 = ctypes.c_uint64
+    lib.int8w_validate.argtypes = [W]
+    lib.int8w_validate.restype = ctypes.c_int
+    lib.int8w_storage_bytes.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
+    lib.int8w_storage_bytes.restype = ctypes.c_uint64
+    lib.int8_dequantize_to.argtypes = [W, P, u64]
+    lib.int8_dequantize_to.restype = ctypes.c_int
+    lib.int8_gemv.argtypes = [W, P, P, u64]
+    lib.int8_gemv.restype = ctypes.c_int
+    lib.int8_gemv_silu_gate.argtypes = [W, P, P, P, u64]
+    lib.int8_gemv_silu_gate.restype = ctypes.c_int
+    lib.int8_gemv_silu_gate_resid.argtypes = [W, P, P, P, P, u64]
+    lib.int8_gemv_silu_gate_resid.restype = ctypes.c_int
+    lib.int8_gemm.argtypes = [W, P, P, ctypes.c_uint32, u64]
+    lib.int8_gemm.restype = ctypes.c_int
+    lib.int8w_last_error.argtypes = []
+    lib.int8w_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != INT8W_OK:
+        msg = load_library().int8w_last_error().decode(errors="replace")
+        raise Int8wError(rc, msg)
+
+
+def storage_bytes(out_features: int, in_features: int, group_size: int) -> int:
+    return int(load_library().int8w_storage_bytes(out_features, in_features, group_size))
+
+
+# ---- raw C-ABI calls (device addresses as ints, stream as int) --------------------------------
+
+def int8w_validate(desc: WeightDesc) -> int:
+    return load_library().int8w_validate(ctypes.byref(desc))
+
+
+def int8_dequantize_to(desc: WeightDesc, out: int, stream: int) -> int:
+    return load_library().int8_dequantize_to(ctypes.byref(desc), out, stream)
+
+
+def int8_gemv(desc: WeightDesc, x: int, y: int, stream: int) -> int:
+    return load_library().int8_gemv(ctypes.byref(desc), x, y, stream)
+
+
+def int8_gemv_silu_gate(desc: WeightDesc, gate: int, up: int, y: int, stream: int) -> int:
+    return load_library().int8_gemv_silu_gate(ctypes.byref(desc), gate, up, y, stream)
+
+
+def int8_gemv_silu_gate_resid(desc: WeightDesc, gate: int, up: int, x_resid: int, y: int, stream: int) -> int:
+    return load_library().int8_gemv_silu_gate_resid(ctypes.byref(desc), gate, up, x_resid, y, stream)
+
+
+def int8_gemm(desc: WeightDesc, x: int, y: int, m: int, stream: int) -> int:
+    return load_library().int8_gemm(ctypes.byref(desc), x, y, m, stream)
+
+
+# ---- tensor-level wrapper -----------------------------------------------------------------------
+
+def _stream_of(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need_bf16(t: torch.Tensor, name: str, numel: int, device: torch.device) -> None:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, weight on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+
+
+class Int8Weight:
+    """One 8-bit affine group-quantized weight on the GPU (borrowed tensors).
+
+    packed:  int32/uint32 [out_features, in_features/4] (code k in byte k%4 of word k/4)
+    scales:  bfloat16 [out_features, in_features/group_size]
+    biases:  bfloat16 [out_features, in_features/group_size]
+    The tensors stay owned by the caller (this object keeps references).
+    """
+
+    def __init__(self, packed: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, group_size: int):
+        if packed.dim() != 2 or packed.dtype not in (torch.int32, torch.uint32):
+            raise ValueError("weight must be a 2-D 32-bit (U32) tensor")
+        if scales.dtype != torch.bfloat16 or biases.dtype != torch.bfloat16:
+            raise ValueError("scales and biases must be bfloat16")
+        N, kw = packed.shape
+        K = 4 * kw
+        gs = int(group_size)
+        if gs <= 0 or K % gs:
+            raise ValueError(f"group_size {gs} does not divide in_features {K}")
+        G = K // gs
+        if tuple(scales.shape) != (N, G) or tuple(biases.shape) != (N, G):
+            raise ValueError(f"scales/biases must be [{N}, {G}] = [out_features, in_features/group_size]")
+        for t, name in ((packed, "packed"), (scales, "scales"), (biases, "biases")):
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if not (packed.device == scales.device == biases.device) or packed.device.type != "cuda":
+            raise ValueError("packed, scales and biases must be on one GPU")
+        self.packed, self.scales, self.biases = packed, scales, biases
+        self.out_features, self.in_features, self.group_size = N, K, gs
+        self.device = packed.device
+        self.desc = WeightDesc(packed.data_ptr(), scales.data_ptr(), biases.data_ptr(), N, K, gs)
+        _check(int8w_validate(self.desc))
+
+    @classmethod
+    def from_arrays(cls, packed, scales_bits, biases_bits, group_size: int, device="cuda") -> "Int8Weight":
+        """Upload NumPy arrays (uint32 words, uint16 BF16 bit patterns)."""
+        import numpy as np
+        p = torch.from_numpy(np.ascontiguousarray(packed).view(np.int32)).to(device)
+        s = torch.from_numpy(np.ascontiguousarray(scales_bits).view(np.int16)).view(torch.bfloat16).to(device)
+        b = torch.from_numpy(np.ascontiguousarray(biases_bits).view(np.int16)).view(torch.bfloat16).to(device)
+        return cls(p, s, b, group_size)
+
+    def storage_bytes(self) -> int:
+        return storage_bytes(self.out_features, self.in_features, self.group_size)
+
+    def dequantize_to(self, out: torch.Tensor | None = None) -> torch.Tensor:
+        N, K = self.out_features, self.in_features
+        if out is None:
+            out = torch.empty((N, K), dtype=torch.bfloat16, device=self.device)
+        _need_bf16(out, "out", N * K, self.device)
+        _check(int8_dequantize_to(self.desc, out.data_ptr(), _stream_of(self.device)))
+        return out
+
+    def gemv(self, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+        _need_bf16(x, "x", self.in_features, self.device)
+        if y is None:
+            y = torch.empty(self.out_features, dtype=torch.bfloat16, device=self.device)
+        _need_bf16(y, "y", self.out_features, self.device)
+        _check(int8_gemv(self.desc, x.data_ptr(), y.data_ptr(), _stream_of(self.device)))
+        return y
+
+    def gemv_silu_gate(self, gate: torch.Tensor, up: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+        _need_bf16(gate, "gate", self.in_features, self.device)
+        _need_bf16(up, "up", self.in_features, self.device)
+        if y is None:
+            y = torch.empty(self.out_features, dtype=torch.bfloat16, device=self.device)
+        _need_bf16(y, "y", self.out_features, self.device)
+        _check(int8_gemv_silu_gate(self.desc, gate.data_ptr(), up.data_ptr(), y.data_ptr(), _stream_of(self.device)))
+        return y
+
+    def gemv_silu_gate_resid(self, gate: torch.Tensor, up: torch.Tensor, x_resid: torch.Tensor,
+                             y: torch.Tensor | None = None) -> torch.Tensor:
+        _need_bf16(gate, "gate", self.in_features, self.device)
+        _need_bf16(up, "up", self.in_features, self.device)
+        _need_bf16(x_resid, "x_resid", self.out_features, self.device)
+        if y is None:
+            y = torch.empty(self.out_features, dtype=torch.bfloat16, device=self.device)
+        _need_bf16(y, "y", self.out_features, self.device)
+        _check(int8_gemv_silu_gate_resid(self.desc, gate.data_ptr(), up.data_ptr(), x_resid.data_ptr(),
+                                         y.data_ptr(), _stream_of(self.device)))
+        return y
+
+    def gemm(self, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+        if x.dim() != 2 or x.shape[1] != self.in_features:
+            raise ValueError(f"X must be [m, {self.in_features}]")
+        m = x.shape[0]
+        _need_bf16(x, "X", m * self.in_features, self.device)
+        if y is None:
+            y = torch.empty((m, self.out_features), dtype=torch.bfloat16, device=self.device)
+        _need_bf16(y, "Y", m * self.out_features, self.device)
+        _check(int8_gemm(self.desc, x.data_ptr(), y.data_ptr(), m, _stream_of(self.device)))
+        return y

@@ -1,0 +1,231 @@
+// capi.cpp -- the C-ABI of libint8w (declared in include/int8w.h).
+//
+// Host-side only: argument validation (the rules the rustdoc page
+// "MlxInt8Weight" gives for its load method, plus alignment, aliasing and
+// size checks), choice of kernel by the number of input rows, and launch on
+// the caller's stream.  Nothing here allocates or frees device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "int8w.h"
+#include "launch.h"
+
+namespace int8w {
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return INT8W_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  const char *name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const char *name, const void *p, uint64_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, lo + (uintptr_t)bytes};
+}
+
+bool overlaps(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Output `out` must not overlap any of the inputs.
+int check_alias(const Range &out, const Range *ins, int n_ins) {
+  for (int i = 0; i < n_ins; ++i)
+    if (ins[i].hi > ins[i].lo && overlaps(out, ins[i]))
+      return fail(INT8W_ERR_ALIAS, "output %s overlaps input %s", out.name, ins[i].name);
+  return INT8W_OK;
+}
+
+int validate(const int8w_weight *w) {
+  if (!w) return fail(INT8W_ERR_NULL, "weight descriptor is NULL");
+  if (!w->packed || !w->scales || !w->biases)
+    return fail(INT8W_ERR_NULL, "weight is missing a tensor (packed, scales or biases is NULL)");
+  if (w->out_features == 0 || w->in_features == 0 || w->group_size == 0)
+    return fail(INT8W_ERR_SHAPE, "zero dimension (out_features=%u in_features=%u group_size=%u)",
+                w->out_features, w->in_features, w->group_size);
+  if (w->in_features % w->group_size != 0)
+    return fail(INT8W_ERR_SHAPE, "group_size %u does not divide in_features %u", w->group_size, w->in_features);
+  if (w->in_features % 4 != 0)
+    return fail(INT8W_ERR_SHAPE, "in_features %u is not a whole number of 4-code words", w->in_features);
+  if (w->group_size != 32 && w->group_size != 64 && w->group_size != 128)
+    return fail(INT8W_ERR_UNSUPPORTED, "group_size %u not supported (32, 64 or 128)", w->group_size);
+  // 16-code runs are indexed with 32-bit integers (with headroom for grid strides).
+  if ((uint64_t)w->out_features * (w->in_features / 16u) > 0x7FFFFFFFull)
+    return fail(INT8W_ERR_SHAPE, "weight too large (%u x %u codes)", w->out_features, w->in_features);
+  if (!aligned(w->packed, 16)) return fail(INT8W_ERR_ALIGN, "packed is not 16-byte aligned");
+  if (!aligned(w->scales, 2) || !aligned(w->biases, 2))
+    return fail(INT8W_ERR_ALIGN, "scales/biases are not 2-byte aligned");
+  return INT8W_OK;
+}
+
+WeightView view(const int8w_weight *w) {
+  return WeightView{w->packed, w->scales, w->biases, w->out_features, w->in_features, w->group_size};
+}
+
+void weight_ranges(const int8w_weight *w, Range *r) {
+  const uint64_t N = w->out_features, K = w->in_features, G = K / w->group_size;
+  r[0] = range("packed", w->packed, N * K);
+  r[1] = range("scales", w->scales, N * G * 2);
+  r[2] = range("biases", w->biases, N * G * 2);
+}
+
+int finish_launch(hipError_t e, hipStream_t stream) {
+  if (e != hipSuccess) return fail(INT8W_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  static const bool sync_check = [] {
+    const char *v = getenv("INT8W_SYNC_CHECK");
+    return v && v[0] && v[0] != '0';
+  }();
+  if (sync_check) {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(INT8W_ERR_HIP, "kernel execution failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+hipStream_t as_stream(uint64_t s) { return reinterpret_cast<hipStream_t>(static_cast<uintptr_t>(s)); }
+
+}  // namespace
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace int8w
+
+using namespace int8w;
+
+extern "C" {
+
+int int8w_validate(const int8w_weight *w) {
+  int rc = validate(w);
+  return rc == INT8W_OK ? ok() : rc;
+}
+
+uint64_t int8w_storage_bytes(uint32_t out_features, uint32_t in_features, uint32_t group_size) {
+  if (out_features == 0 || in_features == 0 || group_size == 0 || in_features % group_size) return 0;
+  const uint64_t N = out_features, K = in_features;
+  return N * K + 4ull * N * (K / group_size);
+}
+
+int int8_dequantize_to(const int8w_weight *w, uint16_t *out, uint64_t stream) {
+  int rc = validate(w);
+  if (rc) return rc;
+  if (!out) return fail(INT8W_ERR_NULL, "out is NULL");
+  if (!aligned(out, 16)) return fail(INT8W_ERR_ALIGN, "out is not 16-byte aligned");
+  Range ins[3];
+  weight_ranges(w, ins);
+  rc = check_alias(range("out", out, (uint64_t)w->out_features * w->in_features * 2), ins, 3);
+  if (rc) return rc;
+  (void)hipGetLastError();
+  return finish_launch(launch_dequant(view(w), out, as_stream(stream)), as_stream(stream));
+}
+
+int int8_gemv(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint64_t stream) {
+  int rc = validate(w);
+  if (rc) return rc;
+  if (!x || !y) return fail(INT8W_ERR_NULL, "x or y is NULL");
+  if (!aligned(x, 16)) return fail(INT8W_ERR_ALIGN, "x is not 16-byte aligned");
+  if (!aligned(y, 2)) return fail(INT8W_ERR_ALIGN, "y is not 2-byte aligned");
+  Range ins[4];
+  weight_ranges(w, ins);
+  ins[3] = range("x", x, (uint64_t)w->in_features * 2);
+  rc = check_alias(range("y", y, (uint64_t)w->out_features * 2), ins, 4);
+  if (rc) return rc;
+  (void)hipGetLastError();
+  return finish_launch(launch_gemv(view(w), kEpiNone, x, nullptr, nullptr, y, as_stream(stream)),
+                       as_stream(stream));
+}
+
+static int gemv_gated(const int8w_weight *w, const uint16_t *gate, const uint16_t *up, const uint16_t *x_resid,
+                      uint16_t *y, uint64_t stream, bool with_resid) {
+  int rc = validate(w);
+  if (rc) return rc;
+  if (!gate || !up || !y || (with_resid && !x_resid))
+    return fail(INT8W_ERR_NULL, with_resid ? "gate, up, x_resid or y is NULL" : "gate, up or y is NULL");
+  if (!aligned(gate, 16) || !aligned(up, 16)) return fail(INT8W_ERR_ALIGN, "gate/up are not 16-byte aligned");
+  if (!aligned(y, 2) || (with_resid && !aligned(x_resid, 2)))
+    return fail(INT8W_ERR_ALIGN, "y/x_resid are not 2-byte aligned");
+  const uint64_t K = w->in_features, N = w->out_features;
+  Range ins[6];
+  weight_ranges(w, ins);
+  ins[3] = range("gate", gate, K * 2);
+  ins[4] = range("up", up, K * 2);
+  int n_ins = 5;
+  // y == x_resid exactly is the allowed in-place residual; any other overlap is not.
+  if (with_resid && reinterpret_cast<const void *>(x_resid) != reinterpret_cast<const void *>(y))
+    ins[n_ins++] = range("x_resid", x_resid, N * 2);
+  rc = check_alias(range("y", y, N * 2), ins, n_ins);
+  if (rc) return rc;
+  (void)hipGetLastError();
+  return finish_launch(launch_gemv(view(w), with_resid ? kEpiSiluGateResid : kEpiSiluGate, gate, up,
+                                   with_resid ? x_resid : nullptr, y, as_stream(stream)),
+                       as_stream(stream));
+}
+
+int int8_gemv_silu_gate(const int8w_weight *w, const uint16_t *gate, const uint16_t *up, uint16_t *y,
+                        uint64_t stream) {
+  return gemv_gated(w, gate, up, nullptr, y, stream, false);
+}
+
+int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const uint16_t *up,
+                              const uint16_t *x_resid, uint16_t *y, uint64_t stream) {
+  return gemv_gated(w, gate, up, x_resid, y, stream, true);
+}
+
+int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, uint64_t stream) {
+  int rc = validate(w);
+  if (rc) return rc;
+  if (m == 0) return ok();
+  if (!x || !y) return fail(INT8W_ERR_NULL, "X or Y is NULL");
+  if (!aligned(x, 16)) return fail(INT8W_ERR_ALIGN, "X is not 16-byte aligned");
+  if (!aligned(y, 2)) return fail(INT8W_ERR_ALIGN, "Y is not 2-byte aligned");
+  const uint64_t K = w->in_features, N = w->out_features;
+  if ((uint64_t)m * K > 0xFFFFFFFFull || (uint64_t)m * N > 0xFFFFFFFFull)
+    return fail(INT8W_ERR_SHAPE, "m=%u rows too many for this weight", m);
+  Range ins[4];
+  weight_ranges(w, ins);
+  ins[3] = range("X", x, (uint64_t)m * K * 2);
+  rc = check_alias(range("Y", y, (uint64_t)m * N * 2), ins, 4);
+  if (rc) return rc;
+  (void)hipGetLastError();
+  hipStream_t s = as_stream(stream);
+  hipError_t e;
+  if (m == 1)
+    e = launch_gemv(view(w), kEpiNone, x, nullptr, nullptr, y, s);
+  else if (m <= 16)
+    e = launch_gemm_smallm(view(w), x, y, m, s);
+  else
+    e = launch_gemm_prefill(view(w), x, y, m, s);
+  return finish_launch(e, s);
+}
+
+const char *int8w_last_error(void) { return g_last_error; }
+
+}  // extern "C"

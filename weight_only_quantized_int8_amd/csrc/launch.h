@@ -1,0 +1,37 @@
+// launch.h -- internal host-side launchers of the gfx950 kernels (not part of
+// the public C-ABI).  Arguments are already validated by capi.cpp; each
+// launcher only sizes the grid and enqueues on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace int8w {
+
+struct WeightView {
+  const uint32_t *packed;
+  const uint16_t *scales;
+  const uint16_t *biases;
+  uint32_t N, K, gs;
+};
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_dequant(const WeightView &w, uint16_t *out, hipStream_t stream);
+
+enum GemvEpilogue { kEpiNone = 0, kEpiSiluGate = 1, kEpiSiluGateResid = 2 };
+
+// y = W a, with a = x (kEpiNone) or silu(gate)*up; plus x_resid for kEpiSiluGateResid.
+hipError_t launch_gemv(const WeightView &w, GemvEpilogue epi, const uint16_t *x_or_gate,
+                       const uint16_t *up, const uint16_t *x_resid, uint16_t *y, hipStream_t stream);
+
+// Y[m, N] = X[m, K] W^T for 2 <= m <= 16 (matrix cores, per-group rescale).
+hipError_t launch_gemm_smallm(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
+                              hipStream_t stream);
+
+// Y[m, N] = X[m, K] W^T for large m (weight tiles dequantized to BF16 in LDS).
+hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
+                               hipStream_t stream);
+
+}  // namespace int8w
