@@ -15,6 +15,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -66,6 +67,29 @@ __device__ __forceinline__ uint2 load_nt(const uint2 *p) {
 __device__ __forceinline__ void store_nt(uint4 v, uint4 *p) {
   u32x4 t = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));
+}
+
+// ---- buffer loads.  A raw buffer resource bounds every access: a load whose
+// byte offset (plus its size) exceeds num_records returns zero and touches no
+// memory, so a pipeline can issue its loads unconditionally and mark the ones
+// past the end with an out-of-range offset instead of branching.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kBufferDword3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
+constexpr int kAuxNontemporal = 2;          // nt: streamed once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)num_bytes, kBufferDword3);
+}
+template <int AUX = 0>
+__device__ __forceinline__ u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+}
+template <int AUX = 0>
+__device__ __forceinline__ u32x2 buf_load_b64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, AUX);
+}
+__device__ __forceinline__ uint16_t buf_load_b16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 
 }  // namespace int8w
