@@ -5,27 +5,31 @@
 //   gemv_silu_gate_resid  y[n] = x_resid[n] + sum_k w[n,k] silu(gate[k]) up[k]
 // with w[n,k] = q[n,k] * s[n, k/gs] + b[n, k/gs].
 //
-// Design (HBM-bound: the codes are ~94% of the bytes at gs = 64):
-//  * The activation a[k] (x, or silu(gate)*up in fp32) is formed once per
-//    workgroup and K-tile into LDS, together with the sum of each run of 16
-//    activations.  The gated product therefore never leaves the chip and its
-//    exp/divide cost is shared by every row of the workgroup.
-//  * Each lane owns runs of 16 consecutive codes (one 16-byte load), so one
-//    wave-wide load streams 1 KiB of a row, fully coalesced, non-temporal.
-//  * A run never straddles a group (gs is a multiple of 16), so the affine
-//    terms factor out of the run:  sum_k (q_k s + b) a_k = s*sum_k q_k a_k +
-//    b*sum_k a_k.  Per code: one byte convert and one fp32 FMA; the bias costs
-//    nothing per code.
-//  * Each wave carries R rows at once (the LDS activation reads are shared by
-//    the R rows).  Its loads run as a two-stage software pipeline of blocks of
-//    U runs per row: block j+1 is in flight while block j is consumed, and the
-//    first block is issued before the activation staging, so the staging hides
-//    under the first HBM round trip.  Loads go through bounded buffer
-//    resources, so the code is branch-free: past-the-end loads return zero
-//    without touching memory.
-//  * Waves of a workgroup may also split K (WK-way) for short, wide matrices;
-//    partial sums meet in LDS.  Lane partials are summed with cross-lane
-//    shuffles; there are no atomics, so results are deterministic.
+// HBM-bound (the codes are ~94% of the bytes at gs = 64).  Design:
+//  * Activation.  a[k] (x, or silu(gate)*up in fp32) is formed once per
+//    workgroup and K-tile into LDS, with the sum of each run of 16
+//    activations.  The gated product therefore never leaves the chip, and its
+//    exp/divide cost is shared by every row the workgroup streams.
+//  * Codes.  A lane owns runs of 16 consecutive codes (one 16-byte load), so a
+//    wave-wide load streams 1 KiB of a row ("segment").  Each wave streams a
+//    balanced, contiguous range of rows, RP rows side by side (the LDS reads
+//    of a segment's activation serve all RP rows).  All loads go through
+//    bounded buffer resources with the wave-uniform part of the offset in a
+//    scalar register; past the wave's last row a load re-reads its last item.
+//  * Arithmetic.  A run never straddles a group (gs is a multiple of 16), so
+//    the affine terms factor out of the run:
+//        sum_k (q_k s + b) a_k = s * sum_k q_k a_k + b * sum_k a_k.
+//    Codes become binary16 (1024 + q) with one byte permute per two codes and
+//    multiply through v_fma_mix_f32 (f16 x f32 -> f32, exact products); the
+//    1024 offset folds into the bias: s*P' + (b - 1024 s)*S with
+//    P' = sum (1024 + q) a and S = sum a.  Per code: half a permute and one
+//    FMA.  (scale, bias - 1024 scale) pairs are staged per wave in LDS as fp32.
+//  * Pipeline.  Loads run two blocks of U items ahead (the next block is
+//    issued before the current one is consumed); the first block goes out
+//    before the activation staging, so staging hides under its latency.
+//  * Reduction.  A row's lane partials are summed with a fixed DPP sequence as
+//    soon as its last segment is consumed; with several K-tiles the partials
+//    meet in LDS in tile order.  No atomics: results are deterministic.
 //  * fp32 accumulation throughout; the residual is added in fp32 before the
 //    one rounding to BF16.
 #include "common.h"
@@ -35,37 +39,51 @@ namespace int8w {
 
 namespace {
 
-constexpr int kGemvThreads = 512;          // 8 waves
-constexpr int kWaves = kGemvThreads / 64;
 constexpr uint32_t kTileRunsMax = 1024;    // 16384 activations per LDS tile
-constexpr int kStagePerThread = kTileRunsMax / kGemvThreads;
-constexpr int kU = 4;                      // 1 KiB wave loads per pipeline block
+constexpr int kLoadsPerBlock = 4;          // 1 KiB wave loads per pipeline block (U items x RP rows)
 constexpr uint32_t kMaxRowsPerWave = 16;   // rows a wave may own
-constexpr size_t kLdsBudget = 150 * 1024;  // dynamic LDS per workgroup
-constexpr int kSbPerLane = 8;              // scale/bias elements a lane prefetches per tile
+constexpr size_t kLdsPerCu = 156 * 1024;   // dynamic LDS budget of one CU
+constexpr int kSbPerLane = 4;              // scale/bias entries a lane prefetches per tile
 
 struct GemvCfg {
-  uint32_t blocks;     // workgroups (8 waves each)
+  int waves;           // waves per workgroup (8 or 16)
+  int rp;              // rows each wave carries side by side (1 or 2)
+  uint32_t blocks;     // workgroups
   uint32_t ct;         // 16-code runs per LDS tile (multiple of 64)
   uint32_t max_rows;   // most rows any wave owns
   bool tail;           // in_features not a multiple of 1024
 };
 
+// LDS bytes of one workgroup (layout in k_gemv).
 size_t lds_bytes(const GemvCfg &c, uint32_t gs) {
   const size_t tg = (size_t)c.ct * 16u / gs;
-  return (size_t)c.ct * 68u + (size_t)kWaves * 2u * c.max_rows * tg * 2u + (size_t)kWaves * c.max_rows * 4u;
+  return (size_t)c.ct * 68u + (size_t)c.waves * c.max_rows * tg * 8u + (size_t)c.waves * c.max_rows * 4u;
 }
 
-template <int U>
-struct Block {
-  u32x4 q[U];
-};
-
-// f16 pair (1024 + q0, 1024 + q1) from bytes 0/1 (sel 0x04010400) or 2/3
-// (sel 0x04030402) of a code word: byte 0x64 over each code is the binary16
-// pattern of 1024 + q, exact for q in 0..255.
+// binary16 pair (1024 + q0, 1024 + q1) from bytes 0/1 (sel 0x04010400) or
+// 2/3 (sel 0x04030402) of a code word: byte 0x64 over each code is the
+// binary16 pattern of 1024 + q, exact for q in 0..255.
 __device__ __forceinline__ uint32_t f16_pair(uint32_t word, uint32_t sel) {
   return __builtin_amdgcn_perm(0x64646464u, word, sel);
+}
+
+// sum_i (1024 + q_i) a_i over one lane's 16 codes.
+__device__ __forceinline__ float run_dot(const u32x4 &w, const float4 &a0, const float4 &a1, const float4 &a2,
+                                         const float4 &a3) {
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  const float av[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                        a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+  float p = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 lo = __builtin_bit_cast(f16x2, f16_pair(words[i], 0x04010400u));
+    const f16x2 hi = __builtin_bit_cast(f16x2, f16_pair(words[i], 0x04030402u));
+    p = __builtin_fmaf((float)lo.x, av[4 * i + 0], p);
+    p = __builtin_fmaf((float)lo.y, av[4 * i + 1], p);
+    p = __builtin_fmaf((float)hi.x, av[4 * i + 2], p);
+    p = __builtin_fmaf((float)hi.y, av[4 * i + 3], p);
+  }
+  return p;
 }
 
 // Sum over the 64 lanes of a wave in a fixed order (row-wise shifts, then row
@@ -80,143 +98,153 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
   return v;
 }
 
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int U, int RP>
+struct Block {
+  u32x4 q[U][RP];
+};
+
 // LDS layout of one workgroup (dynamic):
-//   act   [NSEG][4][64] float4   activation of the tile, run-interleaved
-//   ssum  [NSEG][64]    float    per-run activation sums
-//   sb    [kWaves][2][max_rows][tg_max] u16   each wave's scales / biases for the tile
-//   part  [kWaves][max_rows] float            row partial sums across tiles
-template <int EPI, int U, bool TAIL>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv(
+//   act   [NSEG][4][64] float4   activation of lane l's 16 codes in segment s
+//   ssum  [NSEG][64] float       their sum
+//   sb    [W][max_rows][TG] float2   each wave's (scale, bias - 1024 scale)
+//   part  [W][max_rows] float        row partial sums across K-tiles
+template <int EPI, int W, int RP, int U, bool TAIL>
+__global__ __launch_bounds__(64 * W) void k_gemv(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ xg,
     const uint16_t *__restrict__ up, const uint16_t *resid, uint16_t *y, uint32_t N, uint32_t K,
     uint32_t gs_log2, uint32_t tile_runs, uint32_t max_rows) {
   // y may be resid itself (in-place residual): each output element reads its
   // own residual before it is written, by the same lane.
+  constexpr int kThreads = 64 * W;
+  constexpr int kStage = (int)(kTileRunsMax + kThreads - 1) / kThreads;  // runs staged per thread
   extern __shared__ float4 lds4[];
-  const uint32_t CT = tile_runs;              // multiple of 64
-  const uint32_t NSEG = CT >> 6;              // 1 KiB segments per tile row
-  const uint32_t TG = (CT << 4) >> gs_log2;   // groups per tile row
+  const uint32_t CT = tile_runs;
+  const uint32_t NSEG = CT >> 6;
+  const uint32_t TG = (CT << 4) >> gs_log2;
   float4 *act = lds4;
   float *ssum = reinterpret_cast<float *>(lds4 + NSEG * 256);
-  uint16_t *sb_all = reinterpret_cast<uint16_t *>(ssum + NSEG * 64);
-  float *part_all = reinterpret_cast<float *>(sb_all + kWaves * 2 * max_rows * TG);
+  float2 *sb_all = reinterpret_cast<float2 *>(ssum + NSEG * 64);
+  float *part_all = reinterpret_cast<float *>(sb_all + W * max_rows * TG);
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t gw = blockIdx.x * kWaves + wave;
-  const uint32_t TW = gridDim.x * kWaves;
-  // this wave's rows: a balanced contiguous range
+  const uint32_t wave = uniform(tid >> 6);
+  const uint32_t gw = blockIdx.x * W + wave;
+  const uint32_t TW = gridDim.x * W;
   const uint32_t rq = N / TW, rr = N % TW;  // the first rr waves own rq + 1 rows
   const uint32_t rbeg = gw * rq + (gw < rr ? gw : rr);
   const uint32_t nr = rq + (gw < rr ? 1u : 0u);
-  const uint32_t cpr = K >> 4;      // 16-code runs per row
-  const uint32_t G = K >> gs_log2;  // groups per row
+  const uint32_t ngrp = (nr + RP - 1) / RP;  // row groups of RP rows
+  const uint32_t cpr = K >> 4;
+  const uint32_t G = K >> gs_log2;
+  const uint32_t gps = 1024u >> gs_log2;  // groups per segment
 
   const auto rw = make_rsrc(codes + (size_t)rbeg * K, nr * K);
   const auto rx = make_rsrc(xg, K * 2u);
   const auto ru = make_rsrc(EPI != kEpiNone ? up : xg, K * 2u);
   const uint16_t *srow = scales + (size_t)rbeg * G;
   const uint16_t *brow = biases + (size_t)rbeg * G;
-
-  uint16_t *sbs = sb_all + wave * 2 * max_rows * TG;  // this wave's scales; biases follow
-  uint16_t *sbb = sbs + max_rows * TG;
+  float2 *sb = sb_all + wave * max_rows * TG;
   float *part = part_all + wave * max_rows;
 
-  // per-lane parts of the offsets; everything else is wave-uniform
+  // per-lane offsets; everything else is wave-uniform
   const uint32_t vo_w = lane << 4;
-  const uint32_t lane_grp = (lane << 4) >> gs_log2;  // group of this lane within a 1 KiB segment
+  const uint32_t lane_grp = (lane << 4) >> gs_log2;
+  const uint32_t v_act = lane << 4;
+  const uint32_t v_s = lane << 2;
+  const uint32_t v_sb = lane_grp << 3;
 
-  float acc = 0.f;
-  Block<U> A, B;
+  float acc[RP];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) acc[r] = 0.f;
+  Block<U, RP> A, B;
 
   for (uint32_t t0 = 0; t0 < cpr; t0 += CT) {
     const uint32_t ct = (cpr - t0) < CT ? (cpr - t0) : CT;
     const bool last_tile = t0 + ct == cpr;
     const uint32_t nseg = (ct + 63u) >> 6;
-    const uint32_t nitems = nr * nseg;
-    const uint32_t nblk = (nitems + U - 1) / U;  // blocks of this wave in this tile
-    const uint32_t tg = (ct << 4) >> gs_log2;    // groups of this tile
-    const uint32_t g0 = (t0 << 4) >> gs_log2;    // first group of this tile
+    const uint32_t nitems = ngrp * nseg;
+    const uint32_t nblk = (nitems + U - 1) / U;
+    const uint32_t tg = (ct << 4) >> gs_log2;
+    const uint32_t g0 = (t0 << 4) >> gs_log2;
     const uint32_t last_lanes = ct - ((nseg - 1u) << 6);
+    // lanes past the end of a partial last segment load nothing and read a
+    // staged (finite) scale/bias entry; their activations are zero
     const uint32_t vo_w_last = TAIL && lane >= last_lanes ? kOutOfRange : vo_w;
-    // lanes past the end of a partial last segment read a staged (finite)
-    // scale/bias entry; their codes and activations are zero
-    const uint32_t lane_grp_last = TAIL && lane >= last_lanes ? 0u : lane_grp;
-    const uint32_t seg_bytes0 = t0 << 4;
+    const uint32_t v_sb_last = TAIL && lane >= last_lanes ? 0u : v_sb;
+    const uint32_t grp_skip = RP * K - (nseg << 10);  // to the next row group (mod 2^32)
+    const uint32_t last_off = (nr ? nr - 1u : 0u) * K + (t0 << 4) + ((nseg - 1u) << 10);
 
-    // item (row, seg) iterators, wave-uniform
-    uint32_t i_row = 0, i_seg = 0;
-    // Issue one block of U items.  Only the wave's final block can hold items
-    // past its last row; those are marked out of range in the per-lane offset
-    // (what the buffer bound is checked against), so the code stays
-    // branch-free.  The wave-uniform part of each offset is the scalar offset.
-    auto issue = [&](Block<U> &blk) {
+    uint32_t i_off = t0 << 4, i_seg = 0, i_grp = 0;
+    auto issue = [&](Block<U, RP> &blk) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const bool live = i_row < nr;
-        const uint32_t sw = live ? i_row * K + seg_bytes0 + (i_seg << 10) : 0u;
-        const uint32_t dead = live ? 0u : kOutOfRange;
-        const bool last = TAIL && i_seg == nseg - 1u;
-        const uint32_t vw = (last ? vo_w_last : vo_w) | dead;
-        blk.q[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vw, (int)sw, kAuxNontemporal);
-        if (++i_seg == nseg) { i_seg = 0; ++i_row; }
+        uint32_t vw = vo_w;
+        if constexpr (TAIL) vw = (i_seg == nseg - 1u) ? vo_w_last : vo_w;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          const bool live = i_grp < ngrp && i_grp * RP + r < nr;
+          const uint32_t sw = uniform(live ? i_off + r * K : last_off);
+          blk.q[u][r] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vw, (int)sw, kAuxNontemporal);
+        }
+        i_off += 1024u;
+        if (++i_seg == nseg) { i_seg = 0; ++i_grp; i_off += grp_skip; }
       }
     };
-    uint32_t c_row = 0, c_seg = 0;
-    auto consume = [&](const Block<U> &blk) {
+    uint32_t c_grp = 0, c_seg = 0;
+    auto consume = [&](const Block<U, RP> &blk) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (c_row < nr) {
-          const float4 *ap = act + (c_seg << 8) + lane;
+        if (c_grp < ngrp) {
+          const float4 *ap = reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(act) +
+                                                              uniform(c_seg << 12) + v_act);
           const float4 a0 = ap[0], a1 = ap[64], a2 = ap[128], a3 = ap[192];
-          const float S = ssum[(c_seg << 6) + lane];
-          const bool lastseg = TAIL && c_seg == nseg - 1u;
-          const uint32_t gi = c_row * tg + ((c_seg << 10) >> gs_log2) + (lastseg ? lane_grp_last : lane_grp);
-          const float sc = bf16_bits_to_f32(sbs[gi]);
-          const float bi = __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32(sbb[gi]));
-          const u32x4 w = blk.q[u];
-          // P' = sum (1024 + q) a over the lane's 16 codes (f16 codes, fp32 FMA)
-          float p = 0.f;
-          const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-          const float av[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
-                                a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+          const float S = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(ssum) +
+                                                           uniform(c_seg << 8) + v_s);
+          uint32_t vs = v_sb;
+          if constexpr (TAIL) vs = (c_seg == nseg - 1u) ? v_sb_last : v_sb;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f16x2 lo = __builtin_bit_cast(f16x2, f16_pair(words[i], 0x04010400u));
-            const f16x2 hi = __builtin_bit_cast(f16x2, f16_pair(words[i], 0x04030402u));
-            p = __builtin_fmaf((float)lo.x, av[4 * i + 0], p);
-            p = __builtin_fmaf((float)lo.y, av[4 * i + 1], p);
-            p = __builtin_fmaf((float)hi.x, av[4 * i + 2], p);
-            p = __builtin_fmaf((float)hi.y, av[4 * i + 3], p);
+          for (int r = 0; r < RP; ++r) {
+            const uint32_t row = c_grp * RP + r;
+            const uint32_t rs = row < nr ? row : 0u;
+            const float2 sbv = *reinterpret_cast<const float2 *>(
+                reinterpret_cast<const char *>(sb) + uniform((rs * tg + c_seg * gps) << 3) + vs);
+            const float p = run_dot(blk.q[u][r], a0, a1, a2, a3);
+            acc[r] = __builtin_fmaf(sbv.x, p, __builtin_fmaf(sbv.y, S, acc[r]));
           }
-          // sum (q s + b) a = s P' + (b - 1024 s) S
-          acc = __builtin_fmaf(sc, p, __builtin_fmaf(bi, S, acc));
-          if (c_seg == nseg - 1u) {  // this row's part of the tile is done
-            const float tot = wave_sum_lane63(acc);
-            if (lane == 63u) {
-              float v = t0 ? part[c_row] + tot : tot;
-              if (last_tile) {
-                if constexpr (EPI == kEpiSiluGateResid) v += bf16_bits_to_f32(resid[rbeg + c_row]);
-                y[rbeg + c_row] = to_bf16_bits(v);
-              } else {
-                part[c_row] = v;
+          if (c_seg == nseg - 1u) {  // the group's rows are done for this tile
+#pragma unroll
+            for (int r = 0; r < RP; ++r) {
+              const uint32_t row = c_grp * RP + r;
+              if (row < nr) {
+                const float tot = wave_sum_lane63(acc[r]);
+                if (lane == 63u) {
+                  float v = t0 ? part[row] + tot : tot;
+                  if (last_tile) {
+                    if constexpr (EPI == kEpiSiluGateResid) v += bf16_bits_to_f32(resid[rbeg + row]);
+                    y[rbeg + row] = to_bf16_bits(v);
+                  } else {
+                    part[row] = v;
+                  }
+                }
               }
+              acc[r] = 0.f;
             }
-            acc = 0.f;
           }
         }
-        if (++c_seg == nseg) { c_seg = 0; ++c_row; }
+        if (++c_seg == nseg) { c_seg = 0; ++c_grp; }
       }
     };
 
-    // 1. activation loads for this tile, this wave's scales and biases for
-    //    the tile, then the first weight block: all in flight together
-    u32x4 xv[kStagePerThread][2], uv[kStagePerThread][2];
+    // 1. activation loads, the first weight block, then this wave's scales
+    //    and biases for the tile: all in flight together
+    u32x4 xv[kStage][2], uv[kStage][2];
 #pragma unroll
-    for (int s = 0; s < kStagePerThread; ++s) {
-      const uint32_t e = tid + s * kGemvThreads;
+    for (int s = 0; s < kStage; ++s) {
+      const uint32_t e = tid + s * kThreads;
       const uint32_t off = e < ct ? (t0 + e) * 32u : kOutOfRange;
       xv[s][0] = buf_load_b128(rx, off);
       xv[s][1] = buf_load_b128(rx, off + 16u);
@@ -226,70 +254,65 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(
       }
     }
     if (nblk) issue(A);
-    // this wave's scales and biases for the tile: element e = (row, group)
-    // of the nr x tg slice, loaded up front (kSbPerLane per lane at a time)
     const uint32_t nsb = nr * tg;
+    const uint32_t tg_inv = (uint32_t)(0xFFFFFFFFu / tg) + 1u;  // e / tg == umulhi(e, tg_inv) for e < 2^16
     uint16_t sv[kSbPerLane], bv[kSbPerLane];
 #pragma unroll
     for (int j = 0; j < kSbPerLane; ++j) {
       const uint32_t e = lane + 64u * j;
-      const uint32_t r = e / tg, g = e - r * tg;
+      const uint32_t r = __umulhi(e, tg_inv), g = e - r * tg;
       const uint32_t src = e < nsb ? r * G + g0 + g : 0u;
       sv[j] = srow[src];
       bv[j] = brow[src];
     }
     if (t0) __syncthreads();  // everyone is done with the previous tile's activation
-    // 2. form the activation tile: [seg][4][64] float4 plus per-run sums;
-    //    runs past the end are written as zeros
+    // 2. form the activation tile; runs past the end are written as zeros
 #pragma unroll
-    for (int s = 0; s < kStagePerThread; ++s) {
-      const uint32_t e = tid + s * kGemvThreads;
+    for (int s = 0; s < kStage; ++s) {
+      const uint32_t e = tid + s * kThreads;
       if (e < (nseg << 6)) {
         const uint32_t wv[8] = {xv[s][0].x, xv[s][0].y, xv[s][0].z, xv[s][0].w,
                                 xv[s][1].x, xv[s][1].y, xv[s][1].z, xv[s][1].w};
-        float a[16];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          a[2 * i] = bf16_lo(wv[i]);
-          a[2 * i + 1] = bf16_hi(wv[i]);
-        }
+        uint32_t uw[8];
         if constexpr (EPI != kEpiNone) {
-          const uint32_t uw[8] = {uv[s][0].x, uv[s][0].y, uv[s][0].z, uv[s][0].w,
-                                  uv[s][1].x, uv[s][1].y, uv[s][1].z, uv[s][1].w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            a[2 * i] = silu_mul(a[2 * i], bf16_lo(uw[i]));
-            a[2 * i + 1] = silu_mul(a[2 * i + 1], bf16_hi(uw[i]));
-          }
+          uw[0] = uv[s][0].x; uw[1] = uv[s][0].y; uw[2] = uv[s][0].z; uw[3] = uv[s][0].w;
+          uw[4] = uv[s][1].x; uw[5] = uv[s][1].y; uw[6] = uv[s][1].z; uw[7] = uv[s][1].w;
         }
+        float4 *dst = act + (e >> 6) * 256u + (e & 63u);
         float sum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sum += a[i];
-        float4 *dst = act + ((e >> 6) << 8) + (e & 63u);
-#pragma unroll
-        for (int f = 0; f < 4; ++f) dst[f * 64] = make_float4(a[4 * f], a[4 * f + 1], a[4 * f + 2], a[4 * f + 3]);
+        for (int f = 0; f < 4; ++f) {  // four activations (one float4) at a time
+          float a0 = bf16_lo(wv[2 * f]), a1 = bf16_hi(wv[2 * f]);
+          float a2 = bf16_lo(wv[2 * f + 1]), a3 = bf16_hi(wv[2 * f + 1]);
+          if constexpr (EPI != kEpiNone) {
+            a0 = silu_mul(a0, bf16_lo(uw[2 * f]));
+            a1 = silu_mul(a1, bf16_hi(uw[2 * f]));
+            a2 = silu_mul(a2, bf16_lo(uw[2 * f + 1]));
+            a3 = silu_mul(a3, bf16_hi(uw[2 * f + 1]));
+          }
+          sum += a0; sum += a1; sum += a2; sum += a3;
+          dst[f * 64] = make_float4(a0, a1, a2, a3);
+        }
         ssum[e] = sum;
       }
     }
     __syncthreads();
-    // this wave's private scale/bias slice (no barrier needed: only this wave
-    // reads it, after writing it, and its previous tile is consumed)
+    // this wave's private (scale, bias - 1024 scale) slice: only this wave
+    // reads it, after writing it, and its previous tile is consumed
 #pragma unroll
     for (int j = 0; j < kSbPerLane; ++j) {
       const uint32_t e = lane + 64u * j;
       if (e < nsb) {
-        sbs[e] = sv[j];
-        sbb[e] = bv[j];
+        const float sc = bf16_bits_to_f32(sv[j]);
+        sb[e] = make_float2(sc, __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32(bv[j])));
       }
     }
-    for (uint32_t e = lane + 64u * kSbPerLane; e < nsb; e += 64u) {  // slices beyond kSbPerLane*64
+    for (uint32_t e = lane + 64u * kSbPerLane; e < nsb; e += 64u) {
       const uint32_t r = e / tg, g = e - r * tg;
-      sbs[e] = srow[r * G + g0 + g];
-      sbb[e] = brow[r * G + g0 + g];
+      const float sc = bf16_bits_to_f32(srow[r * G + g0 + g]);
+      sb[e] = make_float2(sc, __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32(brow[r * G + g0 + g])));
     }
-    // 3. two-stage pipeline: the next block is issued before the current one
-    //    is consumed; the only branches are the loop exits, so every issued
-    //    block is a live one
+    // 3. two-stage pipeline; the only branches are the loop exits
     for (uint32_t b = 0; b < nblk;) {
       if (b + 1 >= nblk) { consume(A); break; }
       issue(B);
@@ -303,10 +326,10 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(
   }
 }
 
-template <int EPI, bool TAIL>
+template <int EPI, int W, int RP, bool TAIL>
 hipError_t launch_cfg(const GemvCfg &cfg, hipStream_t stream, const WeightView &w, const uint16_t *xg,
                       const uint16_t *up, const uint16_t *resid, uint16_t *y) {
-  auto kern = k_gemv<EPI, kU, TAIL>;
+  auto kern = k_gemv<EPI, W, RP, kLoadsPerBlock / RP, TAIL>;
   static bool configured = false;  // raise the dynamic-LDS cap once per instantiation
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -314,29 +337,46 @@ hipError_t launch_cfg(const GemvCfg &cfg, hipStream_t stream, const WeightView &
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const size_t lds = lds_bytes(cfg, w.gs);
-  hipLaunchKernelGGL(kern, dim3(cfg.blocks), dim3(kGemvThreads), lds, stream,
+  hipLaunchKernelGGL(kern, dim3(cfg.blocks), dim3(64 * W), lds_bytes(cfg, w.gs), stream,
                      reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, xg, up, resid, y, w.N,
                      w.K, (uint32_t)__builtin_ctz(w.gs), cfg.ct, cfg.max_rows);
   return hipGetLastError();
 }
 
-GemvCfg choose_cfg(uint32_t N, uint32_t K, uint32_t gs, uint32_t blocks_override = 0) {
+template <int EPI, bool TAIL>
+hipError_t launch_shape(const GemvCfg &cfg, hipStream_t stream, const WeightView &w, const uint16_t *xg,
+                        const uint16_t *up, const uint16_t *resid, uint16_t *y) {
+  if (cfg.waves == 16) {
+    return cfg.rp == 2 ? launch_cfg<EPI, 16, 2, TAIL>(cfg, stream, w, xg, up, resid, y)
+                       : launch_cfg<EPI, 16, 1, TAIL>(cfg, stream, w, xg, up, resid, y);
+  }
+  return cfg.rp == 2 ? launch_cfg<EPI, 8, 2, TAIL>(cfg, stream, w, xg, up, resid, y)
+                     : launch_cfg<EPI, 8, 1, TAIL>(cfg, stream, w, xg, up, resid, y);
+}
+
+// Launch shape (measured on MI355X): short rows (K <= 8192) run two 8-wave
+// workgroups per CU; long rows one 16-wave workgroup per CU, so one
+// activation tile serves 16 waves, with two rows side by side when every
+// wave owns at least two.
+GemvCfg choose_cfg(uint32_t N, uint32_t K, uint32_t gs, int waves = 0, int rp = 0, uint32_t wg_per_cu = 0) {
   const uint32_t cus = (uint32_t)device_cu_count();
   GemvCfg c{};
-  // One workgroup of 8 waves per CU; every wave streams a contiguous range of rows.
-  c.blocks = blocks_override ? blocks_override : cus;
-  const uint32_t need = (N + kWaves - 1) / kWaves;
+  c.waves = waves ? waves : (K <= 8192u ? 8 : 16);
+  const uint32_t per_cu = wg_per_cu ? wg_per_cu : (c.waves == 8 ? 2u : 1u);
+  const uint32_t W = (uint32_t)c.waves;
+  c.blocks = per_cu * cus;
+  const uint32_t need = (N + W - 1) / W;
   if (c.blocks > need) c.blocks = need;
-  const uint32_t enough = (N + kWaves * kMaxRowsPerWave - 1) / (kWaves * kMaxRowsPerWave);
-  if (c.blocks < enough) c.blocks = enough;  // at most kMaxRowsPerWave rows per wave
-  const uint32_t tw = c.blocks * kWaves;
+  const uint32_t enough = (N + W * kMaxRowsPerWave - 1) / (W * kMaxRowsPerWave);
+  if (c.blocks < enough) c.blocks = enough;
+  const uint32_t tw = c.blocks * W;
   c.max_rows = (N + tw - 1) / tw;
+  c.rp = rp ? rp : (c.waves == 16 && N / tw >= 2u ? 2 : 1);
   const uint32_t cpr = K / 16u;
-  // Tile K so that the activation tile and the waves' scale/bias slices fit.
+  const size_t budget = kLdsPerCu / per_cu;
   for (uint32_t ntiles = (cpr + kTileRunsMax - 1) / kTileRunsMax;; ++ntiles) {
     c.ct = ((cpr + ntiles - 1) / ntiles + 63u) / 64u * 64u;
-    if (lds_bytes(c, gs) <= kLdsBudget || c.ct == 64u) break;
+    if (lds_bytes(c, gs) <= budget || c.ct == 64u) break;
   }
   c.tail = (cpr % 64u) != 0;
   return c;
@@ -346,15 +386,15 @@ hipError_t launch_gemv_with(const GemvCfg &cfg, const WeightView &w, GemvEpilogu
                             const uint16_t *up, const uint16_t *x_resid, uint16_t *y, hipStream_t stream) {
   if (cfg.tail) {
     switch (epi) {
-      case kEpiNone: return launch_cfg<kEpiNone, true>(cfg, stream, w, x_or_gate, nullptr, nullptr, y);
-      case kEpiSiluGate: return launch_cfg<kEpiSiluGate, true>(cfg, stream, w, x_or_gate, up, nullptr, y);
-      default: return launch_cfg<kEpiSiluGateResid, true>(cfg, stream, w, x_or_gate, up, x_resid, y);
+      case kEpiNone: return launch_shape<kEpiNone, true>(cfg, stream, w, x_or_gate, nullptr, nullptr, y);
+      case kEpiSiluGate: return launch_shape<kEpiSiluGate, true>(cfg, stream, w, x_or_gate, up, nullptr, y);
+      default: return launch_shape<kEpiSiluGateResid, true>(cfg, stream, w, x_or_gate, up, x_resid, y);
     }
   }
   switch (epi) {
-    case kEpiNone: return launch_cfg<kEpiNone, false>(cfg, stream, w, x_or_gate, nullptr, nullptr, y);
-    case kEpiSiluGate: return launch_cfg<kEpiSiluGate, false>(cfg, stream, w, x_or_gate, up, nullptr, y);
-    default: return launch_cfg<kEpiSiluGateResid, false>(cfg, stream, w, x_or_gate, up, x_resid, y);
+    case kEpiNone: return launch_shape<kEpiNone, false>(cfg, stream, w, x_or_gate, nullptr, nullptr, y);
+    case kEpiSiluGate: return launch_shape<kEpiSiluGate, false>(cfg, stream, w, x_or_gate, up, nullptr, y);
+    default: return launch_shape<kEpiSiluGateResid, false>(cfg, stream, w, x_or_gate, up, x_resid, y);
   }
 }
 
