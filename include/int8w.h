@@ -53,14 +53,14 @@ typedef struct int8w_weight {
   const uint16_t *scales; /* [out_features, in_features/group_size] BF16 (device) */
   const uint16_t *biases; /* [out_features, in_features/group_size] BF16 (device) */
   uint32_t out_features;  /* N >= 1 */
-  uint32_t in_features;   /* K >= group_size, K % group_size == 0 */
+  uint32_t in_features;   /* K >= group_size, K % group_size == 0, K <= 2^24 */
   uint32_t group_size;    /* 32, 64 or 128 */
 } int8w_weight;
 
 enum {
   INT8W_OK = 0,
   INT8W_ERR_NULL = -1,        /* a required pointer is NULL */
-  INT8W_ERR_SHAPE = -2,       /* zero dimension, in_features % group_size != 0, size overflow */
+  INT8W_ERR_SHAPE = -2,       /* zero dimension, in_features % group_size != 0, N*K/16 >= 2^31, K > 2^24 */
   INT8W_ERR_UNSUPPORTED = -3, /* group_size not in {32, 64, 128} */
   INT8W_ERR_ALIGN = -4,       /* a pointer violates the alignment rule above */
   INT8W_ERR_ALIAS = -5,       /* an output overlaps an input */
@@ -103,7 +103,7 @@ int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const
 
 /* gemm: Y = X W^T.  X is BF16 [m, in_features] and Y BF16 [m, out_features],
  * both contiguous row-major.  Y[i,n] = RNE_bf16(sum_k w[n,k] * X[i,k]) with fp32
- * accumulation; for m > 64 the weight enters the matrix cores as
+ * accumulation; for m > 16 the weight enters the matrix cores as
  * RNE_bf16(w[n,k]) (the dequantize_to value).  m == 0 enqueues nothing and
  * returns INT8W_OK. */
 int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, uint64_t stream);

@@ -68,8 +68,9 @@ int validate(const int8w_weight *w) {
     return fail(INT8W_ERR_SHAPE, "in_features %u is not a whole number of 4-code words", w->in_features);
   if (w->group_size != 32 && w->group_size != 64 && w->group_size != 128)
     return fail(INT8W_ERR_UNSUPPORTED, "group_size %u not supported (32, 64 or 128)", w->group_size);
-  // 16-code runs are indexed with 32-bit integers (with headroom for grid strides).
-  if ((uint64_t)w->out_features * (w->in_features / 16u) > 0x7FFFFFFFull)
+  // Code runs are indexed with 32-bit integers, and per-wave buffer windows
+  // (a few rows) must stay below 2^31 bytes.
+  if ((uint64_t)w->out_features * (w->in_features / 16u) > 0x7FFFFFFFull || w->in_features > (1u << 24))
     return fail(INT8W_ERR_SHAPE, "weight too large (%u x %u codes)", w->out_features, w->in_features);
   if (!aligned(w->packed, 16)) return fail(INT8W_ERR_ALIGN, "packed is not 16-byte aligned");
   if (!aligned(w->scales, 2) || !aligned(w->biases, 2))
