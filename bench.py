@@ -39,7 +39,10 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 LLC_BYTES = 256 << 20
 METRIC = "int8 GEMV achieved HBM GB/s (% of peak) at m=1; prefill GEMM TFLOP/s"
-GEMV_SOURCE = os.path.join(ROOT, "weight_only_quantized_int8_amd", "csrc", "gemv.hip")
+# the sources the gate/up gemv kernel is compiled from (its traffic record is
+# void once any of them changes)
+GEMV_SOURCES = [os.path.join(ROOT, "weight_only_quantized_int8_amd", "csrc", f)
+                for f in ("gemv.hip", "common.h", "launch.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_gate_up_traffic.json")
 
 
@@ -76,9 +79,12 @@ def copies_for(bytes_per_copy):
     return max(2, -(-2 * LLC_BYTES // bytes_per_copy))
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 # ---------------------------------------------------------------- the decode layer (the step)
@@ -241,31 +247,33 @@ def traffic_record():
         return None
     with open(TRAFFIC_FILE) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != source_sha(GEMV_SOURCE):
+    if rec.get("kernel_source_sha256") != source_sha(GEMV_SOURCES):
         return None  # the kernel changed since the counters were taken
     return rec
 
 
 # ---------------------------------------------------------------- main
 
-def dominant_graph(dl):
-    """A HIP graph of the gate and up gemv of every rotated layer (the dominant
-    kernel, launched back to back with no host launch latency between them)."""
+def dominant_graph(dl, passes=16):
+    """A HIP graph of `passes` rounds of the gate and up gemv over every rotated
+    layer: the dominant kernel launched back to back, with no host launch
+    latency between launches and the per-replay launch cost spread over many."""
     for li in range(len(dl.layers)):
         for name in DOMINANT:
             dl.call(li, name, "gemv")
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for li in range(len(dl.layers)):
-            for name in DOMINANT:
-                dl.call(li, name, "gemv")
+        for _ in range(passes):
+            for li in range(len(dl.layers)):
+                for name in DOMINANT:
+                    dl.call(li, name, "gemv")
     g.replay()
     torch.cuda.synchronize()
-    return g, len(dl.layers) * len(DOMINANT)
+    return g, passes * len(dl.layers) * len(DOMINANT)
 
 
-def profile_only(dev, replays=10):
+def profile_only(dev, replays=2):
     """For rocprofv3: the dominant kernel exactly as timed region 2 runs it
     (graph replays of the gate/up gemv only), then a plain 256 MiB device copy
     that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
@@ -280,7 +288,7 @@ def profile_only(dev, replays=10):
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_only": True, "gemv_launches": per_replay * (replays + 2),
+    print(json.dumps({"profile_only": True, "gemv_launches": per_replay * (replays + 1) + per_replay // 16,
                       "calibration_copy_bytes": src.numel()}), flush=True)
 
 
@@ -345,7 +353,7 @@ def main():
     # ---- timed region 2: the dominant kernel alone, back to back (see
     # dominant_graph); HIP events on the launch stream around the replays.
     g_dom, dom_per_replay = dominant_graph(dl)
-    reps = max(1, args.steps // dom_per_replay * 2)
+    reps = max(2, -(-2 * args.steps // dom_per_replay))
     s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s2.record()
     for _ in range(reps):
