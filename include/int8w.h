@@ -88,6 +88,20 @@ int int8_dequantize_to(const int8w_weight *w, uint16_t *out, uint64_t stream);
  * y[n] = RNE_bf16(sum_k w[n,k] * x[k]), accumulated in fp32. */
 int int8_gemv(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint64_t stream);
 
+/* gemv_multi: y[i] = W[i] x for count weights (1 <= count <= INT8W_MAX_MULTI)
+ * that share in_features and group_size, in one launch -- the projections of
+ * one activation (q, k and v; gate and up) that the page's gemv method runs
+ * one call at a time.  Each y[i] is computed with int8_gemv's arithmetic and
+ * meets the same bound (the split of in_features into on-chip tiles, and so
+ * the fp32 rounding, may differ).  `w` and `y` are HOST arrays of count
+ * entries; y[i] is a device buffer of at least w[i].out_features BF16
+ * elements.  Outputs must not overlap each other, x or any weight.
+ * INT8W_ERR_SHAPE for count outside 1..INT8W_MAX_MULTI or mismatched
+ * in_features / group_size. */
+#define INT8W_MAX_MULTI 4
+int int8_gemv_multi(const int8w_weight *w, uint32_t count, const uint16_t *x, uint16_t *const *y,
+                    uint64_t stream);
+
 /* gemv_silu_gate: y = W (silu(gate) * up) in one launch, silu(g) = g/(1+e^-g).
  * gate and up are BF16 [in_features]; the product silu(gate)*up is formed in
  * fp32 on chip and never written to memory.  y as for int8_gemv. */

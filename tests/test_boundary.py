@@ -157,3 +157,32 @@ def test_wrapper_applies_load_rules_on_tensors():
         B.Int8Weight(p, s, s, 48)
     with pytest.raises(ValueError, match="one GPU"):
         B.Int8Weight(p, s, s, 32)  # CPU tensors are refused before any call
+
+
+def test_gemv_multi_rejects():
+    q, k = desc(N=64, K=256, gs=64), desc(N=16, K=256, gs=64, packed=8 * A16, scales=9 * A16, biases=10 * A16)
+    x, y0, y1 = 4 * A16, 5 * A16, 6 * A16
+    rc, msg = err(B.int8_gemv_multi([], x, [], 0))
+    assert rc == B.INT8W_ERR_SHAPE and "count 0" in msg
+    five = [desc(packed=(20 + 3 * i) * A16, scales=(21 + 3 * i) * A16, biases=(22 + 3 * i) * A16) for i in range(5)]
+    rc, msg = err(B.int8_gemv_multi(five, x, [(40 + i) * A16 for i in range(5)], 0))
+    assert rc == B.INT8W_ERR_SHAPE and "count 5" in msg
+    # every weight is validated; in_features and group_size must agree
+    assert err(B.int8_gemv_multi([q, desc(N=0)], x, [y0, y1], 0))[0] == B.INT8W_ERR_SHAPE
+    rc, msg = err(B.int8_gemv_multi([q, desc(N=16, K=512, packed=8 * A16, scales=9 * A16, biases=10 * A16)],
+                                    x, [y0, y1], 0))
+    assert rc == B.INT8W_ERR_SHAPE and "in_features" in msg
+    rc, msg = err(B.int8_gemv_multi([q, desc(N=16, K=256, gs=32, packed=8 * A16, scales=9 * A16, biases=10 * A16)],
+                                    x, [y0, y1], 0))
+    assert rc == B.INT8W_ERR_SHAPE and "group_size" in msg
+    # pointers
+    assert err(B.int8_gemv_multi([q, k], 0, [y0, y1], 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8_gemv_multi([q, k], x, [y0, 0], 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8_gemv_multi([q, k], x + 2, [y0, y1], 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8_gemv_multi([q, k], x, [y0, y1 + 1], 0))[0] == B.INT8W_ERR_ALIGN
+    # outputs: not over x, not over any weight, not over each other
+    assert err(B.int8_gemv_multi([q, k], x, [y0, x + 64], 0))[0] == B.INT8W_ERR_ALIAS
+    assert err(B.int8_gemv_multi([q, k], x, [y0, 8 * A16 + 16], 0))[0] == B.INT8W_ERR_ALIAS
+    assert err(B.int8_gemv_multi([q, k], x, [y0, 2 * A16], 0))[0] == B.INT8W_ERR_ALIAS
+    rc, msg = err(B.int8_gemv_multi([q, k], x, [y0, y0 + 2 * 64 - 2], 0))
+    assert rc == B.INT8W_ERR_ALIAS and "y[0] and y[1]" in msg

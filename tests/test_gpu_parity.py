@@ -86,6 +86,10 @@ GEMV_SHAPES = [
     (7, 20480, 128),      # K over one LDS tile (two tiles)
     (3000, 40960, 32),    # three LDS tiles, many rows
     (1, 32, 32),          # degenerate: one row, one group
+    (5, 4128, 32),        # rows split over waves, partial last segment
+    (300, 1056, 32),      # two segments, the second with two runs
+    (3, 16384, 128),      # the largest K of one LDS tile
+    (77, 8224, 32),       # 16-wave workgroups, ragged segment
 ]
 
 
@@ -101,6 +105,51 @@ def test_gemv(N, K, gs):
     assert_close(dev_to_bits(y), y_ref, A, f"gemv {N}x{K} gs{gs}")
 
 
+@pytest.mark.parametrize("N,K,gs", [(1024, 4096, 64), (5, 4128, 32), (14336, 4096, 64), (33, 96, 32)])
+def test_gemv_writes_exactly_n_outputs(N, K, gs):
+    log(f"gemv guard N={N} K={K} gs={gs}")
+    w, rng = make_weight(21_000 + N + K + gs, N, K, gs)
+    x = synth.gen_act(rng, K)
+    W = upload(w)
+    buf = torch.full((N + 64,), 1.5, dtype=torch.bfloat16, device="cuda")
+    W.gemv(bits_to_dev(x), buf[:N])
+    _sync()
+    assert (buf[N:].float().cpu() == 1.5).all()
+    y_ref, A = oracle.gemv(w.packed, w.scales, w.biases, gs, x)
+    assert_close(dev_to_bits(buf[:N]), y_ref, A, f"gemv guard {N}x{K} gs{gs}")
+
+
+MULTI_CASES = [
+    ([4096, 1024, 1024], 4096, 64),   # q, k, v of an 8B layer
+    ([14336, 14336], 4096, 64),       # gate and up
+    ([33, 7, 100, 1], 96, 32),        # four ragged weights
+    ([300, 5], 20480, 128),           # two LDS tiles
+    ([77, 3000], 4128, 32),           # partial last segment
+    ([1], 32, 32),
+]
+
+
+@pytest.mark.parametrize("ns,K,gs", MULTI_CASES)
+def test_gemv_multi(ns, K, gs):
+    from weight_only_quantized_int8_amd import gemv_multi
+    log(f"gemv_multi ns={ns} K={K} gs={gs}")
+    ws, Ws = [], []
+    rng = None
+    for i, N in enumerate(ns):
+        w, rng_i = make_weight(25_000 + 17 * i + N + K + gs, N, K, gs)
+        ws.append(w)
+        Ws.append(upload(w))
+        rng = rng or rng_i
+    x = synth.gen_act(rng, K)
+    guards = [torch.full((N + 32,), 1.5, dtype=torch.bfloat16, device="cuda") for N in ns]
+    ys = gemv_multi(Ws, bits_to_dev(x), [g[:N] for g, N in zip(guards, ns)])
+    _sync()
+    for i, (w, y, g, N) in enumerate(zip(ws, ys, guards, ns)):
+        assert (g[N:].float().cpu() == 1.5).all(), f"weight {i} wrote past its output"
+        y_ref, A = oracle.gemv(w.packed, w.scales, w.biases, gs, x)
+        assert_close(dev_to_bits(y), y_ref, A, f"gemv_multi[{i}] {N}x{K} gs{gs}")
+
+
 GATED_SHAPES = [
     (256, 512, 64),
     (4096, 14336, 64),    # 8B down projection
@@ -108,6 +157,8 @@ GATED_SHAPES = [
     (1000, 3072, 32),
     (33, 96, 32),
     (5, 36864, 64),       # K over one LDS tile
+    (77, 4128, 32),       # rows split over waves, partial last segment
+    (3, 16384, 128),
 ]
 
 

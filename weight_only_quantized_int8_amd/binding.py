@@ -37,8 +37,9 @@ ERROR_NAMES = {
 
 EXPORTED = (
     "int8w_validate", "int8w_storage_bytes", "int8_dequantize_to", "int8_gemv", "int8_gemv_silu_gate",
-    "int8_gemv_silu_gate_resid", "int8_gemm", "int8w_last_error",
+    "int8_gemv_silu_gate_resid", "int8_gemm", "int8_gemv_multi", "int8w_last_error",
 )
+MAX_MULTI = 4  # INT8W_MAX_MULTI
 
 
 class Int8wError(RuntimeError):
@@ -93,6 +94,8 @@ def load_library() -> ctypes.CDLL:
     lib.int8_gemv_silu_gate_resid.restype = ctypes.c_int
     lib.int8_gemm.argtypes = [W, P, P, ctypes.c_uint32, u64]
     lib.int8_gemm.restype = ctypes.c_int
+    lib.int8_gemv_multi.argtypes = [W, ctypes.c_uint32, P, ctypes.POINTER(P), u64]
+    lib.int8_gemv_multi.restype = ctypes.c_int
     lib.int8w_last_error.argtypes = []
     lib.int8w_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -133,6 +136,14 @@ def int8_gemv_silu_gate_resid(desc: WeightDesc, gate: int, up: int, x_resid: int
 
 def int8_gemm(desc: WeightDesc, x: int, y: int, m: int, stream: int) -> int:
     return load_library().int8_gemm(ctypes.byref(desc), x, y, m, stream)
+
+
+def int8_gemv_multi(descs, x: int, ys, stream: int) -> int:
+    """descs: sequence of WeightDesc; ys: sequence of device addresses (same length)."""
+    n = len(descs)
+    arr = (WeightDesc * max(n, 1))(*descs)
+    yarr = (ctypes.c_void_p * max(n, 1))(*ys)
+    return load_library().int8_gemv_multi(arr, n, x, yarr, stream)
 
 
 # ---- tensor-level wrapper -----------------------------------------------------------------------
@@ -244,3 +255,23 @@ class Int8Weight:
         _need_bf16(y, "Y", m * self.out_features, self.device)
         _check(int8_gemm(self.desc, x.data_ptr(), y.data_ptr(), m, _stream_of(self.device)))
         return y
+
+
+def gemv_multi(weights, x: torch.Tensor, ys=None):
+    """y_i = W_i x for up to four Int8Weight sharing in_features and group_size, in one launch."""
+    weights = list(weights)
+    if not weights:
+        raise ValueError("gemv_multi needs at least one weight")
+    dev = weights[0].device
+    _need_bf16(x, "x", weights[0].in_features, dev)
+    if ys is None:
+        ys = [torch.empty(w.out_features, dtype=torch.bfloat16, device=dev) for w in weights]
+    ys = list(ys)
+    if len(ys) != len(weights):
+        raise ValueError("gemv_multi: one output per weight")
+    for w, y in zip(weights, ys):
+        if w.device != dev:
+            raise ValueError("gemv_multi: weights on different devices")
+        _need_bf16(y, "y", w.out_features, dev)
+    _check(int8_gemv_multi([w.desc for w in weights], x.data_ptr(), [y.data_ptr() for y in ys], _stream_of(dev)))
+    return ys

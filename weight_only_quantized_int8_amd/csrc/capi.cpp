@@ -164,6 +164,38 @@ int int8_gemv(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint64_t st
                        as_stream(stream));
 }
 
+int int8_gemv_multi(const int8w_weight *w, uint32_t count, const uint16_t *x, uint16_t *const *y,
+                    uint64_t stream) {
+  if (!w || !y || !x) return fail(INT8W_ERR_NULL, "weights, x or y is NULL");
+  if (count == 0 || count > INT8W_MAX_MULTI)
+    return fail(INT8W_ERR_SHAPE, "count %u outside 1..%d", count, INT8W_MAX_MULTI);
+  WeightView views[INT8W_MAX_MULTI];
+  Range ins[3 * INT8W_MAX_MULTI + 1];
+  for (uint32_t i = 0; i < count; ++i) {
+    int rc = validate(&w[i]);
+    if (rc) return rc;
+    if (w[i].in_features != w[0].in_features || w[i].group_size != w[0].group_size)
+      return fail(INT8W_ERR_SHAPE, "weight %u has in_features %u / group_size %u, weight 0 has %u / %u", i,
+                  w[i].in_features, w[i].group_size, w[0].in_features, w[0].group_size);
+    if (!y[i]) return fail(INT8W_ERR_NULL, "y[%u] is NULL", i);
+    if (!aligned(y[i], 2)) return fail(INT8W_ERR_ALIGN, "y[%u] is not 2-byte aligned", i);
+    weight_ranges(&w[i], ins + 3 * i);
+    views[i] = view(&w[i]);
+  }
+  if (!aligned(x, 16)) return fail(INT8W_ERR_ALIGN, "x is not 16-byte aligned");
+  ins[3 * count] = range("x", x, (uint64_t)w[0].in_features * 2);
+  for (uint32_t i = 0; i < count; ++i) {
+    const Range yi = range("y", y[i], (uint64_t)w[i].out_features * 2);
+    int rc = check_alias(yi, ins, 3 * (int)count + 1);
+    if (rc) return rc;
+    for (uint32_t j = 0; j < i; ++j)
+      if (overlaps(yi, range("y", y[j], (uint64_t)w[j].out_features * 2)))
+        return fail(INT8W_ERR_ALIAS, "outputs y[%u] and y[%u] overlap", j, i);
+  }
+  (void)hipGetLastError();
+  return finish_launch(launch_gemv_multi(views, y, count, x, as_stream(stream)), as_stream(stream));
+}
+
 static int gemv_gated(const int8w_weight *w, const uint16_t *gate, const uint16_t *up, const uint16_t *x_resid,
                       uint16_t *y, uint64_t stream, bool with_resid) {
   int rc = validate(w);

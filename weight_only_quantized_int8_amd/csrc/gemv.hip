@@ -100,6 +100,20 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// The weights one launch streams: one for gemv and the gated variants, up to
+// kMaxTargets sharing one activation for gemv_multi (same in_features and
+// group size).  Passed by value as a kernel argument.
+constexpr int kMaxTargets = 4;
+struct GemvTargets {
+  const uint8_t *codes[kMaxTargets];
+  const uint16_t *scales[kMaxTargets];
+  const uint16_t *biases[kMaxTargets];
+  uint16_t *y[kMaxTargets];
+  uint32_t n[kMaxTargets];         // rows of each weight
+  uint32_t wave_end[kMaxTargets];  // waves [wave_end[i-1], wave_end[i]) stream weight i
+  uint32_t count;
+};
+
 template <int U, int RP>
 struct Block {
   u32x4 q[U][RP];
@@ -111,13 +125,14 @@ struct Block {
 //   sb    [W][max_rows][TG] float2   each wave's (scale, bias - 1024 scale)
 //   part  [W][max_rows] float        row partial sums across K-tiles
 template <int EPI, int W, int RP, int U, bool TAIL>
-__global__ __launch_bounds__(64 * W) void k_gemv(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ xg,
-    const uint16_t *__restrict__ up, const uint16_t *resid, uint16_t *y, uint32_t N, uint32_t K,
-    uint32_t gs_log2, uint32_t tile_runs, uint32_t max_rows) {
-  // y may be resid itself (in-place residual): each output element reads its
-  // own residual before it is written, by the same lane.
+__device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+                                          const uint16_t *__restrict__ biases, uint16_t *y, uint32_t N,
+                                          uint32_t lw, uint32_t TW, const uint16_t *__restrict__ xg,
+                                          const uint16_t *__restrict__ up, const uint16_t *resid, uint32_t K,
+                                          uint32_t gs_log2, uint32_t tile_runs, uint32_t max_rows) {
+  // This wave is wave lw of the TW waves that stream the N rows of one
+  // weight.  y may be resid itself (in-place residual): each output element
+  // reads its own residual before it is written, by the same lane.
   constexpr int kThreads = 64 * W;
   constexpr int kStage = (int)(kTileRunsMax + kThreads - 1) / kThreads;  // runs staged per thread
   extern __shared__ float4 lds4[];
@@ -132,11 +147,9 @@ __global__ __launch_bounds__(64 * W) void k_gemv(
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
   const uint32_t wave = uniform(tid >> 6);
-  const uint32_t gw = blockIdx.x * W + wave;
-  const uint32_t TW = gridDim.x * W;
   const uint32_t rq = N / TW, rr = N % TW;  // the first rr waves own rq + 1 rows
-  const uint32_t rbeg = gw * rq + (gw < rr ? gw : rr);
-  const uint32_t nr = rq + (gw < rr ? 1u : 0u);
+  const uint32_t rbeg = lw * rq + (lw < rr ? lw : rr);
+  const uint32_t nr = lw < TW ? rq + (lw < rr ? 1u : 0u) : 0u;
   const uint32_t ngrp = (nr + RP - 1) / RP;  // row groups of RP rows
   const uint32_t cpr = K >> 4;
   const uint32_t G = K >> gs_log2;
@@ -145,8 +158,10 @@ __global__ __launch_bounds__(64 * W) void k_gemv(
   const auto rw = make_rsrc(codes + (size_t)rbeg * K, nr * K);
   const auto rx = make_rsrc(xg, K * 2u);
   const auto ru = make_rsrc(EPI != kEpiNone ? up : xg, K * 2u);
-  const uint16_t *srow = scales + (size_t)rbeg * G;
-  const uint16_t *brow = biases + (size_t)rbeg * G;
+  // a wave without rows still issues its (unused) scale/bias loads: point
+  // them at the weight's first row
+  const uint16_t *srow = scales + (size_t)(nr ? rbeg : 0u) * G;
+  const uint16_t *brow = biases + (size_t)(nr ? rbeg : 0u) * G;
   float2 *sb = sb_all + wave * max_rows * TG;
   float *part = part_all + wave * max_rows;
 
@@ -186,9 +201,12 @@ __global__ __launch_bounds__(64 * W) void k_gemv(
         if constexpr (TAIL) vw = (i_seg == nseg - 1u) ? vo_w_last : vo_w;
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
+          // past the wave's rows a load re-reads the last segment of its last
+          // row (last_off), with that segment's lane mask
           const bool live = i_grp < ngrp && i_grp * RP + r < nr;
           const uint32_t sw = uniform(live ? i_off + r * K : last_off);
-          blk.q[u][r] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vw, (int)sw, kAuxNontemporal);
+          const uint32_t vwr = live ? vw : vo_w_last;
+          blk.q[u][r] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vwr, (int)sw, kAuxNontemporal);
         }
         i_off += 1024u;
         if (++i_seg == nseg) { i_seg = 0; ++i_grp; i_off += grp_skip; }
@@ -307,10 +325,23 @@ __global__ __launch_bounds__(64 * W) void k_gemv(
         sb[e] = make_float2(sc, __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32(bv[j])));
       }
     }
-    for (uint32_t e = lane + 64u * kSbPerLane; e < nsb; e += 64u) {
-      const uint32_t r = e / tg, g = e - r * tg;
-      const float sc = bf16_bits_to_f32(srow[r * G + g0 + g]);
-      sb[e] = make_float2(sc, __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32(brow[r * G + g0 + g])));
+    for (uint32_t e0 = 64u * kSbPerLane; e0 < nsb; e0 += 64u * kSbPerLane) {  // rows beyond the prefetch
+#pragma unroll
+      for (int j = 0; j < kSbPerLane; ++j) {
+        const uint32_t e = e0 + lane + 64u * j;
+        const uint32_t r = __umulhi(e, tg_inv), g = e - r * tg;
+        const uint32_t src = e < nsb ? r * G + g0 + g : 0u;
+        sv[j] = srow[src];
+        bv[j] = brow[src];
+      }
+#pragma unroll
+      for (int j = 0; j < kSbPerLane; ++j) {
+        const uint32_t e = e0 + lane + 64u * j;
+        if (e < nsb) {
+          const float sc = bf16_bits_to_f32(sv[j]);
+          sb[e] = make_float2(sc, __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32(bv[j])));
+        }
+      }
     }
     // 3. two-stage pipeline; the only branches are the loop exits
     for (uint32_t b = 0; b < nblk;) {
@@ -326,40 +357,126 @@ __global__ __launch_bounds__(64 * W) void k_gemv(
   }
 }
 
-template <int EPI, int W, int RP, bool TAIL>
-hipError_t launch_cfg(const GemvCfg &cfg, hipStream_t stream, const WeightView &w, const uint16_t *xg,
-                      const uint16_t *up, const uint16_t *resid, uint16_t *y) {
-  auto kern = k_gemv<EPI, W, RP, kLoadsPerBlock / RP, TAIL>;
-  static bool configured = false;  // raise the dynamic-LDS cap once per instantiation
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    configured = true;
+// gemv, gemv_silu_gate, gemv_silu_gate_resid: one weight, all waves.
+template <int EPI, int W, int RP, int U, bool TAIL>
+__global__ __launch_bounds__(64 * W) void k_gemv(const uint8_t *__restrict__ codes,
+                                                 const uint16_t *__restrict__ scales,
+                                                 const uint16_t *__restrict__ biases, const uint16_t *__restrict__ xg,
+                                                 const uint16_t *__restrict__ up, const uint16_t *resid, uint16_t *y,
+                                                 uint32_t N, uint32_t K, uint32_t gs_log2, uint32_t tile_runs,
+                                                 uint32_t max_rows) {
+  const uint32_t gw = blockIdx.x * W + uniform(threadIdx.x >> 6);
+  gemv_wave<EPI, W, RP, U, TAIL>(codes, scales, biases, y, N, gw, gridDim.x * W, xg, up, resid, K, gs_log2,
+                                 tile_runs, max_rows);
+}
+
+// gemv_multi: the waves are dealt to the weights of the launch in proportion
+// to their rows; each wave streams its share of one weight.
+template <int W, int RP, int U, bool TAIL>
+__global__ __launch_bounds__(64 * W) void k_gemv_multi(GemvTargets t, const uint16_t *__restrict__ xg, uint32_t K,
+                                                       uint32_t gs_log2, uint32_t tile_runs, uint32_t max_rows) {
+  const uint32_t gw = blockIdx.x * W + uniform(threadIdx.x >> 6);
+  uint32_t j = 0;
+#pragma unroll
+  for (int i = 0; i + 1 < kMaxTargets; ++i) j += (i + 1 < (int)t.count && gw >= t.wave_end[i]) ? 1u : 0u;
+  const uint8_t *codes = t.codes[0];
+  const uint16_t *scales = t.scales[0], *biases = t.biases[0];
+  uint16_t *y = t.y[0];
+  uint32_t N = t.n[0], wb = 0, we = t.wave_end[0];
+#pragma unroll
+  for (int i = 1; i < kMaxTargets; ++i) {
+    if (j == (uint32_t)i) {
+      codes = t.codes[i]; scales = t.scales[i]; biases = t.biases[i]; y = t.y[i];
+      N = t.n[i]; wb = t.wave_end[i - 1]; we = t.wave_end[i];
+    }
   }
-  hipLaunchKernelGGL(kern, dim3(cfg.blocks), dim3(64 * W), lds_bytes(cfg, w.gs), stream,
-                     reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, xg, up, resid, y, w.N,
-                     w.K, (uint32_t)__builtin_ctz(w.gs), cfg.ct, cfg.max_rows);
+  // waves past the last weight's share (the grid is whole workgroups) own no rows
+  gemv_wave<kEpiNone, W, RP, U, TAIL>(codes, scales, biases, y, N, gw - wb, we - wb, xg, xg, nullptr, K, gs_log2,
+                                      tile_runs, max_rows);
+}
+
+template <typename Kern>
+hipError_t raise_lds_cap(Kern kern, bool &configured) {
+  if (configured) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) configured = true;
+  return e;
+}
+
+template <int EPI, int W, int RP, bool TAIL>
+hipError_t launch_cfg(const GemvCfg &cfg, const GemvTargets &t, uint32_t K, uint32_t gs, const uint16_t *xg,
+                      const uint16_t *up, const uint16_t *resid, hipStream_t stream) {
+  static bool configured = false;  // raise the dynamic-LDS cap once per instantiation
+  const uint32_t gs_log2 = (uint32_t)__builtin_ctz(gs);
+  if (t.count == 1) {
+    auto kern = k_gemv<EPI, W, RP, kLoadsPerBlock / RP, TAIL>;
+    hipError_t e = raise_lds_cap(kern, configured);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(cfg.blocks), dim3(64 * W), lds_bytes(cfg, gs), stream, t.codes[0], t.scales[0],
+                       t.biases[0], xg, up, resid, t.y[0], t.n[0], K, gs_log2, cfg.ct, cfg.max_rows);
+  } else {
+    static bool configured_multi = false;
+    auto kern = k_gemv_multi<W, RP, kLoadsPerBlock / RP, TAIL>;
+    hipError_t e = raise_lds_cap(kern, configured_multi);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(cfg.blocks), dim3(64 * W), lds_bytes(cfg, gs), stream, t, xg, K, gs_log2, cfg.ct,
+                       cfg.max_rows);
+  }
   return hipGetLastError();
 }
 
 template <int EPI, bool TAIL>
-hipError_t launch_shape(const GemvCfg &cfg, hipStream_t stream, const WeightView &w, const uint16_t *xg,
-                        const uint16_t *up, const uint16_t *resid, uint16_t *y) {
+hipError_t launch_shape(const GemvCfg &cfg, const GemvTargets &t, uint32_t K, uint32_t gs, const uint16_t *xg,
+                        const uint16_t *up, const uint16_t *resid, hipStream_t stream) {
   if (cfg.waves == 16) {
-    return cfg.rp == 2 ? launch_cfg<EPI, 16, 2, TAIL>(cfg, stream, w, xg, up, resid, y)
-                       : launch_cfg<EPI, 16, 1, TAIL>(cfg, stream, w, xg, up, resid, y);
+    return cfg.rp == 2 ? launch_cfg<EPI, 16, 2, TAIL>(cfg, t, K, gs, xg, up, resid, stream)
+                       : launch_cfg<EPI, 16, 1, TAIL>(cfg, t, K, gs, xg, up, resid, stream);
   }
-  return cfg.rp == 2 ? launch_cfg<EPI, 8, 2, TAIL>(cfg, stream, w, xg, up, resid, y)
-                     : launch_cfg<EPI, 8, 1, TAIL>(cfg, stream, w, xg, up, resid, y);
+  return cfg.rp == 2 ? launch_cfg<EPI, 8, 2, TAIL>(cfg, t, K, gs, xg, up, resid, stream)
+                     : launch_cfg<EPI, 8, 1, TAIL>(cfg, t, K, gs, xg, up, resid, stream);
+}
+
+// Deal the launch's waves to its weights in proportion to their rows (every
+// weight at least one wave, none more waves than rows); returns the most
+// rows any wave owns.
+uint32_t deal_waves(uint32_t tw, const uint32_t *n, uint32_t count, uint32_t *wave_end) {
+  uint64_t total = 0;
+  for (uint32_t i = 0; i < count; ++i) total += n[i];
+  uint32_t share[kMaxTargets], used = 0;
+  for (uint32_t i = 0; i < count; ++i) {
+    share[i] = (uint32_t)((uint64_t)tw * n[i] / total);
+    if (share[i] == 0) share[i] = 1;
+    used += share[i];
+  }
+  while (used < tw) {  // leftover waves to the weight with the most rows per wave
+    uint32_t best = 0;
+    for (uint32_t i = 1; i < count; ++i)
+      if ((uint64_t)n[i] * share[best] > (uint64_t)n[best] * share[i]) best = i;
+    ++share[best];
+    ++used;
+  }
+  uint32_t acc = 0, max_rows = 0;
+  for (uint32_t i = 0; i < count; ++i) {
+    if (share[i] > n[i]) share[i] = n[i];
+    acc += share[i];
+    wave_end[i] = acc;
+    const uint32_t r = (n[i] + share[i] - 1) / share[i];
+    if (r > max_rows) max_rows = r;
+  }
+  for (uint32_t i = count; i < kMaxTargets; ++i) wave_end[i] = acc;
+  return max_rows;
 }
 
 // Launch shape (measured on MI355X): short rows (K <= 8192) run two 8-wave
 // workgroups per CU; long rows one 16-wave workgroup per CU, so one
 // activation tile serves 16 waves, with two rows side by side when every
 // wave owns at least two.
-GemvCfg choose_cfg(uint32_t N, uint32_t K, uint32_t gs, int waves = 0, int rp = 0, uint32_t wg_per_cu = 0) {
+GemvCfg choose_cfg(const uint32_t *n, uint32_t count, uint32_t K, uint32_t gs, uint32_t *wave_end, int waves = 0,
+                   int rp = 0, uint32_t wg_per_cu = 0) {
   const uint32_t cus = (uint32_t)device_cu_count();
+  uint32_t N = 0;
+  for (uint32_t i = 0; i < count; ++i) N += n[i];
   GemvCfg c{};
   c.waves = waves ? waves : (K <= 8192u ? 8 : 16);
   const uint32_t per_cu = wg_per_cu ? wg_per_cu : (c.waves == 8 ? 2u : 1u);
@@ -369,8 +486,12 @@ GemvCfg choose_cfg(uint32_t N, uint32_t K, uint32_t gs, int waves = 0, int rp = 
   if (c.blocks > need) c.blocks = need;
   const uint32_t enough = (N + W * kMaxRowsPerWave - 1) / (W * kMaxRowsPerWave);
   if (c.blocks < enough) c.blocks = enough;
+  for (;; ++c.blocks) {  // a weight's share of waves is rounded: keep every wave within kMaxRowsPerWave rows
+    c.max_rows = deal_waves(c.blocks * W, n, count, wave_end);
+    if (c.max_rows <= kMaxRowsPerWave) break;
+  }
   const uint32_t tw = c.blocks * W;
-  c.max_rows = (N + tw - 1) / tw;
+  c.blocks = (wave_end[count - 1] + W - 1) / W;  // no workgroup of idle waves only
   c.rp = rp ? rp : (c.waves == 16 && N / tw >= 2u ? 2 : 1);
   const uint32_t cpr = K / 16u;
   const size_t budget = kLdsPerCu / per_cu;
@@ -382,20 +503,44 @@ GemvCfg choose_cfg(uint32_t N, uint32_t K, uint32_t gs, int waves = 0, int rp = 
   return c;
 }
 
-hipError_t launch_gemv_with(const GemvCfg &cfg, const WeightView &w, GemvEpilogue epi, const uint16_t *x_or_gate,
-                            const uint16_t *up, const uint16_t *x_resid, uint16_t *y, hipStream_t stream) {
+hipError_t launch_targets(const GemvCfg &cfg, const GemvTargets &t, uint32_t K, uint32_t gs, GemvEpilogue epi,
+                          const uint16_t *x_or_gate, const uint16_t *up, const uint16_t *x_resid,
+                          hipStream_t stream) {
   if (cfg.tail) {
     switch (epi) {
-      case kEpiNone: return launch_shape<kEpiNone, true>(cfg, stream, w, x_or_gate, nullptr, nullptr, y);
-      case kEpiSiluGate: return launch_shape<kEpiSiluGate, true>(cfg, stream, w, x_or_gate, up, nullptr, y);
-      default: return launch_shape<kEpiSiluGateResid, true>(cfg, stream, w, x_or_gate, up, x_resid, y);
+      case kEpiNone: return launch_shape<kEpiNone, true>(cfg, t, K, gs, x_or_gate, nullptr, nullptr, stream);
+      case kEpiSiluGate: return launch_shape<kEpiSiluGate, true>(cfg, t, K, gs, x_or_gate, up, nullptr, stream);
+      default: return launch_shape<kEpiSiluGateResid, true>(cfg, t, K, gs, x_or_gate, up, x_resid, stream);
     }
   }
   switch (epi) {
-    case kEpiNone: return launch_shape<kEpiNone, false>(cfg, stream, w, x_or_gate, nullptr, nullptr, y);
-    case kEpiSiluGate: return launch_shape<kEpiSiluGate, false>(cfg, stream, w, x_or_gate, up, nullptr, y);
-    default: return launch_shape<kEpiSiluGateResid, false>(cfg, stream, w, x_or_gate, up, x_resid, y);
+    case kEpiNone: return launch_shape<kEpiNone, false>(cfg, t, K, gs, x_or_gate, nullptr, nullptr, stream);
+    case kEpiSiluGate: return launch_shape<kEpiSiluGate, false>(cfg, t, K, gs, x_or_gate, up, nullptr, stream);
+    default: return launch_shape<kEpiSiluGateResid, false>(cfg, t, K, gs, x_or_gate, up, x_resid, stream);
   }
+}
+
+GemvTargets make_targets(const WeightView *w, uint16_t *const *y, uint32_t count) {
+  GemvTargets t{};
+  for (uint32_t i = 0; i < kMaxTargets; ++i) {
+    const uint32_t s = i < count ? i : 0u;  // unused slots repeat the first weight
+    t.codes[i] = reinterpret_cast<const uint8_t *>(w[s].packed);
+    t.scales[i] = w[s].scales;
+    t.biases[i] = w[s].biases;
+    t.y[i] = y[s];
+    t.n[i] = w[s].N;
+  }
+  t.count = count;
+  return t;
+}
+
+// One launch over `count` weights with the same K and group size.
+hipError_t launch_gemv_list(const WeightView *w, uint16_t *const *y, uint32_t count, GemvEpilogue epi,
+                            const uint16_t *x_or_gate, const uint16_t *up, const uint16_t *x_resid,
+                            hipStream_t stream) {
+  GemvTargets t = make_targets(w, y, count);
+  const GemvCfg cfg = choose_cfg(t.n, count, w[0].K, w[0].gs, t.wave_end);
+  return launch_targets(cfg, t, w[0].K, w[0].gs, epi, x_or_gate, up, x_resid, stream);
 }
 
 }  // namespace
@@ -403,7 +548,12 @@ hipError_t launch_gemv_with(const GemvCfg &cfg, const WeightView &w, GemvEpilogu
 hipError_t launch_gemv(const WeightView &w, GemvEpilogue epi, const uint16_t *x_or_gate,
                        const uint16_t *up, const uint16_t *x_resid, uint16_t *y,
                        hipStream_t stream) {
-  return launch_gemv_with(choose_cfg(w.N, w.K, w.gs), w, epi, x_or_gate, up, x_resid, y, stream);
+  return launch_gemv_list(&w, &y, 1, epi, x_or_gate, up, x_resid, stream);
+}
+
+hipError_t launch_gemv_multi(const WeightView *w, uint16_t *const *y, uint32_t count, const uint16_t *x,
+                             hipStream_t stream) {
+  return launch_gemv_list(w, y, count, kEpiNone, x, nullptr, nullptr, stream);
 }
 
 }  // namespace int8w

@@ -26,6 +26,11 @@ enum GemvEpilogue { kEpiNone = 0, kEpiSiluGate = 1, kEpiSiluGateResid = 2 };
 hipError_t launch_gemv(const WeightView &w, GemvEpilogue epi, const uint16_t *x_or_gate,
                        const uint16_t *up, const uint16_t *x_resid, uint16_t *y, hipStream_t stream);
 
+// y_i = W_i x for count (1..4) weights with the same K and group size, in one
+// launch (each weight's rows streamed by its own share of the waves).
+hipError_t launch_gemv_multi(const WeightView *w, uint16_t *const *y, uint32_t count, const uint16_t *x,
+                             hipStream_t stream);
+
 // Y[m, N] = X[m, K] W^T for 2 <= m <= 16 (matrix cores, per-group rescale).
 hipError_t launch_gemm_smallm(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                               hipStream_t stream);
