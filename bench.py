@@ -1,16 +1,18 @@
 """Benchmark of the 8-bit affine weight-only linear layers on one MI355X.
 
-A step is one Llama-3-8B-shaped decode layer at m = 1, group_size 64: the
-gemv calls of q [4096,4096], k and v [1024,4096], o [4096,4096], gate and up
+A step is one Llama-3-8B-shaped decode layer at m = 1, group_size 64, in four
+launches: gemv_multi over q [4096,4096], k and v [1024,4096] (one activation,
+three weights), gemv on o [4096,4096], gemv_multi over gate and up
 [14336,4096], then gemv_silu_gate_resid on down [4096,14336] fed by the gate
 and up outputs.  Weights of several layers are cycled so that successive steps
 stream different bytes and the 256 MB last-level cache cannot serve them.
 
-value = algorithmic bytes per step (codes + scales + biases + activations in
-and out, per call) / measured time per step, in GB/s, with each layer's seven
-launches replayed as a HIP graph.  The roofline object reports the dominant
-kernel (the gate/up gemv) from HIP events around a batched, graph-replayed
-run of that kernel alone.  Secondary lines time dequantize_to and the
+value = algorithmic bytes per step (codes + scales + biases of every weight,
+plus the activations each launch reads and writes) / measured time per step,
+in GB/s, with each layer's launches replayed as a HIP graph.  The roofline
+object reports the dominant kernel (the gate+up gemv_multi launch) from HIP
+events around a batched, graph-replayed run of that launch alone.  Secondary
+lines: the same layer as seven single-weight launches, dequantize_to and the
 gated GEMV of the 70B-shaped FFN, the small-batch gemm (m = 2..16) and the
 prefill gemm (m = 512, 2048) in TFLOP/s.
 
@@ -23,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,7 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from weight_only_quantized_int8_amd import Int8Weight, load_library, synth  # noqa: E402
+from weight_only_quantized_int8_amd import Int8Weight, gemv_multi, load_library, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
@@ -89,25 +92,39 @@ def source_sha(paths):
 
 # ---------------------------------------------------------------- the decode layer (the step)
 
-LAYER = [  # name, N, K, kind
-    ("q", 4096, 4096, "gemv"),
-    ("k", 1024, 4096, "gemv"),
-    ("v", 1024, 4096, "gemv"),
-    ("o", 4096, 4096, "gemv"),
-    ("gate", 14336, 4096, "gemv"),
-    ("up", 14336, 4096, "gemv"),
-    ("down", 4096, 14336, "silu_gate_resid"),
+WEIGHTS = [  # name, N, K
+    ("q", 4096, 4096),
+    ("k", 1024, 4096),
+    ("v", 1024, 4096),
+    ("o", 4096, 4096),
+    ("gate", 14336, 4096),
+    ("up", 14336, 4096),
+    ("down", 4096, 14336),
 ]
+SHAPE = {name: (N, K) for name, N, K in WEIGHTS}
 GS = 64
-DOMINANT = ("gate", "up")  # the two 14336 x 4096 gemv launches of each step
+# launches of one step: (launch, kind, weights)
+FUSED = [
+    ("qkv", "multi", ("q", "k", "v")),
+    ("o", "gemv", ("o",)),
+    ("gate_up", "multi", ("gate", "up")),
+    ("down", "silu_gate_resid", ("down",)),
+]
+UNFUSED = [(n, "gemv", (n,)) for n in ("q", "k", "v", "o", "gate", "up")] + [("down", "silu_gate_resid", ("down",))]
+DOMINANT = "gate_up"  # the 2 x 14336 x 4096 launch of each step
 
 
-def call_bytes(N, K, kind):
-    return gemv_bytes(N, K, GS) if kind == "gemv" else gated_resid_bytes(N, K, GS)
+def launch_bytes(kind, names):
+    """Algorithmic bytes of one launch: every weight once, the activation(s) read once, the outputs written."""
+    K = SHAPE[names[0]][1]
+    if kind == "silu_gate_resid":
+        N = SHAPE[names[0]][0]
+        return gated_resid_bytes(N, K, GS)
+    return sum(N * K + 4 * N * K // GS + 2 * N for N, _ in (SHAPE[n] for n in names)) + 2 * K
 
 
-def layer_bytes():
-    return sum(call_bytes(N, K, kind) for _, N, K, kind in LAYER)
+def plan_bytes(plan):
+    return sum(launch_bytes(kind, names) for _, kind, names in plan)
 
 
 class DecodeLayers:
@@ -116,7 +133,7 @@ class DecodeLayers:
         self.layers = []
         for li in range(n_layers):
             d = {}
-            for si, (name, N, K, kind) in enumerate(LAYER):
+            for si, (name, N, K) in enumerate(WEIGHTS):
                 rng = np.random.Generator(np.random.PCG64(synth.make_seed(1, si) + 7919 * li))
                 w = synth.gen_weight(rng, N, K, GS)
                 d[name] = Int8Weight.from_arrays(w.packed, w.scales, w.biases, GS, device=dev)
@@ -124,26 +141,53 @@ class DecodeLayers:
         rng = np.random.Generator(np.random.PCG64(synth.make_seed(1, 99)))
         self.x = bits_dev(synth.gen_act(rng, 4096), dev)
         self.x_resid = bits_dev(synth.gen_act(rng, 4096), dev)
-        self.out = {name: torch.empty(N, dtype=torch.bfloat16, device=dev) for name, N, _, _ in LAYER}
+        self.out = {name: torch.empty(N, dtype=torch.bfloat16, device=dev) for name, N, _ in WEIGHTS}
 
-    def call(self, li, name, kind):
+    def launch(self, li, kind, names):
         L, o = self.layers[li], self.out
-        if kind == "gemv":
-            L[name].gemv(self.x, o[name])
+        if kind == "multi":
+            gemv_multi([L[n] for n in names], self.x, [o[n] for n in names])
+        elif kind == "gemv":
+            L[names[0]].gemv(self.x, o[names[0]])
         else:
-            L[name].gemv_silu_gate_resid(o["gate"], o["up"], self.x_resid, o[name])
+            L[names[0]].gemv_silu_gate_resid(o["gate"], o["up"], self.x_resid, o[names[0]])
 
-    def step(self, i, timings=None):
+    def step(self, i, plan, timings=None):
         li = i % len(self.layers)
-        for name, _, _, kind in LAYER:
+        for name, kind, names in plan:
             if timings is None:
-                self.call(li, name, kind)
+                self.launch(li, kind, names)
             else:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
-                self.call(li, name, kind)
+                self.launch(li, kind, names)
                 b.record()
                 timings.append((name, a, b))
+
+    def graphs(self, plan):
+        """One HIP graph per rotated layer holding that layer's launches."""
+        out = []
+        for li in range(len(self.layers)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(li, plan)
+            out.append(g)
+        for g in out:
+            g.replay()
+        torch.cuda.synchronize()
+        return out
+
+
+def time_graph_steps(graphs, steps):
+    """Seconds per step over `steps` replays (cycling the layers), HIP events on the replay stream."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
 
 
 def time_batches(fn, iters, reps=5):
@@ -214,11 +258,12 @@ def secondary(dev, quick):
 # ---------------------------------------------------------------- CPU oracle baseline
 
 def cpu_baseline(budget_s=12.0):
+    """The oracle computing the same step (each weight's product, the gated down projection)."""
     import oracle
-    layers = []
-    for si, (name, N, K, kind) in enumerate(LAYER):
+    ws = {}
+    for si, (name, N, K) in enumerate(WEIGHTS):
         rng = np.random.Generator(np.random.PCG64(synth.make_seed(1, si)))
-        layers.append((synth.gen_weight(rng, N, K, GS), kind))
+        ws[name] = synth.gen_weight(rng, N, K, GS)
     rng = np.random.Generator(np.random.PCG64(synth.make_seed(1, 99)))
     x = synth.gen_act(rng, 4096)
     r = synth.gen_act(rng, 4096)
@@ -227,17 +272,18 @@ def cpu_baseline(budget_s=12.0):
     n = 0
     t0 = time.perf_counter()
     while True:
-        for w, kind in layers:
-            if kind == "gemv":
-                oracle.gemv(w.packed, w.scales, w.biases, GS, x)
-            else:
-                oracle.gemv_silu_gate_resid(w.packed, w.scales, w.biases, GS, g, u, r)
+        for name in ("q", "k", "v", "o", "gate", "up"):
+            w = ws[name]
+            oracle.gemv(w.packed, w.scales, w.biases, GS, x)
+        w = ws["down"]
+        oracle.gemv_silu_gate_resid(w.packed, w.scales, w.biases, GS, g, u, r)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 200:
             break
-    return {"value": layer_bytes() * n / el / 1e9, "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{n} decode-layer steps (the same 7 calls, shapes and byte count as the GPU step), "
+    return {"value": plan_bytes(FUSED) * n / el / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{n} decode-layer steps (the same products, shapes and byte count as the GPU step), "
                       f"{el:.1f} s"}
 
 
@@ -252,33 +298,79 @@ def traffic_record():
     return rec
 
 
+def write_traffic_record(fetch_csv, write_csv):
+    """Turn two rocprofv3 --pmc counter_collection.csv files of `bench.py
+    --profile-only` (FETCH_SIZE, then WRITE_SIZE) into the traffic record:
+    median KiB per dispatch of the dominant kernel, scaled by what the same
+    counter reads for the 256 MiB calibration copy."""
+    import csv
+    import statistics
+
+    def per_kernel(path):
+        out = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                out.setdefault((row["Kernel_Name"], row["Grid_Size"]), []).append(float(row["Counter_Value"]))
+        return out
+
+    f, w = per_kernel(fetch_csv), per_kernel(write_csv)
+    dom = [k for k in f if "k_gemv_multi" in k[0]]
+    cal = [k for k in f if "copyBuffer" in k[0] and max(f[k]) > 100000]
+    if len(dom) != 1 or len(cal) != 1:
+        raise SystemExit(f"expected one dominant kernel and one calibration copy, got {dom} / {cal}")
+    dom, cal = dom[0], cal[0]
+    copy_kib = (256 << 20) / 1024
+    ff, wf = copy_kib / statistics.median(f[cal]), copy_kib / statistics.median(w[cal])
+    fk, wk = statistics.median(f[dom]), statistics.median(w[dom])
+    hbm = fk * 1024 * ff + wk * 1024 * wf
+    alg = launch_bytes("multi", ("gate", "up"))
+    short = re.search(r"(k_\w+<[^>]*>)", dom[0])
+    rec = {"kernel": (short.group(1) if short else dom[0]) + " (gemv_multi: gate+up, 2 x 14336x4096, group_size 64)",
+           "kernel_source_sha256": source_sha(GEMV_SOURCES),
+           "kernel_sources": [os.path.relpath(p, ROOT) for p in GEMV_SOURCES],
+           "dispatches": len(f[dom]),
+           "fetch_size_kib_median": fk, "write_size_kib_median": wk,
+           "calibration_copy_bytes": 256 << 20,
+           "calibration_fetch_size_kib": statistics.median(f[cal]),
+           "calibration_write_size_kib": statistics.median(w[cal]),
+           "fetch_factor": ff, "write_factor": wf,
+           "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": alg,
+           "ratio_to_algorithmic": hbm / alg}
+    with open(TRAFFIC_FILE, "w") as fo:
+        json.dump(rec, fo, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 # ---------------------------------------------------------------- main
 
 def dominant_graph(dl, passes=16):
-    """A HIP graph of `passes` rounds of the gate and up gemv over every rotated
-    layer: the dominant kernel launched back to back, with no host launch
-    latency between launches and the per-replay launch cost spread over many."""
+    """A HIP graph of `passes` rounds of the dominant launch over every rotated
+    layer: back to back, no host launch latency between launches, and the
+    per-replay launch cost spread over many launches."""
+    kind, names = next((k, n) for nm, k, n in FUSED if nm == DOMINANT)
     for li in range(len(dl.layers)):
-        for name in DOMINANT:
-            dl.call(li, name, "gemv")
+        dl.launch(li, kind, names)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for _ in range(passes):
             for li in range(len(dl.layers)):
-                for name in DOMINANT:
-                    dl.call(li, name, "gemv")
+                dl.launch(li, kind, names)
     g.replay()
     torch.cuda.synchronize()
-    return g, passes * len(dl.layers) * len(DOMINANT)
+    return g, passes * len(dl.layers)
+
+
+def n_rotated_layers():
+    per_layer = sum(N * K for _, N, K in WEIGHTS)
+    return max(2, -(-2 * LLC_BYTES // per_layer))
 
 
 def profile_only(dev, replays=2):
-    """For rocprofv3: the dominant kernel exactly as timed region 2 runs it
-    (graph replays of the gate/up gemv only), then a plain 256 MiB device copy
-    that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
-    per_layer = sum(N * K for _, N, K, _ in LAYER)
-    dl = DecodeLayers(dev, max(2, -(-2 * LLC_BYTES // per_layer)))
+    """For rocprofv3: the dominant launch exactly as timed region 2 runs it
+    (graph replays), then a plain 256 MiB device copy that calibrates the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    dl = DecodeLayers(dev, n_rotated_layers())
     g, per_replay = dominant_graph(dl)
     for _ in range(replays):
         g.replay()
@@ -288,7 +380,7 @@ def profile_only(dev, replays=2):
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_only": True, "gemv_launches": per_replay * (replays + 1) + per_replay // 16,
+    print(json.dumps({"profile_only": True, "dominant_launches": per_replay * (replays + 1) + per_replay // 16,
                       "calibration_copy_bytes": src.numel()}), flush=True)
 
 
@@ -300,9 +392,13 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--full-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--profile-only", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic record from two rocprofv3 --pmc runs of --profile-only, then exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic_record(*args.traffic_from)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -313,44 +409,23 @@ def main():
         profile_only(dev)
         return
 
-    per_layer = sum(N * K for _, N, K, _ in LAYER)
-    n_layers = max(2, -(-2 * LLC_BYTES // per_layer))
+    n_layers = n_rotated_layers()
     dl = DecodeLayers(dev, n_layers)
-    print(f"# decode layer: {len(LAYER)} calls, {layer_bytes() / 1e6:.1f} MB/step, {n_layers} layers rotated",
+    step_bytes = plan_bytes(FUSED)
+    print(f"# decode layer: {len(FUSED)} launches, {step_bytes / 1e6:.1f} MB/step, {n_layers} layers rotated",
           file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        dl.step(i)
+        dl.step(i, FUSED)
     torch.cuda.synchronize()
 
-    # one HIP graph per layer: its seven launches, replayed as a unit
-    graphs = []
-    if not args.eager:
-        for li in range(n_layers):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                dl.step(li)
-            graphs.append(g)
-        for g in graphs:
-            g.replay()
-        torch.cuda.synchronize()
-
-    # ---- timed region 1: K steps (graph replays, or eager launches)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # ---- timed region 1: K steps, each layer's launches replayed as one HIP graph
+    graphs = dl.graphs(FUSED)
     t0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        if graphs:
-            graphs[i % n_layers].replay()
-        else:
-            dl.step(i)
-    end.record()
-    torch.cuda.synchronize()
+    step_s = time_graph_steps(graphs, args.steps)
     wall = time.perf_counter() - t0
-    step_s = start.elapsed_time(end) / 1e3 / args.steps
-    value = layer_bytes() / step_s / 1e9
+    value = step_bytes / step_s / 1e9
 
-    # ---- timed region 2: the dominant kernel alone, back to back (see
+    # ---- timed region 2: the dominant launch alone, back to back (see
     # dominant_graph); HIP events on the launch stream around the replays.
     g_dom, dom_per_replay = dominant_graph(dl)
     reps = max(2, -(-2 * args.steps // dom_per_replay))
@@ -361,45 +436,51 @@ def main():
     e2.record()
     torch.cuda.synchronize()
     avg_dom = s2.elapsed_time(e2) / 1e3 / (reps * dom_per_replay)
+    b_dom = launch_bytes("multi", ("gate", "up"))
+    traffic = traffic_record()
+    roofline = {"bound": "hbm", "achieved": b_dom / avg_dom / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": b_dom / avg_dom / 1e9 / HBM_PEAK_GBS,
+                "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
+                "kernel": "k_gemv_multi: gate+up, 2 x 14336x4096 gs64", "bytes_per_launch": b_dom,
+                "avg_launch_us": avg_dom * 1e6, "launches": reps * dom_per_replay}
 
-    # ---- per-call view (eager launches, HIP events around each; includes
+    # ---- per-launch view (eager launches, HIP events around each; includes
     # host launch latency, reported for reference only)
     timings = []
     for i in range(min(args.steps, 30)):
-        dl.step(i, timings)
+        dl.step(i, FUSED, timings)
     torch.cuda.synchronize()
     per_call = {}
     for name, a, b in timings:
         per_call.setdefault(name, []).append(a.elapsed_time(b) / 1e3)
     calls = {}
-    for name, N, K, kind in LAYER:
+    for name, kind, names in FUSED:
         avg = float(np.mean(per_call[name]))
-        b = call_bytes(N, K, kind)
-        calls[name] = {"N": N, "K": K, "kind": kind, "avg_event_us": avg * 1e6, "GB/s": b / avg / 1e9}
-    b_dom = gemv_bytes(14336, 4096, GS)
-    traffic = traffic_record()
-    roofline = {"bound": "hbm", "achieved": b_dom / avg_dom / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": b_dom / avg_dom / 1e9 / HBM_PEAK_GBS,
-                "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
-                "kernel": "k_gemv, 14336x4096 gs64 (gate/up)", "bytes_per_launch": b_dom,
-                "avg_launch_us": avg_dom * 1e6, "launches": reps * dom_per_replay}
+        b = launch_bytes(kind, names)
+        calls[name] = {"weights": list(names), "kind": kind, "bytes": b, "avg_event_us": avg * 1e6,
+                       "GB/s": b / avg / 1e9}
+
+    # ---- the same layer as seven single-weight launches (one graph per layer)
+    unfused_s = time_graph_steps(dl.graphs(UNFUSED), args.steps)
+    unfused = {"launches": len(UNFUSED), "ms_per_step": unfused_s * 1e3,
+               "GB/s": plan_bytes(UNFUSED) / unfused_s / 1e9, "bytes_per_step": plan_bytes(UNFUSED)}
 
     result = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "llama3-8b-shaped decode layer: gemv q,k,v,o,gate,up + gemv_silu_gate_resid down, "
-                               "m=1, group_size=64",
-                   "bytes_per_step": layer_bytes(), "layers_rotated": n_layers, "frac_hbm_peak": value / HBM_PEAK_GBS,
-                   "timing": "eager launches" if args.eager else "HIP graph per layer",
-                   "wall_s": wall},
+        "config": {"workload": "llama3-8b-shaped decode layer at m=1, group_size=64: gemv_multi(q,k,v), gemv(o), "
+                               "gemv_multi(gate,up), gemv_silu_gate_resid(down)",
+                   "bytes_per_step": step_bytes, "layers_rotated": n_layers, "frac_hbm_peak": value / HBM_PEAK_GBS,
+                   "timing": "HIP graph per layer", "wall_s": wall},
         "roofline": roofline,
         "calls": calls,
+        "unfused_step": unfused,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     if not args.no_secondary:
-        del dl, graphs
+        del dl, graphs, g_dom
         torch.cuda.empty_cache()
         result["secondary"] = secondary(dev, quick=not args.full_secondary)
     print(json.dumps(result), flush=True)
