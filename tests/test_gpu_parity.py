@@ -237,6 +237,11 @@ def test_gemm_small_batch_decode(m, N, K, gs):
     (16, 100, 160, 32),
     (7, 33, 384, 128),
     (16, 1, 64, 64),
+    (9, 50, 4128, 32),      # K ends inside a 64-code step and inside an LDS block
+    (2, 20, 1056, 32),
+    (4, 300, 14336, 32),    # 16-wave workgroups, long scale/bias rows
+    (16, 520, 12288, 128),
+    (3, 64, 131072, 32),    # scale/bias rows too long to stage: routed to the tiled kernel
 ])
 def test_gemm_small_m_ragged(m, N, K, gs):
     log(f"gemm ragged m={m} N={N} K={K} gs={gs}")

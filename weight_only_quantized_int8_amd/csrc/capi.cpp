@@ -252,7 +252,7 @@ int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m,
   hipError_t e;
   if (m == 1)
     e = launch_gemv(view(w), kEpiNone, x, nullptr, nullptr, y, s);
-  else if (m <= 16)
+  else if (m <= 16 && smallm_supported(w->in_features, w->group_size))
     e = launch_gemm_smallm(view(w), x, y, m, s);
   else
     e = launch_gemm_prefill(view(w), x, y, m, s);

@@ -6,24 +6,33 @@
 // FMAs per code would swamp the vector ALUs, so the products go to
 // v_mfma_f32_16x16x32_bf16:
 //  * The raw codes 0..255 are exact in BF16 (8 significant bits), so they
-//    enter the MFMA unscaled; the affine terms are applied per window of 32 or
-//    64 codes that lies inside one group:
+//    enter the MFMA unscaled; the affine terms are applied per window of 32
+//    or 64 codes that lies inside one group:
 //        sum_{k in win} (q s + b) x = s * sum q x + b * sum x
-//    The first sum is the MFMA on raw codes; the second comes from a second
-//    MFMA against a constant all-ones operand, which leaves sum_k X[i,k] in
-//    exactly the accumulator lanes that need it.  Products q*x are exact.
-//  * MFMA D[i][j] = sum_k A[i][k] B[k][j] with A = X (i: input row, padded to
-//    16 with zeros), B = codes (j: weight row).  For this shape lane l holds
-//    A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and D[4*(l/16)+r][l%16].
-//    Any lane->k assignment works as long as A and B use the same one.
-//  * gs >= 64: a lane loads 16 consecutive codes (16 B) of its weight row per
-//    64-code step; the two MFMAs of the step take codes 0..7 and 8..15 of each
-//    lane, so a step is one window inside one group.
-//    gs == 32: a lane loads 8 codes from each 32-code half of the step, so
-//    each MFMA sees exactly one group.
-//  * A workgroup of 4 waves owns RT tiles of 16 weight rows; its waves split K
-//    into interleaved 64-code steps and meet in LDS at the end (fixed order,
-//    no atomics: deterministic).
+//    The first sum is the MFMA on raw codes; the second comes from an MFMA
+//    against a constant all-ones operand, which leaves sum_k X[i,k] in exactly
+//    the accumulator lanes that need it.  Products q*x are exact.
+//  * MFMA D[i][j] = sum_k A[i][k] B[k][j] with A = X (i: input row, rows past
+//    m are zero), B = codes (j: weight row).  Lane l holds
+//    A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and D[4*(l/16)+r][l%16];
+//    the k positions behind a lane's 8 values are the same for A and B.
+//    gs >= 64: a 64-code step is two MFMAs over codes 16*(l/16) + 0..7 and
+//    + 8..15 of each lane (one group); gs == 32: the two MFMAs take 8 codes of
+//    each 32-code half, one group each.
+//  * A workgroup of KS waves owns RT tiles of 16 weight rows and walks K in
+//    blocks of KB = 64*KS*SPW codes.  Each block (the tiles' codes and the 16
+//    X rows, rows past m zero) is loaded with every load reading whole 16-byte
+//    chunks of one row in contiguous runs (the weight stream stays sequential
+//    in HBM), written to LDS with the 16-byte chunks of row r XOR-swizzled by
+//    r mod 16 (so the 16 rows an MFMA operand read touches sit in distinct
+//    banks), and read back in MFMA operand layout.  Wave w takes the SPW steps
+//    [w*SPW, (w+1)*SPW) of every block for all RT tiles.
+//  * Pipeline: D blocks are in flight in registers while the LDS copy of
+//    another is consumed; one workgroup barrier per block.  Every global load
+//    goes through a bounded buffer resource: past the end it reads zeros.
+//  * Scales and biases of the workgroup's rows are staged in LDS once, packed
+//    as BF16 pairs.  The KS partial sums meet in LDS in wave order (no
+//    atomics: deterministic).
 #include "common.h"
 #include "launch.h"
 
@@ -31,7 +40,7 @@ namespace int8w {
 
 namespace {
 
-constexpr int kSmallmThreads = 256;  // 4 waves, K split 4 ways
+__device__ __forceinline__ uint32_t uniform_sm(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t word, int half) {
   // bytes (2*half, 2*half+1) of word -> packed BF16 pair (exact for 0..255)
@@ -45,124 +54,252 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int RT, bool G32>
-__global__ __launch_bounds__(kSmallmThreads) void k_gemm_smallm(
+// Loads of one block held in registers: NC code chunks and NX X chunks of
+// 64 x 16 bytes per wave.
+template <int NC, int NX>
+struct SmRegs {
+  u32x4 c[NC];
+  u32x4 x[NX];
+};
+
+template <int KS, int RT, int SPW, bool G32>
+struct SmShape {
+  static constexpr int kThreads = 64 * KS;
+  static constexpr uint32_t KB = 64u * KS * SPW;         // codes per block
+  static constexpr uint32_t CPR = KB / 16u;               // 16-byte code chunks per row per block
+  static constexpr uint32_t XCPR = 2u * CPR;              // 16-byte X chunks per row per block
+  static constexpr uint32_t CODE_BYTES = 16u * RT * KB;   // one block of codes in LDS
+  static constexpr uint32_t X_BYTES = 16u * 2u * KB;      // 16 X rows (rows past m are zero)
+  static constexpr uint32_t BUF_BYTES = CODE_BYTES + X_BYTES;
+  static constexpr int NC = (int)(CODE_BYTES / 1024u / KS);  // code loads per wave per block
+  static constexpr int NX = (int)(X_BYTES / 1024u / KS);     // X loads per wave per block
+  static_assert(CODE_BYTES % (1024u * KS) == 0 && X_BYTES % (1024u * KS) == 0, "whole loads per wave");
+  static_assert(CPR >= 16, "swizzle needs 16 chunks per row");
+};
+
+// LDS (dynamic): two block buffers [codes | X], then sb [16*RT][G+1] packed
+// (scale | bias << 16).  The partial-sum exchange reuses buffer 0.
+template <int KS, int RT, int SPW, int D, bool G32>
+__global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ X, uint16_t *__restrict__ Y,
     uint32_t N, uint32_t K, uint32_t m, uint32_t gs_log2) {
-  __shared__ f32x4 red[4][RT][64];
-
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t wave = threadIdx.x >> 6;
-  const uint32_t lr = lane & 15u;   // row of A (input row) / column of B (weight row)
-  const uint32_t lg = lane >> 4;    // 8-wide k block of this lane
-  const uint32_t n0 = blockIdx.x * (16u * RT);
+  using S = SmShape<KS, RT, SPW, G32>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_sm[];
   const uint32_t G = K >> gs_log2;
-  const uint32_t steps = (K + 63u) >> 6;
+  const uint32_t SBP = G + 1u;  // odd pitch: the 16 rows of a read hit distinct banks
+  uint32_t *sb = reinterpret_cast<uint32_t *>(lds_sm + 2u * S::BUF_BYTES);
 
-  const bool xrow_ok = lr < m;
-  const uint16_t *xrow = X + (size_t)(xrow_ok ? lr : 0) * K;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave = uniform_sm(tid >> 6);
+  const uint32_t lr = lane & 15u;  // X row of A / weight row of B within a tile
+  const uint32_t lg = lane >> 4;   // 8-wide k block of this lane
+  const uint32_t n0 = blockIdx.x * (16u * RT);
+  const uint32_t rows = N - n0 < 16u * RT ? N - n0 : 16u * RT;  // rows of the workgroup
+  const uint32_t nb = (K + S::KB - 1u) / S::KB;                   // blocks
 
-  const uint8_t *wrow[RT];
-  uint32_t nrow[RT];
-  bool wrow_ok[RT];
+  const auto rw = make_rsrc(codes + (size_t)n0 * K, rows * K);
+  const auto rx = make_rsrc(X, m * K * 2u);
+
+  // ---- per-lane global offsets of this wave's loads (the block's k is added
+  // per block).  Load j of the wave fills LDS bytes [q*1024, (q+1)*1024) of
+  // the block's code (or X) region, q = wave*NC + j; lane i writes the 16
+  // bytes at q*1024 + 16*i, i.e. (row, physical chunk p) with the logical
+  // chunk c = p ^ (row & 15) read from global memory.
+  uint32_t vc[S::NC], vx[S::NX];
+  uint32_t cchunk[S::NC], xchunk[S::NX];  // logical chunk (for the k bound)
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    nrow[t] = n0 + 16u * t + lr;
-    wrow_ok[t] = nrow[t] < N;
-    wrow[t] = codes + (size_t)(wrow_ok[t] ? nrow[t] : 0) * K;
+  for (int j = 0; j < S::NC; ++j) {
+    const uint32_t slot = (wave * S::NC + j) * 64u + lane;
+    const uint32_t row = slot / S::CPR, p = slot % S::CPR;
+    const uint32_t c = p ^ (row & 15u);
+    cchunk[j] = c;
+    vc[j] = row < rows ? row * K + 16u * c : kOutOfRange;
   }
+#pragma unroll
+  for (int j = 0; j < S::NX; ++j) {
+    const uint32_t slot = (wave * S::NX + j) * 64u + lane;
+    const uint32_t row = slot / S::XCPR, p = slot % S::XCPR;
+    const uint32_t c = p ^ (row & 15u);
+    xchunk[j] = c;
+    vx[j] = row < m ? row * K * 2u + 16u * c : kOutOfRange;
+  }
+
+  using Regs = SmRegs<S::NC, S::NX>;
+  auto issue = [&](Regs &r, uint32_t blk) {
+    const bool live = blk < nb;
+    const uint32_t kb = live ? blk * S::KB : 0u;
+#pragma unroll
+    for (int j = 0; j < S::NC; ++j) {
+      const bool in = live && kb + 16u * cchunk[j] < K;
+      r.c[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(in ? vc[j] : kOutOfRange), (int)uniform_sm(kb),
+                                                     kAuxNontemporal);
+    }
+#pragma unroll
+    for (int j = 0; j < S::NX; ++j) {
+      const bool in = live && 2u * kb + 16u * xchunk[j] < 2u * K;
+      r.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(in ? vx[j] : kOutOfRange), (int)uniform_sm(2u * kb),
+                                                     0);
+    }
+  };
+  auto stage = [&](const Regs &r, uint32_t buf) {
+    uint8_t *base = lds_sm + buf * S::BUF_BYTES;
+#pragma unroll
+    for (int j = 0; j < S::NC; ++j)
+      *reinterpret_cast<u32x4 *>(base + (wave * S::NC + j) * 1024u + 16u * lane) = r.c[j];
+#pragma unroll
+    for (int j = 0; j < S::NX; ++j)
+      *reinterpret_cast<u32x4 *>(base + S::CODE_BYTES + (wave * S::NX + j) * 1024u + 16u * lane) = r.x[j];
+  };
+
+  // ---- scales and biases of the workgroup's rows, all groups, packed as
+  // (scale | bias << 16).  Entries past the first kSbPre per thread are staged
+  // first (long rows only); the first kSbPre are loaded, then the first D
+  // blocks are issued, and only then are those entries written, so the
+  // pipeline starts full and the loop sees the same loads in flight on entry
+  // as on every later iteration.
+  const auto rs = make_rsrc(scales + (size_t)n0 * G, rows * G * 2u);
+  const auto rb = make_rsrc(biases + (size_t)n0 * G, rows * G * 2u);
+  const uint32_t total = 16u * RT * G;
+  const uint32_t spare = 16u * RT * SBP;  // slot for entries past the end (branch-free writes)
+  constexpr int kSbPre = 8;
+  for (uint32_t e0 = kSbPre * S::kThreads; e0 < total; e0 += 4u * S::kThreads) {
+    uint16_t sv[4], bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t e = e0 + tid + (uint32_t)j * S::kThreads;
+      const uint32_t off = e < total ? e * 2u : kOutOfRange;
+      sv[j] = buf_load_b16(rs, off);
+      bv[j] = buf_load_b16(rb, off);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t e = e0 + tid + (uint32_t)j * S::kThreads;
+      const uint32_t r = e / G, g = e - r * G;
+      sb[e < total ? r * SBP + g : spare] = (uint32_t)sv[j] | ((uint32_t)bv[j] << 16);
+    }
+  }
+  uint16_t sv0[kSbPre], bv0[kSbPre];
+#pragma unroll
+  for (int j = 0; j < kSbPre; ++j) {
+    const uint32_t e = tid + (uint32_t)j * S::kThreads;
+    const uint32_t off = e < total ? e * 2u : kOutOfRange;
+    sv0[j] = buf_load_b16(rs, off);
+    bv0[j] = buf_load_b16(rb, off);
+  }
+
+  Regs R[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(R[d], (uint32_t)d);
+#pragma unroll
+  for (int j = 0; j < kSbPre; ++j) {
+    const uint32_t e = tid + (uint32_t)j * S::kThreads;
+    const uint32_t r = e / G, g = e - r * G;
+    sb[e < total ? r * SBP + g : spare] = (uint32_t)sv0[j] | ((uint32_t)bv0[j] << 16);
+  }
+  stage(R[0], 0);
+  __syncthreads();
+  issue(R[0], (uint32_t)D);
 
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[RT];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < RT; ++t) acc[t] = zero;
 
-  for (uint32_t st = wave; st < steps; st += 4) {
-    const uint32_t k0 = st << 6;
-    // ---- loads: X fragments (2 x 8 bf16) and RT weight fragments (16 codes)
-    uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-    uint32_t kA, kB;  // first k of the two 8-code pieces of this lane
-    if constexpr (G32) {
-      kA = k0 + 8u * lg;
-      kB = k0 + 32u + 8u * lg;
-    } else {
-      kA = k0 + 16u * lg;
-      kB = kA + 8u;
-    }
-    const bool okA = kA < K, okB = kB < K;
-    if (xrow_ok) {
-      if (okA) xa = *reinterpret_cast<const uint4 *>(xrow + kA);
-      if (okB) xb = *reinterpret_cast<const uint4 *>(xrow + kB);
-    }
-    uint32_t wq[RT][4];
-    float sA[RT], bA[RT], sB[RT], bB[RT];
+  auto compute = [&](uint32_t blk) {
+    const uint8_t *cb = lds_sm + (blk & 1u) * S::BUF_BYTES;
+    const uint8_t *xbp = cb + S::CODE_BYTES;
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
+    for (int st = 0; st < SPW; ++st) {
+      const uint32_t kl = 64u * (wave * SPW + st);  // step's first code within the block
+      const uint32_t kg = blk * S::KB + kl;          // ... within the row
+      uint32_t g = kg >> gs_log2;
+      if (g >= G) g = G - 1u;  // a step past K holds zeros: any finite pair
+      // X fragments of the step's two MFMAs (row lr)
+      u32x4 xa, xb;
       if constexpr (G32) {
-        uint2 pa = make_uint2(0, 0), pb = make_uint2(0, 0);
-        if (wrow_ok[t] && okA) pa = load_nt(reinterpret_cast<const uint2 *>(wrow[t] + kA));
-        if (wrow_ok[t] && okB) pb = load_nt(reinterpret_cast<const uint2 *>(wrow[t] + kB));
-        wq[t][0] = pa.x; wq[t][1] = pa.y; wq[t][2] = pb.x; wq[t][3] = pb.y;
+        const uint32_t ca = (kl + 8u * lg) >> 3, cbx = (kl + 32u + 8u * lg) >> 3;  // 16-byte X chunks
+        xa = *reinterpret_cast<const u32x4 *>(xbp + lr * (2u * S::KB) + 16u * (ca ^ lr));
+        xb = *reinterpret_cast<const u32x4 *>(xbp + lr * (2u * S::KB) + 16u * (cbx ^ lr));
       } else {
-        uint4 p = make_uint4(0, 0, 0, 0);
-        if (wrow_ok[t] && okA) p = load_nt(reinterpret_cast<const uint4 *>(wrow[t] + kA));
-        wq[t][0] = p.x; wq[t][1] = p.y; wq[t][2] = p.z; wq[t][3] = p.w;
+        const uint32_t ca = (kl + 16u * lg) >> 3;
+        xa = *reinterpret_cast<const u32x4 *>(xbp + lr * (2u * S::KB) + 16u * (ca ^ lr));
+        xb = *reinterpret_cast<const u32x4 *>(xbp + lr * (2u * S::KB) + 16u * ((ca + 1u) ^ lr));
       }
-      const size_t grow = (size_t)(wrow_ok[t] ? nrow[t] : 0) * G;
-      const uint32_t gA = okA ? (kA >> gs_log2) : 0;
-      sA[t] = bf16_bits_to_f32(scales[grow + gA]);
-      bA[t] = bf16_bits_to_f32(biases[grow + gA]);
+      const bf16x8 xa8 = __builtin_bit_cast(bf16x8, xa), xb8 = __builtin_bit_cast(bf16x8, xb);
       if constexpr (G32) {
-        const uint32_t gB = okB ? (kB >> gs_log2) : 0;
-        sB[t] = bf16_bits_to_f32(scales[grow + gB]);
-        bB[t] = bf16_bits_to_f32(biases[grow + gB]);
-      }
-    }
-    // ---- input sums of the window(s): MFMA against ones
-    const bf16x8 xa8 = __builtin_bit_cast(bf16x8, xa), xb8 = __builtin_bit_cast(bf16x8, xb);
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8, ones, zero, 0, 0, 0);
-    f32x4 SB = zero;
-    if constexpr (G32) {
-      SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, ones, zero, 0, 0, 0);
-    } else {
-      SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, ones, SA, 0, 0, 0);
-    }
-    // ---- raw-code products and per-window affine rescale
+        const f32x4 SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8, ones, zero, 0, 0, 0);
+        const f32x4 SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, ones, zero, 0, 0, 0);
+        const uint32_t gb = g + 1u < G ? g + 1u : g;
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const bf16x8 qa = codes8_to_bf16x8(wq[t][0], wq[t][1]);
-      const bf16x8 qb = codes8_to_bf16x8(wq[t][2], wq[t][3]);
-      if constexpr (G32) {
-        f32x4 PA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8, qa, zero, 0, 0, 0);
-        f32x4 PB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, qb, zero, 0, 0, 0);
+        for (int t = 0; t < RT; ++t) {
+          const uint32_t row = 16u * t + lr;
+          const uint8_t *rp = cb + row * S::KB;
+          const uint32_t c0 = (kl + 8u * lg) >> 4, c1 = (kl + 32u + 8u * lg) >> 4, h = 8u * (lg & 1u);
+          const u32x2 qa = *reinterpret_cast<const u32x2 *>(rp + 16u * (c0 ^ lr) + h);
+          const u32x2 qb = *reinterpret_cast<const u32x2 *>(rp + 16u * (c1 ^ lr) + h);
+          const uint32_t pa = sb[row * SBP + g], pb = sb[row * SBP + gb];
+          const float sa = __uint_as_float(pa << 16), ba = __uint_as_float(pa & 0xFFFF0000u);
+          const float sbv = __uint_as_float(pb << 16), bbv = __uint_as_float(pb & 0xFFFF0000u);
+          const f32x4 PA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8, codes8_to_bf16x8(qa.x, qa.y), zero, 0, 0, 0);
+          const f32x4 PB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, codes8_to_bf16x8(qb.x, qb.y), zero, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = __builtin_fmaf(sA[t], PA[r], __builtin_fmaf(bA[t], SA[r], acc[t][r]));
-          acc[t][r] = __builtin_fmaf(sB[t], PB[r], __builtin_fmaf(bB[t], SB[r], v));
+          for (int r = 0; r < 4; ++r) {
+            const float v = __builtin_fmaf(sa, PA[r], __builtin_fmaf(ba, SA[r], acc[t][r]));
+            acc[t][r] = __builtin_fmaf(sbv, PB[r], __builtin_fmaf(bbv, SB[r], v));
+          }
         }
       } else {
-        f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8, qa, zero, 0, 0, 0);
-        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, qb, P, 0, 0, 0);
+        f32x4 Sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8, ones, zero, 0, 0, 0);
+        Sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, ones, Sx, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[t][r] = __builtin_fmaf(sA[t], P[r], __builtin_fmaf(bA[t], SA[r], acc[t][r]));
+        for (int t = 0; t < RT; ++t) {
+          const uint32_t row = 16u * t + lr;
+          const uint32_t c = (kl >> 4) + lg;
+          const u32x4 q = *reinterpret_cast<const u32x4 *>(cb + row * S::KB + 16u * (c ^ lr));
+          const uint32_t p = sb[row * SBP + g];
+          const float s = __uint_as_float(p << 16), b = __uint_as_float(p & 0xFFFF0000u);
+          f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8, codes8_to_bf16x8(q.x, q.y), zero, 0, 0, 0);
+          P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, codes8_to_bf16x8(q.z, q.w), P, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[t][r] = __builtin_fmaf(s, P[r], __builtin_fmaf(b, Sx[r], acc[t][r]));
+        }
       }
     }
-  }
+  };
 
-  // ---- combine the 4 K-slices in a fixed order and store
+  // ---- pipeline: while block b is consumed from LDS, blocks b+1 .. b+D are
+  // in flight in the D register sets; the set holding block b+1 is then
+  // written to the other LDS buffer and refilled with block b+1+D.  The only
+  // branches are the loop exits.
+  for (uint32_t b = 0;;) {
 #pragma unroll
-  for (int t = 0; t < RT; ++t) red[wave][t][lane] = acc[t];
+    for (int d = 1; d <= D; ++d) {
+      compute(b);
+      if (b + 1u >= nb) goto pipeline_done;
+      stage(R[d % D], (b + 1u) & 1u);
+      __syncthreads();
+      issue(R[d % D], b + 1u + D);
+      ++b;
+    }
+  }
+pipeline_done:
+
+  // ---- combine the KS partial sums in wave order and store
+  __syncthreads();  // every wave is done with the block buffers
+  f32x4 *red = reinterpret_cast<f32x4 *>(lds_sm);
+#pragma unroll
+  for (int t = 0; t < RT; ++t) red[(wave * RT + t) * 64u + lane] = acc[t];
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
-    f32x4 v = red[0][t][lane];
+    f32x4 v = red[t * 64u + lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      const f32x4 o = red[w][t][lane];
+    for (int w = 1; w < KS; ++w) {
+      const f32x4 o = red[(w * RT + t) * 64u + lane];
       v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
     }
     const uint32_t n = n0 + 16u * t + lr;
@@ -176,29 +313,88 @@ __global__ __launch_bounds__(kSmallmThreads) void k_gemm_smallm(
   }
 }
 
-template <int RT>
-hipError_t launch_rt(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream) {
+// Register sets in flight.  Two: with more, the compiler's wait-count
+// tracking drains every set once per pass of the unrolled loop (measured no
+// faster on MI355X).
+constexpr int kSmDepth = 2;
+
+template <int KS, int RT, int SPW>
+size_t smallm_lds_bytes(uint32_t K, uint32_t gs) {
+  using S = SmShape<KS, RT, SPW, false>;
+  const size_t G = K / gs;
+  size_t bytes = 2u * S::BUF_BYTES + (16u * RT * (G + 1u) + 1u) * 4u;  // + the spare slot
+  const size_t red = (size_t)KS * RT * 64u * 16u;
+  return bytes > red ? bytes : red;
+}
+
+template <int KS, int RT, int SPW, int D, bool G32>
+hipError_t launch_sm(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream) {
+  auto kern = k_gemm_smallm<KS, RT, SPW, D, G32>;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
   const uint32_t blocks = (w.N + 16u * RT - 1u) / (16u * RT);
-  const uint32_t gs_log2 = (uint32_t)__builtin_ctz(w.gs);
-  const uint8_t *codes = reinterpret_cast<const uint8_t *>(w.packed);
-  if (w.gs == 32)
-    hipLaunchKernelGGL((k_gemm_smallm<RT, true>), dim3(blocks), dim3(kSmallmThreads), 0, stream, codes,
-                       w.scales, w.biases, X, Y, w.N, w.K, m, gs_log2);
-  else
-    hipLaunchKernelGGL((k_gemm_smallm<RT, false>), dim3(blocks), dim3(kSmallmThreads), 0, stream, codes,
-                       w.scales, w.biases, X, Y, w.N, w.K, m, gs_log2);
+  const size_t lds = smallm_lds_bytes<KS, RT, SPW>(w.K, w.gs);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * KS), lds, stream,
+                     reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m,
+                     (uint32_t)__builtin_ctz(w.gs));
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Launch shapes (ks waves per workgroup, rt tiles of 16 rows, spw steps of 64
+// codes per wave per block).  Shape 0: 4/2/1 (many rows: two tiles share each
+// X block); shape 1: 16/1/1 (few rows, long K: more waves per tile); shape 2:
+// 8/1/1; shape 3: 4/1/2.
+constexpr int kSmShapes = 4;
+
+size_t smallm_shape_lds(int shape, uint32_t K, uint32_t gs) {
+  switch (shape) {
+    case 0: return smallm_lds_bytes<4, 2, 1>(K, gs);
+    case 1: return smallm_lds_bytes<16, 1, 1>(K, gs);
+    case 2: return smallm_lds_bytes<8, 1, 1>(K, gs);
+    default: return smallm_lds_bytes<4, 1, 2>(K, gs);
+  }
+}
+
+int smallm_choose(uint32_t N, uint32_t K, uint32_t gs) {
+  const uint32_t cus = (uint32_t)device_cu_count();
+  const uint32_t tiles = (N + 15u) / 16u;
+  int shape;
+  if (tiles >= 2u * cus) shape = 0;       // >= 2 tile pairs per CU
+  else if (tiles >= cus / 2u) shape = 1;  // a 16-wave workgroup per tile
+  else shape = 1;
+  // fall back to smaller LDS footprints when the staged scale/bias rows are long
+  if (smallm_shape_lds(shape, K, gs) > 160u * 1024u) shape = 2;
+  if (smallm_shape_lds(shape, K, gs) > 160u * 1024u) shape = 3;
+  return shape;
+}
+
+bool smallm_supported(uint32_t K, uint32_t gs) {
+  for (int s = 0; s < kSmShapes; ++s)
+    if (smallm_shape_lds(s, K, gs) <= 160u * 1024u) return true;
+  return false;
+}
+
+hipError_t launch_gemm_smallm_shape(int shape, const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
+                                    hipStream_t stream) {
+  const bool g32 = w.gs == 32;
+  switch (shape) {
+    case 0: return g32 ? launch_sm<4, 2, 1, kSmDepth, true>(w, X, Y, m, stream) : launch_sm<4, 2, 1, kSmDepth, false>(w, X, Y, m, stream);
+    case 1: return g32 ? launch_sm<16, 1, 1, kSmDepth, true>(w, X, Y, m, stream) : launch_sm<16, 1, 1, kSmDepth, false>(w, X, Y, m, stream);
+    case 2: return g32 ? launch_sm<8, 1, 1, kSmDepth, true>(w, X, Y, m, stream) : launch_sm<8, 1, 1, kSmDepth, false>(w, X, Y, m, stream);
+    default: return g32 ? launch_sm<4, 1, 2, kSmDepth, true>(w, X, Y, m, stream) : launch_sm<4, 1, 2, kSmDepth, false>(w, X, Y, m, stream);
+  }
+}
+
 hipError_t launch_gemm_smallm(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                               hipStream_t stream) {
-  const uint32_t cus = (uint32_t)device_cu_count();
-  // Enough 16-row tiles per workgroup to keep the tile count near 2 per CU.
-  const uint32_t tiles = (w.N + 15u) / 16u;
-  if (tiles >= 4u * cus) return launch_rt<2>(w, X, Y, m, stream);
-  return launch_rt<1>(w, X, Y, m, stream);
+  return launch_gemm_smallm_shape(smallm_choose(w.N, w.K, w.gs), w, X, Y, m, stream);
 }
 
 }  // namespace int8w

@@ -32,6 +32,9 @@ hipError_t launch_gemv_multi(const WeightView *w, uint16_t *const *y, uint32_t c
                              hipStream_t stream);
 
 // Y[m, N] = X[m, K] W^T for 2 <= m <= 16 (matrix cores, per-group rescale).
+// Only for shapes where smallm_supported(K, gs) (the per-row scale/bias stage
+// fits the LDS); others go to launch_gemm_prefill.
+bool smallm_supported(uint32_t K, uint32_t gs);
 hipError_t launch_gemm_smallm(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                               hipStream_t stream);
 
