@@ -260,6 +260,8 @@ def test_gemm_small_m_ragged(m, N, K, gs):
     (129, 130, 96, 32),
     (300, 1024, 2048, 128),
     (257, 333, 4096, 64),
+    (1100, 5000, 256, 32),   # enough tiles for the 256 x 128 eight-wave shape, ragged edges
+    (777, 7777, 96, 32),     # same shape, K ends inside the second step
 ])
 def test_gemm_prefill_small(m, N, K, gs):
     log(f"gemm prefill m={m} N={N} K={K} gs={gs}")

@@ -3,16 +3,22 @@
 // Y BF16 [m, out_features]).
 //
 // A dense contraction, bound by v_mfma_f32_16x16x32_bf16 throughput:
-//  * Block tile BM x BN = 128 x 128 outputs, K step 64, 4 waves (2 x 2), each
-//    wave 64 x 64 outputs = 4 x 4 MFMA tiles of 16 x 16, fp32 accumulators.
+//  * Block tile BM x BN = 256 x 128 outputs over 8 waves (4 x 2, each wave
+//    64 x 64), or 128 x 128 / 128 x 64 over 4 waves when there are too few
+//    large tiles to occupy the CUs; K step 64; MFMA tiles of 16 x 16 with
+//    fp32 accumulators.
 //  * Per K step the block stages a 128 x 64 BF16 tile of X and a 128 x 64
 //    tile of the weight into LDS.  The weight arrives as codes (16 per lane,
 //    one 16-byte load) and is dequantized on the way in: w = q*s + b in fp32
 //    (one FMA), rounded to BF16 nearest-even -- the same values
 //    dequantize_to writes.  Each code is thus dequantized once per block and
 //    reused by all 128 rows of X in the block.
-//  * LDS is double-buffered: the next step's global loads are in flight while
-//    the MFMAs consume the current buffer; one barrier per step.
+//  * Pipeline: the global loads of the next two K steps are in flight in two
+//    register sets while the MFMAs consume the LDS copy of the current one;
+//    LDS is double-buffered, one barrier per step.  Every global load goes
+//    through a bounded buffer resource (past the matrix edges it reads
+//    zeros: a zero code with zero scale and bias is a zero weight), so the
+//    loop has no branches but its exits.
 //  * LDS rows are 128 B (64 BF16); 16-byte chunk c of row r is stored at
 //    chunk c ^ (r & 7), so the 16 lanes reading 16 consecutive rows of one
 //    chunk hit distinct banks.
@@ -26,19 +32,41 @@ namespace int8w {
 
 namespace {
 
-constexpr int kPfThreads = 256;
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BK = 64;
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
   return row * (BK * 2) + ((chunk ^ (row & 7u)) << 4);
 }
 
-__global__ __launch_bounds__(kPfThreads) void k_gemm_prefill(
+__device__ __forceinline__ uint32_t uniform_pf(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Global loads of one K step held in registers.
+template <int XP, int WP>
+struct PfRegs {
+  u32x4 x[XP];
+  u32x4 w[WP];
+  uint16_t s[WP], b[WP];
+};
+
+// WGM x WGN waves; wave (wm, wn) owns rows wm*BM/WGM.. and columns wn*BN/WGN.. of the tile.
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_prefill(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ X, uint16_t *__restrict__ Y,
     uint32_t N, uint32_t K, uint32_t m, uint32_t gs_log2, uint32_t mtiles, uint32_t nwork) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * BK * 2];
+  constexpr int kThreads = 64 * WGM * WGN;
+  constexpr int XR = kThreads / 8;  // X rows per load pass (8 chunks of 16 B per row)
+  constexpr int WR = kThreads / 4;  // weight rows per load pass (4 chunks of 16 codes per row)
+  constexpr int XP = BM / XR;       // X loads per thread per step
+  constexpr int WP = BN / WR;       // weight loads per thread per step
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
+  constexpr int TI = WTM / 16;      // 16-row MFMA tiles per wave
+  constexpr int TJ = WTN / 16;      // 16-column MFMA tiles per wave
+  static_assert(XP >= 1 && WP >= 1 && BM % XR == 0 && BN % WR == 0, "whole load passes");
+  constexpr uint32_t kStage = (BM + BN) * BK * 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_pf[];
+  uint8_t *lds[2] = {lds_pf, lds_pf + kStage};
 
   // ---- work item: XCD-grouped, M-fastest
   uint32_t bid = blockIdx.x;
@@ -48,132 +76,190 @@ __global__ __launch_bounds__(kPfThreads) void k_gemm_prefill(
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u, wave = tid >> 6;
-  const uint32_t wm = wave >> 1, wn = wave & 1u;
+  const uint32_t wm = wave / WGN, wn = wave % WGN;
   const uint32_t G = K >> gs_log2;
   const uint32_t ksteps = (K + BK - 1) / BK;
+  const uint32_t mrows = m - m0 < (uint32_t)BM ? m - m0 : (uint32_t)BM;
+  const uint32_t nrows = N - n0 < (uint32_t)BN ? N - n0 : (uint32_t)BN;
+
+  // bounded views of this tile's rows; the step's k is the uniform soffset
+  const auto rx = make_rsrc(X + (size_t)m0 * K, mrows * K * 2u);
+  const auto rw = make_rsrc(codes + (size_t)n0 * K, nrows * K);
+  const auto rs = make_rsrc(scales + (size_t)n0 * G, nrows * G * 2u);
+  const auto rb = make_rsrc(biases + (size_t)n0 * G, nrows * G * 2u);
 
   // global->LDS assignment
-  // X: 4 passes of 32 rows, 8 threads per row, 8 BF16 (16 B) each
+  // X: XP passes of XR rows, 8 threads per row, 8 BF16 (16 B) each
   const uint32_t xr = tid >> 3, xc = tid & 7u;
-  // W: 2 passes of 64 rows, 4 threads per row, 16 codes each
+  // W: WP passes of WR rows, 4 threads per row, 16 codes each (one group)
   const uint32_t wr = tid >> 2, wp = tid & 3u;
-
-  uint4 xreg[4];
-  uint4 wreg[2];
-  float wsc[2], wbi[2];
-
-  auto load_tile = [&](uint32_t k0) {
+  uint32_t vx[XP], vw[WP], vsb[WP];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t row = m0 + p * 32u + xr;
-      const uint32_t k = k0 + xc * 8u;
-      xreg[p] = (row < m && k < K) ? *reinterpret_cast<const uint4 *>(X + (size_t)row * K + k)
-                                   : make_uint4(0, 0, 0, 0);
-    }
+  for (int p = 0; p < XP; ++p) {
+    const uint32_t row = p * XR + xr;
+    vx[p] = row < mrows ? row * K * 2u + xc * 16u : kOutOfRange;
+  }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const uint32_t row = n0 + p * 64u + wr;
-      const uint32_t k = k0 + wp * 16u;
-      if (row < N && k < K) {
-        wreg[p] = load_nt(reinterpret_cast<const uint4 *>(codes + (size_t)row * K + k));
-        const size_t gi = (size_t)row * G + (k >> gs_log2);
-        wsc[p] = bf16_bits_to_f32(scales[gi]);
-        wbi[p] = bf16_bits_to_f32(biases[gi]);
-      } else {
-        wreg[p] = make_uint4(0, 0, 0, 0);
-        wsc[p] = 0.f;  // q*0 + 0 = 0: padding contributes nothing
-        wbi[p] = 0.f;
-      }
+  for (int p = 0; p < WP; ++p) {
+    const uint32_t row = p * WR + wr;
+    vw[p] = row < nrows ? row * K + wp * 16u : kOutOfRange;
+    vsb[p] = row < nrows ? row * G * 2u : kOutOfRange;
+  }
+
+  using Regs = PfRegs<XP, WP>;
+  auto issue = [&](Regs &r, uint32_t ks) {
+    const bool live = ks < ksteps;
+    const uint32_t k0 = live ? ks * BK : 0u;
+    const bool xin = live && k0 + xc * 8u < K;
+    const bool win = live && k0 + wp * 16u < K;
+#pragma unroll
+    for (int p = 0; p < XP; ++p)
+      r.x[p] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xin ? vx[p] : kOutOfRange), (int)uniform_pf(2u * k0), 0);
+#pragma unroll
+    for (int p = 0; p < WP; ++p) {
+      r.w[p] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(win ? vw[p] : kOutOfRange), (int)uniform_pf(k0),
+                                                     kAuxNontemporal);
+      // the lane's 16 codes lie in one group (gs >= 32)
+      const uint32_t go = win ? vsb[p] + 2u * ((k0 + wp * 16u) >> gs_log2) : kOutOfRange;
+      r.s[p] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)go, 0, 0);
+      r.b[p] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)go, 0, 0);
     }
   };
 
-  auto store_tile = [&](uint8_t *buf, uint32_t k0) {
+  auto store = [&](const Regs &r, uint8_t *buf) {
     uint8_t *xs = buf;
     uint8_t *ws = buf + BM * BK * 2;
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-      *reinterpret_cast<uint4 *>(xs + swz(p * 32u + xr, xc)) = xreg[p];
+    for (int p = 0; p < XP; ++p) *reinterpret_cast<u32x4 *>(xs + swz(p * XR + xr, xc)) = r.x[p];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const uint32_t word[4] = {wreg[p].x, wreg[p].y, wreg[p].z, wreg[p].w};
+    for (int p = 0; p < WP; ++p) {
+      const float sc = bf16_bits_to_f32(r.s[p]), bi = bf16_bits_to_f32(r.b[p]);
+      const uint32_t word[4] = {r.w[p].x, r.w[p].y, r.w[p].z, r.w[p].w};
       uint32_t o[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        o[2 * i] = pack_bf16x2(__builtin_fmaf(code_f32(word[i], 0), wsc[p], wbi[p]),
-                               __builtin_fmaf(code_f32(word[i], 1), wsc[p], wbi[p]));
-        o[2 * i + 1] = pack_bf16x2(__builtin_fmaf(code_f32(word[i], 2), wsc[p], wbi[p]),
-                                   __builtin_fmaf(code_f32(word[i], 3), wsc[p], wbi[p]));
+        o[2 * i] = pack_bf16x2(__builtin_fmaf(code_f32(word[i], 0), sc, bi), __builtin_fmaf(code_f32(word[i], 1), sc, bi));
+        o[2 * i + 1] =
+            pack_bf16x2(__builtin_fmaf(code_f32(word[i], 2), sc, bi), __builtin_fmaf(code_f32(word[i], 3), sc, bi));
       }
-      const uint32_t row = p * 64u + wr;
-      *reinterpret_cast<uint4 *>(ws + swz(row, 2u * wp)) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4 *>(ws + swz(row, 2u * wp + 1u)) = make_uint4(o[4], o[5], o[6], o[7]);
+      const uint32_t row = p * WR + wr;
+      *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp)) = u32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp + 1u)) = u32x4{o[4], o[5], o[6], o[7]};
     }
-    (void)k0;
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  load_tile(0);
-  store_tile(lds[0], 0);
-  __syncthreads();
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t lr = lane & 15u, lg = lane >> 4;
-  for (uint32_t ks = 0; ks < ksteps; ++ks) {
-    const bool more = ks + 1 < ksteps;
-    if (more) load_tile((ks + 1) * BK);
-    const uint8_t *xs = lds[ks & 1];
-    const uint8_t *ws = xs + BM * BK * 2;
+  auto compute = [&](const uint8_t *buf) {
+    const uint8_t *xs = buf;
+    const uint8_t *ws = buf + BM * BK * 2;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       const uint32_t chunk = 4u * kh + lg;
-      bf16x8 a[4], b[4];
+      bf16x8 a[TI], b[TJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8 *>(xs + swz(wm * 64u + 16u * i + lr, chunk));
+      for (int i = 0; i < TI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8 *>(xs + swz(wm * WTM + 16u * i + lr, chunk));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8 *>(ws + swz(wn * 64u + 16u * j + lr, chunk));
+      for (int j = 0; j < TJ; ++j)
+        b[j] = *reinterpret_cast<const bf16x8 *>(ws + swz(wn * WTN + 16u * j + lr, chunk));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (more) store_tile(lds[(ks + 1) & 1], (ks + 1) * BK);
+  };
+
+  // ---- pipeline: R0/R1 hold steps ks+1 and ks+2 in flight while step ks is
+  // consumed from LDS; the only branches are the loop exits
+  Regs R0, R1;
+  issue(R0, 0);
+  issue(R1, 1);
+  store(R0, lds[0]);
+  __syncthreads();
+  issue(R0, 2);
+  for (uint32_t ks = 0;;) {
+    compute(lds[ks & 1u]);
+    if (ks + 1u >= ksteps) break;
+    store(R1, lds[(ks + 1u) & 1u]);
     __syncthreads();
+    issue(R1, ks + 3u);
+    ++ks;
+    compute(lds[ks & 1u]);
+    if (ks + 1u >= ksteps) break;
+    store(R0, lds[(ks + 1u) & 1u]);
+    __syncthreads();
+    issue(R0, ks + 3u);
+    ++ks;
   }
 
   // ---- epilogue: lane holds D[4*lg + r][lr] of each 16 x 16 tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TI; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t n = n0 + wn * 64u + 16u * j + lr;
+    for (int j = 0; j < TJ; ++j) {
+      const uint32_t n = n0 + wn * WTN + 16u * j + lr;
       if (n >= N) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint32_t row = m0 + wm * 64u + 16u * i + 4u * lg + r;
+        const uint32_t row = m0 + wm * WTM + 16u * i + 4u * lg + r;
         if (row < m) Y[(size_t)row * N + n] = to_bf16_bits(acc[i][j][r]);
       }
     }
   }
 }
 
-}  // namespace
-
-hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
-                               hipStream_t stream) {
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_tile(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream) {
+  auto kern = k_gemm_prefill<BM, BN, WGM, WGN>;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
   const uint32_t mtiles = (m + BM - 1) / BM;
   const uint32_t ntiles = (w.N + BN - 1) / BN;
   const uint32_t nwork = mtiles * ntiles;
-  hipLaunchKernelGGL(k_gemm_prefill, dim3(nwork), dim3(kPfThreads), 0, stream,
-                     reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m,
-                     (uint32_t)__builtin_ctz(w.gs), mtiles, nwork);
+  const size_t lds = 2u * (BM + BN) * BK * 2u;
+  hipLaunchKernelGGL(kern, dim3(nwork), dim3(64 * WGM * WGN), lds, stream, reinterpret_cast<const uint8_t *>(w.packed),
+                     w.scales, w.biases, X, Y, w.N, w.K, m, (uint32_t)__builtin_ctz(w.gs), mtiles, nwork);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile shapes (BM x BN, waves): 0 = 128 x 128 (2 x 2), 1 = 128 x 64 (2 x 2),
+// 2 = 256 x 128 (2 x 2), 3 = 256 x 128 (4 x 2), 4 = 256 x 256 (4 x 2),
+// 5 = 128 x 128 (4 x 2).
+hipError_t launch_gemm_prefill_tile(int t, const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
+                                    hipStream_t stream) {
+  switch (t) {
+    case 1: return launch_tile<128, 64, 2, 2>(w, X, Y, m, stream);
+    case 2: return launch_tile<256, 128, 2, 2>(w, X, Y, m, stream);
+    case 3: return launch_tile<256, 128, 4, 2>(w, X, Y, m, stream);
+    case 4: return launch_tile<256, 256, 4, 2>(w, X, Y, m, stream);
+    case 5: return launch_tile<128, 128, 4, 2>(w, X, Y, m, stream);
+    default: return launch_tile<128, 128, 2, 2>(w, X, Y, m, stream);
+  }
+}
+
+hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
+                               hipStream_t stream) {
+  // Measured on MI355X: 256 x 128 tiles over 8 waves when they give at least
+  // ~3/4 of a tile per CU, else 128 x 128, else 128 x 64 (fewer idle CUs).
+  const uint32_t cus = (uint32_t)device_cu_count();
+  const uint32_t t256 = ((m + 255u) / 256u) * ((w.N + 127u) / 128u);
+  const uint32_t t128 = ((m + 127u) / 128u) * ((w.N + 127u) / 128u);
+  const int shape = 4u * t256 >= 3u * cus ? 3 : (4u * t128 >= 3u * cus ? 0 : 1);
+  return launch_gemm_prefill_tile(shape, w, X, Y, m, stream);
 }
 
 }  // namespace int8w
