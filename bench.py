@@ -42,10 +42,10 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 LLC_BYTES = 256 << 20
 METRIC = "int8 GEMV achieved HBM GB/s (% of peak) at m=1; prefill GEMM TFLOP/s"
-# the sources the gate/up gemv kernel is compiled from (its traffic record is
-# void once any of them changes)
+# the device sources of the gate/up gemv kernel (its traffic record is void
+# once either changes)
 GEMV_SOURCES = [os.path.join(ROOT, "weight_only_quantized_int8_amd", "csrc", f)
-                for f in ("gemv.hip", "common.h", "launch.h")]
+                for f in ("gemv.hip", "common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_gate_up_traffic.json")
 
 
