@@ -9,7 +9,9 @@ this module only marshals NumPy arrays through ctypes.  Each function follows
 the rustdoc page "MlxInt8Weight" (metrale_gpu_runtime::mlx_int8): the struct
 description ("8-bit affine", no Drop), the packed/scales/biases field sections
 and the methods dequantize_to, gemv, gemv_silu_gate, gemv_silu_gate_resid and
-gemm.  Readings the page leaves open (byte order, signedness, precision,
+gemm.  ``quantize`` (BF16 weight -> codes, scales, biases) follows the rustdoc
+page of the DynQuantizedStorage trait, method quantize, which gives no formula:
+its reading (affine min/max in fp32) is stated in ``int8w_oracle.c``.  Readings the page leaves open (byte order, signedness, precision,
 rounding, silu) are stated in ``int8w_oracle.c``'s header.
 
 Pins: every function is checked against something other than itself in
@@ -64,6 +66,7 @@ def _load():
         lib.orc_silu_gate_act.argtypes = [p, p, i64, p]
         lib.orc_gemv_silu_gate.argtypes = [p, p, p, i64, i64, i64, p, p, p, p]
         lib.orc_gemv_silu_gate_resid.argtypes = [p, p, p, i64, i64, i64, p, p, p, p, p]
+        lib.orc_quantize.argtypes = [p, i64, i64, i64, p, p, p]
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -209,6 +212,24 @@ def gemv_silu_gate_resid(packed, scales, biases, group_size, gate, up, x_resid):
     _load().orc_gemv_silu_gate_resid(_ptr(packed), _ptr(scales), _ptr(biases), N, K, gs, _ptr(g), _ptr(u), _ptr(r),
                                      _ptr(y), _ptr(A))
     return y, A
+
+
+def quantize(w_bits, group_size):
+    """BF16 weight [N, K] (bit patterns) -> (packed uint32 [N, K/4], scales, biases BF16 bits [N, K/gs]).
+
+    The plain affine min/max quantizer (see orc_quantize for the exact steps)."""
+    w = _c(w_bits, np.uint16)
+    if w.ndim != 2:
+        raise ValueError("weight must be 2-D [out_features, in_features]")
+    N, K = w.shape
+    gs = int(group_size)
+    if gs <= 0 or K % gs or K % 4:
+        raise ValueError(f"group_size {gs} must divide in_features {K} (a multiple of 4)")
+    packed = np.zeros((N, K // 4), np.uint32)
+    scales = np.zeros((N, K // gs), np.uint16)
+    biases = np.zeros((N, K // gs), np.uint16)
+    _load().orc_quantize(_ptr(w), N, K, gs, _ptr(packed), _ptr(scales), _ptr(biases))
+    return packed, scales, biases
 
 
 def within_tolerance(y_bf16_bits, y_ref, A, rel: float = 8e-3, absA: float = 2e-3) -> np.ndarray:

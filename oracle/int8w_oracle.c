@@ -201,6 +201,62 @@ void orc_gemv_silu_gate_resid(const uint32_t *packed, const uint16_t *scales,
   for (int64_t n = 0; n < N; ++n) y[n] = (double)orc_bf16_to_f32(x_resid[n]) + y[n];
 }
 
+/* ---- quantizer: BF16 weight -> codes, scales, biases.
+ *
+ * Source: the rustdoc page of the DynQuantizedStorage trait (fuel_quantized),
+ * required method quantize, and the MlxInt8Weight page's field sections for
+ * the target layout.  The pages give no formula; this is the plain affine
+ * min/max reading, evaluated in fp32 one operation at a time:
+ *   per group of gs consecutive values v of a row (BF16, widened exactly):
+ *     lo = min v, hi = max v
+ *     s  = RNE_bf16((hi - lo) / 255)       fp32 subtraction, fp32 division
+ *     b  = lo                              already a BF16 value
+ *     q  = clamp(rint((v - b) / s), 0, 255)  fp32 subtraction and division,
+ *                                           round half to even
+ *   and q = 0 for every value of a group whose s is zero.
+ * Inputs must be finite. */
+static uint32_t quantize_code(float v, float b, float s) {
+  if (s == 0.0f) return 0u;
+  float d = v - b;
+  float t = d / s;
+  float r = rintf(t); /* current rounding mode: nearest, ties to even */
+  if (r < 0.0f) r = 0.0f;
+  if (r > 255.0f) r = 255.0f;
+  return (uint32_t)r;
+}
+
+void orc_quantize(const uint16_t *w, int64_t N, int64_t K, int64_t gs, uint32_t *packed,
+                  uint16_t *scales, uint16_t *biases) {
+  const int64_t G = K / gs;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    const uint16_t *row = w + n * K;
+    uint32_t *out = packed + n * (K / 4);
+    for (int64_t k = 0; k < K / 4; ++k) out[k] = 0u;
+    for (int64_t g = 0; g < G; ++g) {
+      float lo = orc_bf16_to_f32(row[g * gs]);
+      float hi = lo;
+      for (int64_t i = 1; i < gs; ++i) {
+        float v = orc_bf16_to_f32(row[g * gs + i]);
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+      }
+      float span = hi - lo;
+      float sf = span / 255.0f;
+      uint16_t s_bits = orc_f32_to_bf16_rne(sf);
+      uint16_t b_bits = orc_f32_to_bf16_rne(lo); /* exact: lo is a BF16 value */
+      scales[n * G + g] = s_bits;
+      biases[n * G + g] = b_bits;
+      float s = orc_bf16_to_f32(s_bits), b = orc_bf16_to_f32(b_bits);
+      for (int64_t i = 0; i < gs; ++i) {
+        int64_t k = g * gs + i;
+        uint32_t q = quantize_code(orc_bf16_to_f32(row[k]), b, s);
+        out[k / 4] |= q << (8 * (k % 4));
+      }
+    }
+  }
+}
+
 int orc_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -432,3 +432,89 @@ def test_tolerance_accepts_rounded_oracle_and_rejects_perturbed():
     nan = yb.copy()
     nan[3] = 0x7FC0
     assert not oracle.within_tolerance(nan, y, A)[3]
+
+
+# ---------------------------------------------------------------- quantizer (BF16 weight -> codes, scales, biases)
+# Reading of the DynQuantizedStorage page's quantize method (no formula on the
+# pages): per group, s = RNE_bf16((max - min) / 255), b = min,
+# q = clamp(rint((v - b) / s), 0, 255).  The pins below hold for that reading
+# independent of how it is evaluated.
+
+def _codes_of(packed):
+    return np.ascontiguousarray(packed, dtype=np.uint32).view(np.uint8).reshape(packed.shape[0], -1)
+
+
+def test_quantize_recovers_every_code_of_an_exact_grid():
+    # v = (q - 128)/16 for q = 0..255: a group spanning the whole code range on
+    # the grid s = 1/16, b = -8 (all values exact in BF16): the codes come back.
+    q = np.arange(256, dtype=np.int64)
+    vals = (q - 128) / 16.0
+    bits = np.array([rne_bf16_of_fraction(Fraction(int(x) - 128, 16)) for x in q], dtype=np.uint16)
+    assert np.array_equal(oracle.bf16_to_f32(bits), vals.astype(np.float32))
+    full = np.concatenate([bits, bits[::-1]]).reshape(2, 256)  # one 256-value group per row
+    packed, s, b = oracle.quantize(full, 256)
+    assert (s == 0x3D80).all() and (b == 0xC100).all()  # 1/16 and -8
+    c = _codes_of(packed)
+    assert np.array_equal(c[0], q.astype(np.uint8)) and np.array_equal(c[1], q[::-1].astype(np.uint8))
+
+
+def test_quantize_constant_group_has_zero_scale_and_bias_equal_to_the_value():
+    w = np.full((3, 64), 0x3FC0, np.uint16)  # 1.5
+    w[1, 32:] = 0xBF80  # -1: second group of row 1 constant too
+    packed, s, b = oracle.quantize(w, 32)
+    assert (s == 0).all()
+    assert (b[0] == 0x3FC0).all() and b[1, 0] == 0x3FC0 and b[1, 1] == 0xBF80
+    assert (_codes_of(packed) == 0).all()
+
+
+@pytest.mark.parametrize("gs", [32, 64, 128])
+def test_quantize_round_trip_bound_exact_rationals(gs):
+    # |q*s + b - v| <= s/2 for every value, except the top of a group whose s
+    # was rounded down: there the clamp at 255 adds at most 255*(s_exact - s).
+    rng = np.random.Generator(np.random.PCG64(600 + gs))
+    w = synth.gen_dense_weight(rng, 6, 4 * gs)
+    packed, s_bits, b_bits = oracle.quantize(w, gs)
+    codes = _codes_of(packed)
+    for n in range(w.shape[0]):
+        for g in range(w.shape[1] // gs):
+            vs = [frac_of_bf16(int(x)) for x in w[n, g * gs:(g + 1) * gs]]
+            lo, hi = min(vs), max(vs)
+            s, b = frac_of_bf16(int(s_bits[n, g])), frac_of_bf16(int(b_bits[n, g]))
+            assert b == lo
+            s_exact = (hi - lo) / 255
+            assert abs(s - s_exact) <= s_exact / 256  # RNE to 8 significant bits
+            for i, v in enumerate(vs):
+                q = int(codes[n, g * gs + i])
+                err = abs(q * s + b - v)
+                ok = err <= s / 2 * (1 + Fraction(1, 1 << 10))
+                clamp = q == 255 and v - b > 255 * s and err <= 255 * (s_exact - s) + s * Fraction(1, 1 << 10)
+                assert ok or clamp, (n, g, i, float(err / s))
+
+
+def test_quantize_extremes_and_monotone_codes():
+    rng = np.random.Generator(np.random.PCG64(611))
+    w = synth.gen_dense_weight(rng, 16, 512)
+    gs = 64
+    packed, s, b = oracle.quantize(w, gs)
+    codes = _codes_of(packed).astype(np.int64)
+    v = oracle.bf16_to_f32(w).astype(np.float64)
+    for n in range(16):
+        for g in range(512 // gs):
+            sl = slice(g * gs, (g + 1) * gs)
+            vv, cc = v[n, sl], codes[n, sl]
+            assert cc[np.argmin(vv)] == 0
+            assert cc[np.argmax(vv)] >= 254
+            order = np.argsort(vv, kind="stable")
+            assert (np.diff(cc[order]) >= 0).all()  # larger value, no smaller code
+
+
+def test_quantize_then_dequantize_is_close_to_the_weight():
+    rng = np.random.Generator(np.random.PCG64(612))
+    w = synth.gen_dense_weight(rng, 32, 256)
+    for gs in (32, 64, 128):
+        packed, s, b = oracle.quantize(w, gs)
+        dq = oracle.bf16_to_f32(oracle.dequantize_to(packed, s, b, gs)).astype(np.float64)
+        v = oracle.bf16_to_f32(w).astype(np.float64)
+        sc = np.repeat(oracle.bf16_to_f32(s).astype(np.float64), gs, axis=1)
+        # quantizer bound (<= s, see above) plus the BF16 rounding of the dequantized value
+        assert (np.abs(dq - v) <= sc + np.abs(dq) * 2.0 ** -8).all()

@@ -10,7 +10,10 @@ Value distributions (the decode/prefill workloads of these layers):
   codes   uint8 uniform on [0, 255], packed 4 per uint32, code k in byte k%4;
   scales  BF16 of fp32 uniform[0.002, 0.01];
   biases  BF16 of fp32 (-128 * scale_bf16 * (1 + U(-0.05, 0.05)));
-  x, gate, up, x_resid: BF16 of fp32 N(0, 1).
+  x, gate, up, x_resid: BF16 of fp32 N(0, 1);
+  dense BF16 weights (the quantizer's input): BF16 of fp32 N(0, 0.02^2), with
+  one row in 64 scaled by 8 (outlier rows) and one value in 512 by 16
+  (outlier values).
 Generator: NumPy PCG64, seed = 1000 * workload_index + shape_index, draws in
 the fixed order codes, scales, bias jitter, then activations.
 """
@@ -69,3 +72,13 @@ def gen_case(workload_index: int, shape_index: int, N: int, K: int, group_size: 
     w = gen_weight(rng, N, K, group_size)
     acts = {name: gen_act(rng, shape) for name, shape in act_shapes.items()}
     return w, acts
+
+
+def gen_dense_weight(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """BF16 bit patterns [N, K] of a dense weight with outlier rows and values."""
+    w = rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.02)
+    rows = rng.random(N) < 1.0 / 64
+    w[rows] *= np.float32(8.0)
+    spikes = rng.random((N, K)) < 1.0 / 512
+    w[spikes] *= np.float32(16.0)
+    return to_bf16_bits(w)
