@@ -12,8 +12,8 @@ plus the activations each launch reads and writes) / measured time per step,
 in GB/s, with each layer's launches replayed as a HIP graph.  The roofline
 object reports the dominant kernel (the gate+up gemv_multi launch) from HIP
 events around a batched, graph-replayed run of that launch alone.  Secondary
-lines: the same layer as seven single-weight launches, dequantize_to and the
-gated GEMV of the 70B-shaped FFN, the small-batch gemm (m = 2..16) and the
+lines: the same layer as seven single-weight launches, the quantizer on an
+8B gate/up weight, dequantize_to and the gated GEMV of the 70B-shaped FFN, the small-batch gemm (m = 2..16) and the
 prefill gemm (m = 512, 2048) in TFLOP/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
@@ -36,7 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from weight_only_quantized_int8_amd import Int8Weight, gemv_multi, load_library, synth  # noqa: E402
+from weight_only_quantized_int8_amd import Int8Weight, binding, gemv_multi, load_library, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
@@ -217,6 +217,24 @@ def secondary(dev, quick):
     b = dequant_bytes(N, K, gs)
     res["dequantize_to_28672x8192_gs128"] = {"us": t * 1e6, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
     del ws, outs
+    torch.cuda.empty_cache()
+
+    N, K, gs = 14336, 4096, 64  # quantize an 8B gate/up weight (BF16 -> codes, scales, biases)
+    rng = np.random.Generator(np.random.PCG64(4200))
+    wd = [bits_dev(synth.gen_dense_weight(rng, N, K), dev) for _ in range(copies_for(3 * N * K))]
+    packed = torch.empty((N, K // 4), dtype=torch.int32, device=dev)
+    sc = torch.empty((N, K // gs), dtype=torch.bfloat16, device=dev)
+    bi = torch.empty((N, K // gs), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def quant(i):
+        w_ = wd[i % len(wd)]
+        binding.int8_quantize(w_.data_ptr(), N, K, gs, packed.data_ptr(), sc.data_ptr(), bi.data_ptr(), stream)
+
+    t = time_batches(quant, 10)
+    b = 2 * N * K + N * K + 4 * N * K // gs
+    res["quantize_14336x4096_gs64"] = {"us": t * 1e6, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
+    del wd, packed, sc, bi
     torch.cuda.empty_cache()
 
     N, K, gs = 8192, 28672, 128  # 70B-shaped down projection, gated + residual

@@ -88,6 +88,21 @@ int int8_dequantize_to(const int8w_weight *w, uint16_t *out, uint64_t stream);
  * y[n] = RNE_bf16(sum_k w[n,k] * x[k]), accumulated in fp32. */
 int int8_gemv(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint64_t stream);
 
+/* quantize: the step before the weight exists -- a BF16 weight w [out_features,
+ * in_features] (row-major, 16-byte aligned) is encoded into packed / scales /
+ * biases with the layout of int8w_weight (rustdoc page of the DynQuantizedStorage
+ * trait, method quantize; the pages give no formula, this is the plain affine
+ * min/max reading).  Per group of group_size values v of a row, in fp32:
+ *   lo = min v (a zero minimum taken as +0), hi = max v,
+ *   scale = RNE_bf16((hi - lo) / 255), bias = lo,
+ *   q = clamp(rint((v - bias) / scale), 0, 255), and q = 0 when scale == 0.
+ * Then |q*scale + bias - v| <= scale/2 except at the top of a group whose
+ * scale rounded down, where the clamp adds at most 255*((hi-lo)/255 - scale).
+ * Inputs must be finite.  Outputs must not overlap w or each other; the shape
+ * rules and error codes are those of int8w_validate applied to the outputs. */
+int int8_quantize(const uint16_t *w, uint32_t out_features, uint32_t in_features, uint32_t group_size,
+                  uint32_t *packed, uint16_t *scales, uint16_t *biases, uint64_t stream);
+
 /* gemv_multi: y[i] = W[i] x for count weights (1 <= count <= INT8W_MAX_MULTI)
  * that share in_features and group_size, in one launch -- the projections of
  * one activation (q, k and v; gate and up) that the page's gemv method runs

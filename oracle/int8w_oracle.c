@@ -210,7 +210,7 @@ void orc_gemv_silu_gate_resid(const uint32_t *packed, const uint16_t *scales,
  *   per group of gs consecutive values v of a row (BF16, widened exactly):
  *     lo = min v, hi = max v
  *     s  = RNE_bf16((hi - lo) / 255)       fp32 subtraction, fp32 division
- *     b  = lo                              already a BF16 value
+ *     b  = lo                              already a BF16 value; -0 taken as +0
  *     q  = clamp(rint((v - b) / s), 0, 255)  fp32 subtraction and division,
  *                                           round half to even
  *   and q = 0 for every value of a group whose s is zero.
@@ -241,6 +241,7 @@ void orc_quantize(const uint16_t *w, int64_t N, int64_t K, int64_t gs, uint32_t 
         if (v < lo) lo = v;
         if (v > hi) hi = v;
       }
+      if (lo == 0.0f) lo = 0.0f; /* a zero minimum is taken as +0 */
       float span = hi - lo;
       float sf = span / 255.0f;
       uint16_t s_bits = orc_f32_to_bf16_rne(sf);

@@ -186,3 +186,19 @@ def test_gemv_multi_rejects():
     assert err(B.int8_gemv_multi([q, k], x, [y0, 2 * A16], 0))[0] == B.INT8W_ERR_ALIAS
     rc, msg = err(B.int8_gemv_multi([q, k], x, [y0, y0 + 2 * 64 - 2], 0))
     assert rc == B.INT8W_ERR_ALIAS and "y[0] and y[1]" in msg
+
+
+def test_quantize_rejects():
+    w, pk, sc, bi = 4 * A16, A16, 2 * A16, 3 * A16
+    assert err(B.int8_quantize(0, 64, 256, 64, pk, sc, bi, 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8_quantize(w, 64, 256, 64, 0, sc, bi, 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8_quantize(w, 0, 256, 64, pk, sc, bi, 0))[0] == B.INT8W_ERR_SHAPE
+    assert err(B.int8_quantize(w, 64, 96, 64, pk, sc, bi, 0))[0] == B.INT8W_ERR_SHAPE
+    assert err(B.int8_quantize(w, 64, 96, 48, pk, sc, bi, 0))[0] == B.INT8W_ERR_UNSUPPORTED
+    assert err(B.int8_quantize(w + 2, 64, 256, 64, pk, sc, bi, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8_quantize(w, 64, 256, 64, pk + 8, sc, bi, 0))[0] == B.INT8W_ERR_ALIGN
+    # outputs over the input or over each other
+    rc, msg = err(B.int8_quantize(w, 64, 256, 64, w + 1024, sc, bi, 0))
+    assert rc == B.INT8W_ERR_ALIAS and "packed" in msg
+    rc, msg = err(B.int8_quantize(w, 64, 256, 64, pk, sc, sc + 64, 0))
+    assert rc == B.INT8W_ERR_ALIAS and "scales" in msg and "biases" in msg

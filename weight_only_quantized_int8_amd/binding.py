@@ -37,7 +37,7 @@ ERROR_NAMES = {
 
 EXPORTED = (
     "int8w_validate", "int8w_storage_bytes", "int8_dequantize_to", "int8_gemv", "int8_gemv_silu_gate",
-    "int8_gemv_silu_gate_resid", "int8_gemm", "int8_gemv_multi", "int8w_last_error",
+    "int8_gemv_silu_gate_resid", "int8_gemm", "int8_gemv_multi", "int8_quantize", "int8w_last_error",
 )
 MAX_MULTI = 4  # INT8W_MAX_MULTI
 
@@ -96,6 +96,9 @@ def load_library() -> ctypes.CDLL:
     lib.int8_gemm.restype = ctypes.c_int
     lib.int8_gemv_multi.argtypes = [W, ctypes.c_uint32, P, ctypes.POINTER(P), u64]
     lib.int8_gemv_multi.restype = ctypes.c_int
+    u32 = ctypes.c_uint32
+    lib.int8_quantize.argtypes = [P, u32, u32, u32, P, P, P, u64]
+    lib.int8_quantize.restype = ctypes.c_int
     lib.int8w_last_error.argtypes = []
     lib.int8w_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -136,6 +139,11 @@ def int8_gemv_silu_gate_resid(desc: WeightDesc, gate: int, up: int, x_resid: int
 
 def int8_gemm(desc: WeightDesc, x: int, y: int, m: int, stream: int) -> int:
     return load_library().int8_gemm(ctypes.byref(desc), x, y, m, stream)
+
+
+def int8_quantize(w: int, out_features: int, in_features: int, group_size: int, packed: int, scales: int,
+                  biases: int, stream: int) -> int:
+    return load_library().int8_quantize(w, out_features, in_features, group_size, packed, scales, biases, stream)
 
 
 def int8_gemv_multi(descs, x: int, ys, stream: int) -> int:
@@ -195,6 +203,22 @@ class Int8Weight:
         self.device = packed.device
         self.desc = WeightDesc(packed.data_ptr(), scales.data_ptr(), biases.data_ptr(), N, K, gs)
         _check(int8w_validate(self.desc))
+
+    @classmethod
+    def quantize(cls, w: torch.Tensor, group_size: int) -> "Int8Weight":
+        """Encode a BF16 weight [out_features, in_features] on the GPU (int8_quantize)."""
+        if w.dtype != torch.bfloat16 or w.dim() != 2 or not w.is_contiguous() or w.device.type != "cuda":
+            raise ValueError("w must be a contiguous 2-D bfloat16 GPU tensor")
+        N, K = w.shape
+        gs = int(group_size)
+        if gs <= 0 or K % gs or K % 4:
+            raise ValueError(f"group_size {gs} must divide in_features {K} (a multiple of 4)")
+        packed = torch.empty((N, K // 4), dtype=torch.int32, device=w.device)
+        scales = torch.empty((N, K // gs), dtype=torch.bfloat16, device=w.device)
+        biases = torch.empty((N, K // gs), dtype=torch.bfloat16, device=w.device)
+        _check(int8_quantize(w.data_ptr(), N, K, gs, packed.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                             _stream_of(w.device)))
+        return cls(packed, scales, biases, gs)
 
     @classmethod
     def from_arrays(cls, packed, scales_bits, biases_bits, group_size: int, device="cuda") -> "Int8Weight":

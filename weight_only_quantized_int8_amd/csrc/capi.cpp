@@ -164,6 +164,27 @@ int int8_gemv(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint64_t st
                        as_stream(stream));
 }
 
+int int8_quantize(const uint16_t *w, uint32_t out_features, uint32_t in_features, uint32_t group_size,
+                  uint32_t *packed, uint16_t *scales, uint16_t *biases, uint64_t stream) {
+  const int8w_weight out = {packed, scales, biases, out_features, in_features, group_size};
+  int rc = validate(&out);
+  if (rc) return rc;
+  if (!w) return fail(INT8W_ERR_NULL, "w is NULL");
+  if (!aligned(w, 16)) return fail(INT8W_ERR_ALIGN, "w is not 16-byte aligned");
+  Range outs[3];
+  weight_ranges(&out, outs);
+  const Range in = range("w", w, (uint64_t)out_features * in_features * 2);
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], in)) return fail(INT8W_ERR_ALIAS, "output %s overlaps input w", outs[i].name);
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(INT8W_ERR_ALIAS, "outputs %s and %s overlap", outs[j].name, outs[i].name);
+  }
+  (void)hipGetLastError();
+  return finish_launch(launch_quantize(w, out_features, in_features, group_size, packed, scales, biases,
+                                       as_stream(stream)),
+                       as_stream(stream));
+}
+
 int int8_gemv_multi(const int8w_weight *w, uint32_t count, const uint16_t *x, uint16_t *const *y,
                     uint64_t stream) {
   if (!w || !y || !x) return fail(INT8W_ERR_NULL, "weights, x or y is NULL");

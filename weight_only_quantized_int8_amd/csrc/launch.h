@@ -31,6 +31,10 @@ hipError_t launch_gemv(const WeightView &w, GemvEpilogue epi, const uint16_t *x_
 hipError_t launch_gemv_multi(const WeightView *w, uint16_t *const *y, uint32_t count, const uint16_t *x,
                              hipStream_t stream);
 
+// BF16 weight [N, K] -> codes (packed), scales, biases [N, K/gs] (affine min/max).
+hipError_t launch_quantize(const uint16_t *w, uint32_t N, uint32_t K, uint32_t gs, uint32_t *packed, uint16_t *scales,
+                           uint16_t *biases, hipStream_t stream);
+
 // Y[m, N] = X[m, K] W^T for 2 <= m <= 16 (matrix cores, per-group rescale).
 // Only for shapes where smallm_supported(K, gs) (the per-row scale/bias stage
 // fits the LDS); others go to launch_gemm_prefill.

@@ -1,0 +1,171 @@
+// quantize.hip -- BF16 weight -> 8-bit affine codes, scales and biases for
+// gfx950 (rustdoc page of the DynQuantizedStorage trait, method quantize; the
+// target layout is the MlxInt8Weight page's packed / scales / biases fields).
+//
+// The pages give no formula; this is the plain affine min/max reading, in
+// fp32, one operation at a time (the CPU oracle takes the same steps, so the
+// codes agree bit for bit):
+//   per group of gs consecutive values v of a row:
+//     lo = min v, hi = max v
+//     s  = RNE_bf16((hi - lo) / 255)            (fp32 subtraction, IEEE division)
+//     b  = lo                                   (a BF16 value already; -0 taken as +0)
+//     q  = clamp(rint((v - b) / s), 0, 255)     (IEEE division, ties to even)
+//   and q = 0 for a group whose s is zero.  Inputs must be finite.
+//
+// HBM-bound streaming kernel: 2 bytes read and 1 + 4/gs bytes written per
+// value.  The matrix is a flat run of 16-byte chunks (8 values); a group is
+// gs/8 consecutive chunks and never crosses a row (gs divides K), so a wave
+// handles 64 consecutive chunks (1 KiB) per item and its lanes meet per group
+// with cross-lane min/max.  Waves stream contiguous, balanced item ranges
+// through bounded buffer resources, two blocks of items in flight.
+#include "common.h"
+#include "launch.h"
+
+namespace int8w {
+
+namespace {
+
+constexpr int kQThreads = 512;  // 8 waves
+constexpr int kQWaves = kQThreads / 64;
+constexpr int kQU = 4;          // items per pipeline block
+
+__device__ __forceinline__ uint32_t uniform_q(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// one code, in the order of the definition above
+__device__ __forceinline__ uint32_t quant_code(float v, float b, float s) {
+  if (s == 0.0f) return 0u;
+  const float t = __fdiv_rn(v - b, s);
+  float r = __builtin_rintf(t);
+  r = r < 0.0f ? 0.0f : r;
+  r = r > 255.0f ? 255.0f : r;
+  return (uint32_t)r;
+}
+
+template <int U>
+struct QBlock {
+  u32x4 v[U];
+};
+
+// LPG = lanes per group = gs / 8
+template <int U, int LPG>
+__global__ __launch_bounds__(kQThreads) void k_quantize(const uint16_t *__restrict__ w, uint8_t *__restrict__ codes,
+                                                        uint16_t *__restrict__ scales, uint16_t *__restrict__ biases,
+                                                        uint64_t chunks) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint64_t gw = (uint64_t)blockIdx.x * kQWaves + uniform_q(threadIdx.x >> 6);
+  const uint64_t TW = (uint64_t)gridDim.x * kQWaves;
+  const uint64_t items = (chunks + 63u) >> 6;
+  const uint64_t iq = items / TW, ir = items % TW;
+  const uint64_t ibeg = gw * iq + (gw < ir ? gw : ir);
+  const uint32_t nit = (uint32_t)(iq + (gw < ir ? 1u : 0u));
+
+  // this wave's window of the input: items [ibeg, ibeg + nit), 1 KiB each
+  const uint64_t c0 = ibeg << 6;  // first chunk
+  const uint64_t cend = (ibeg + nit) << 6 < chunks ? (ibeg + nit) << 6 : chunks;
+  const auto rw = make_rsrc(w + (c0 << 3), (uint32_t)((cend > c0 ? cend - c0 : 0u) << 4));
+  const uint32_t vo = lane << 4;
+
+  uint32_t i_item = 0, i_left = nit;
+  auto issue = [&](QBlock<U> &blk) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = i_left != 0u;
+      const uint32_t so = uniform_q(live ? i_item << 10 : 0u);
+      blk.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(live ? vo : kOutOfRange), (int)so, kAuxNontemporal);
+      i_left -= live ? 1u : 0u;
+      ++i_item;
+    }
+  };
+  uint32_t c_item = 0, c_left = nit;
+  auto consume = [&](const QBlock<U> &blk) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c_left) {
+        const uint64_t c = c0 + ((uint64_t)c_item << 6) + lane;  // this lane's chunk
+        const bool mine = c < chunks;
+        const uint32_t wv[4] = {blk.v[u].x, blk.v[u].y, blk.v[u].z, blk.v[u].w};
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = bf16_lo(wv[i]);
+          f[2 * i + 1] = bf16_hi(wv[i]);
+        }
+        float lo = f[0], hi = f[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+          lo = fminf(lo, f[i]);
+          hi = fmaxf(hi, f[i]);
+        }
+        // lanes past the end hold zeros; they sit in their own (unwritten)
+        // groups, since chunks is a whole number of groups
+#pragma unroll
+        for (int off = 1; off < LPG; off <<= 1) {
+          lo = fminf(lo, __shfl_xor(lo, off, 64));
+          hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+        }
+        if (lo == 0.0f) lo = 0.0f;  // a zero minimum is +0 (the bias of an all-zero group is +0)
+        const float sf = __fdiv_rn(hi - lo, 255.0f);
+        const uint16_t s_bits = to_bf16_bits(sf);
+        const uint16_t b_bits = to_bf16_bits(lo);  // exact
+        const float s = bf16_bits_to_f32(s_bits), b = bf16_bits_to_f32(b_bits);
+        uint32_t q0 = 0, q1 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          q0 |= quant_code(f[i], b, s) << (8 * i);
+          q1 |= quant_code(f[4 + i], b, s) << (8 * i);
+        }
+        if (mine) {
+          *reinterpret_cast<uint2 *>(codes + (c << 3)) = make_uint2(q0, q1);
+          if ((lane & (LPG - 1)) == 0u) {
+            const uint64_t grp = c / LPG;
+            scales[grp] = s_bits;
+            biases[grp] = b_bits;
+          }
+        }
+        --c_left;
+        ++c_item;
+      }
+    }
+  };
+
+  QBlock<U> A, B;
+  const uint32_t nblk = (nit + U - 1) / U;
+  if (nblk) issue(A);
+  for (uint32_t bl = 0; bl < nblk;) {
+    if (bl + 1 >= nblk) { consume(A); break; }
+    issue(B);
+    consume(A);
+    ++bl;
+    if (bl + 1 >= nblk) { consume(B); break; }
+    issue(A);
+    consume(B);
+    ++bl;
+  }
+}
+
+template <int LPG>
+hipError_t launch_lpg(const uint16_t *w, uint64_t chunks, uint32_t *packed, uint16_t *scales, uint16_t *biases,
+                      hipStream_t stream) {
+  const uint64_t items = (chunks + 63u) / 64u;
+  uint64_t blocks = 2u * (uint64_t)device_cu_count();
+  const uint64_t need = (items + kQWaves - 1) / kQWaves;
+  if (blocks > need) blocks = need;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL((k_quantize<kQU, LPG>), dim3((uint32_t)blocks), dim3(kQThreads), 0, stream, w,
+                     reinterpret_cast<uint8_t *>(packed), scales, biases, chunks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const uint16_t *w, uint32_t N, uint32_t K, uint32_t gs, uint32_t *packed, uint16_t *scales,
+                           uint16_t *biases, hipStream_t stream) {
+  const uint64_t chunks = (uint64_t)N * K / 8u;
+  switch (gs) {
+    case 32: return launch_lpg<4>(w, chunks, packed, scales, biases, stream);
+    case 64: return launch_lpg<8>(w, chunks, packed, scales, biases, stream);
+    default: return launch_lpg<16>(w, chunks, packed, scales, biases, stream);
+  }
+}
+
+}  // namespace int8w
