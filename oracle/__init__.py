@@ -11,7 +11,11 @@ description ("8-bit affine", no Drop), the packed/scales/biases field sections
 and the methods dequantize_to, gemv, gemv_silu_gate, gemv_silu_gate_resid and
 gemm.  ``quantize`` (BF16 weight -> codes, scales, biases) follows the rustdoc
 page of the DynQuantizedStorage trait, method quantize, which gives no formula:
-its reading (affine min/max in fp32) is stated in ``int8w_oracle.c``.  Readings the page leaves open (byte order, signedness, precision,
+its reading (affine min/max in fp32) is stated in ``int8w_oracle.c``.
+``moe_gemv`` (expert-indexed products) follows the same trait page, provided
+method indexed_moe_forward, which gives only a signature; its reading (stacked
+experts, per-slot ids, NaN for an id with no expert) is stated in
+``int8w_oracle.c``.  Readings the page leaves open (byte order, signedness, precision,
 rounding, silu) are stated in ``int8w_oracle.c``'s header.
 
 Pins: every function is checked against something other than itself in
@@ -67,6 +71,7 @@ def _load():
         lib.orc_gemv_silu_gate.argtypes = [p, p, p, i64, i64, i64, p, p, p, p]
         lib.orc_gemv_silu_gate_resid.argtypes = [p, p, p, i64, i64, i64, p, p, p, p, p]
         lib.orc_quantize.argtypes = [p, i64, i64, i64, p, p, p]
+        lib.orc_moe_gemv.argtypes = [p, p, p, i64, i64, i64, i64, p, i64, p, i64, i64, p, p]
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -230,6 +235,33 @@ def quantize(w_bits, group_size):
     biases = np.zeros((N, K // gs), np.uint16)
     _load().orc_quantize(_ptr(w), N, K, gs, _ptr(packed), _ptr(scales), _ptr(biases))
     return packed, scales, biases
+
+
+def moe_gemv(packed, scales, biases, group_size, num_experts, x, ids):
+    """Expert-indexed products (see orc_moe_gemv for the reading).
+
+    packed [E*N, K/4], scales/biases [E*N, K/gs] hold E = num_experts stacked
+    experts; x is BF16 [T, S, K] with S = 1 or topk; ids is uint32 [T, topk].
+    Returns fp64 (y [T, topk, N], A [T, topk, N]); a slot whose id is not below
+    E gets NaN outputs (A = 0)."""
+    packed, scales, biases, EN, K, gs = _weight(packed, scales, biases, group_size)
+    E = int(num_experts)
+    if E <= 0 or EN % E:
+        raise ValueError(f"{EN} stacked rows are not a whole number of {E} experts")
+    N = EN // E
+    ids = _c(ids, np.uint32)
+    if ids.ndim != 2:
+        raise ValueError("ids must be [tokens, topk]")
+    T, topk = ids.shape
+    x = _c(x, np.uint16)
+    if x.ndim != 3 or x.shape[0] != T or x.shape[2] != K or x.shape[1] not in (1, topk):
+        raise ValueError("x must be [tokens, 1 or topk, in_features]")
+    S = x.shape[1]
+    y = np.empty((T, topk, N), dtype=np.float64)
+    A = np.empty((T, topk, N), dtype=np.float64)
+    _load().orc_moe_gemv(_ptr(packed), _ptr(scales), _ptr(biases), E, N, K, gs, _ptr(x), S, _ptr(ids), T, topk,
+                         _ptr(y), _ptr(A))
+    return y, A
 
 
 def within_tolerance(y_bf16_bits, y_ref, A, rel: float = 8e-3, absA: float = 2e-3) -> np.ndarray:

@@ -258,6 +258,43 @@ void orc_quantize(const uint16_t *w, int64_t N, int64_t K, int64_t gs, uint32_t 
   }
 }
 
+/* ---- expert-indexed product: the DynQuantizedStorage trait page, provided
+ * method indexed_moe_forward.  The page gives only the signature (the
+ * quantized tensor's shape, an input, and ids selecting experts); the reading
+ * taken here:
+ *   - the quantized tensor holds E experts of [N, K], stacked along rows, so
+ *     expert e is rows e*N .. e*N + N - 1 of one packed/scales/biases set;
+ *   - the input is BF16 [T, S, K] with S = 1 (every slot of a token reads the
+ *     token's row) or S = topk (slot j of token t reads its own row);
+ *   - ids are uint32 [T, topk]; slot (t, j) uses expert ids[t, j];
+ *   - the output is [T, topk, N]: y[t, j, :] = W_e x_(t, j) with e = ids[t, j].
+ * A slot whose id is not below E has no expert: its outputs are NaN.  Each
+ * slot's product is the gemm above on that expert's rows, so the arithmetic
+ * (fp32 weight, fp64 sums) is the same. */
+void orc_moe_gemv(const uint32_t *packed, const uint16_t *scales, const uint16_t *biases, int64_t E,
+                  int64_t N, int64_t K, int64_t gs, const uint16_t *x, int64_t S, const uint32_t *ids,
+                  int64_t T, int64_t topk, double *y, double *Aabs) {
+  const int64_t G = K / gs;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t j = 0; j < topk; ++j) {
+      const int64_t slot = t * topk + j;
+      const uint32_t e = ids[slot];
+      double *ys = y + slot * N;
+      double *as = Aabs + slot * N;
+      if ((int64_t)e >= E) {
+        for (int64_t n = 0; n < N; ++n) {
+          ys[n] = NAN;
+          as[n] = 0.0;
+        }
+        continue;
+      }
+      const uint16_t *xs = x + (t * S + (S == 1 ? 0 : j)) * K;
+      orc_gemm(packed + (int64_t)e * N * (K / 4), scales + (int64_t)e * N * G, biases + (int64_t)e * N * G, N, K,
+               gs, xs, 1, ys, as);
+    }
+  }
+}
+
 int orc_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

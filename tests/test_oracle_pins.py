@@ -518,3 +518,108 @@ def test_quantize_then_dequantize_is_close_to_the_weight():
         sc = np.repeat(oracle.bf16_to_f32(s).astype(np.float64), gs, axis=1)
         # quantizer bound (<= s, see above) plus the BF16 rounding of the dequantized value
         assert (np.abs(dq - v) <= sc + np.abs(dq) * 2.0 ** -8).all()
+
+
+# ---------------------------------------------------------------- expert-indexed products
+#
+# The DynQuantizedStorage trait page, provided method indexed_moe_forward,
+# gives only a signature.  The oracle reads it as: E experts of [N, K] stacked
+# along rows, x [T, S, K] with S = 1 or topk, ids [T, topk], y [T, topk, N]
+# with y[t, j] = W_ids[t, j] x_(t, j), NaN for an id with no expert.  The pins
+# build experts whose products have closed forms, so a wrong expert offset (in
+# the codes, the scales or the biases), a wrong input row or a wrong output
+# slot fails one of them.
+
+def _stack_codes(codes_u8):
+    """uint8 codes [rows, K] -> packed words, code k in byte k % 4 of word k / 4."""
+    assert np.little_endian
+    return np.ascontiguousarray(codes_u8, dtype=np.uint8).view(np.uint32)
+
+
+def _shifted_experts(E, N, K, gs):
+    # expert e, row n: a single code 1 at k* = (3n + 5e) % K, every other code
+    # 0, bias 0, scale (1 + g + 2e) / 4 in group g (exact in BF16)
+    codes = np.zeros((E * N, K), np.uint8)
+    kstar = np.zeros((E, N), np.int64)
+    G = K // gs
+    sv = np.zeros((E * N, G), np.float64)
+    for e in range(E):
+        for n in range(N):
+            k = (3 * n + 5 * e) % K
+            kstar[e, n] = k
+            codes[e * N + n, k] = 1
+            sv[e * N + n] = [(1 + g + 2 * e) / 4.0 for g in range(G)]
+    s_bits = np.array([[rne_bf16_of_fraction(Fraction(v).limit_denominator(4)) for v in row] for row in sv], np.uint16)
+    assert np.array_equal(oracle.bf16_to_f32(s_bits).astype(np.float64), sv)
+    b_bits = np.zeros_like(s_bits)
+    return _stack_codes(codes), s_bits, b_bits, kstar, sv
+
+
+@pytest.mark.parametrize("S", ["one", "topk"])
+def test_moe_gemv_selects_expert_row_and_slot(S):
+    E, N, K, gs, T, topk = 4, 24, 64, 32, 5, 3
+    packed, s_bits, b_bits, kstar, sv = _shifted_experts(E, N, K, gs)
+    rng = np.random.Generator(np.random.PCG64(700))
+    ids = rng.integers(0, E, size=(T, topk)).astype(np.uint32)
+    ids[0, :] = [2, 2, 1]  # a repeated expert within one token
+    xs = 1 if S == "one" else topk
+    x = synth.gen_act(rng, (T, xs, K))
+    y, A = oracle.moe_gemv(packed, s_bits, b_bits, gs, E, x, ids)
+    xv = oracle.bf16_to_f32(x).astype(np.float64)
+    assert y.shape == (T, topk, N)
+    for t in range(T):
+        for j in range(topk):
+            e = int(ids[t, j])
+            row = xv[t, 0 if xs == 1 else j]
+            for n in range(N):
+                k = kstar[e, n]
+                want = sv[e * N + n, k // gs] * row[k]
+                assert y[t, j, n] == want, (t, j, n)
+                assert A[t, j, n] == abs(want)
+
+
+def test_moe_gemv_bias_terms_use_the_experts_biases():
+    # all codes 0: y[t, j, n] = sum_g b[e, n, g] * sum_{k in g} x[k]
+    E, N, K, gs, T, topk = 3, 16, 128, 32, 4, 2
+    G = K // gs
+    rng = np.random.Generator(np.random.PCG64(701))
+    packed = np.zeros((E * N, K // 4), np.uint32)
+    s_bits = oracle.f32_to_bf16(rng.uniform(0.002, 0.01, (E * N, G)).astype(np.float32))
+    b_bits = oracle.f32_to_bf16(rng.normal(0, 1, (E * N, G)).astype(np.float32))
+    ids = rng.integers(0, E, size=(T, topk)).astype(np.uint32)
+    x = synth.gen_act(rng, (T, 1, K))
+    y, _ = oracle.moe_gemv(packed, s_bits, b_bits, gs, E, x, ids)
+    bv = oracle.bf16_to_f32(b_bits).astype(np.float64).reshape(E, N, G)
+    xg = oracle.bf16_to_f32(x).astype(np.float64).reshape(T, G, gs).sum(axis=2)
+    want = np.einsum("tjng,tg->tjn", bv[ids.astype(np.int64)], xg)
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-12)
+
+
+def test_moe_gemv_id_without_expert_gives_nan_and_leaves_other_slots():
+    E, N, K, gs = 4, 8, 64, 64
+    packed, s_bits, b_bits, kstar, sv = _shifted_experts(E, N, K, gs)
+    rng = np.random.Generator(np.random.PCG64(702))
+    x = synth.gen_act(rng, (2, 1, K))
+    good = np.array([[1, 3], [0, 2]], np.uint32)
+    bad = good.copy()
+    bad[0, 1] = E
+    bad[1, 0] = 0xFFFFFFFF
+    yg, _ = oracle.moe_gemv(packed, s_bits, b_bits, gs, E, x, good)
+    yb, Ab = oracle.moe_gemv(packed, s_bits, b_bits, gs, E, x, bad)
+    assert np.isnan(yb[0, 1]).all() and np.isnan(yb[1, 0]).all()
+    assert (Ab[0, 1] == 0).all() and (Ab[1, 0] == 0).all()
+    assert np.array_equal(yb[0, 0], yg[0, 0]) and np.array_equal(yb[1, 1], yg[1, 1])
+
+
+def test_moe_gemv_per_slot_rows_equal_to_token_row_match_shared_row():
+    rng = np.random.Generator(np.random.PCG64(703))
+    E, N, K, gs, T, topk = 3, 20, 96, 32, 3, 2
+    w = synth.gen_weight(rng, E * N, K, gs)
+    ids = rng.integers(0, E, size=(T, topk)).astype(np.uint32)
+    x1 = synth.gen_act(rng, (T, 1, K))
+    xk = np.repeat(x1, topk, axis=1)
+    y1, A1 = oracle.moe_gemv(w.packed, w.scales, w.biases, gs, E, x1, ids)
+    yk, Ak = oracle.moe_gemv(w.packed, w.scales, w.biases, gs, E, xk, ids)
+    assert np.array_equal(y1, yk) and np.array_equal(A1, Ak)
+    y0, _ = oracle.moe_gemv(w.packed, w.scales, w.biases, gs, E, x1[:0], ids[:0])
+    assert y0.shape == (0, topk, N)
