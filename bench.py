@@ -13,8 +13,10 @@ in GB/s, with each layer's launches replayed as a HIP graph.  The roofline
 object reports the dominant kernel (the gate+up gemv_multi launch) from HIP
 events around a batched, graph-replayed run of that launch alone.  Secondary
 lines: the same layer as seven single-weight launches, the quantizer on an
-8B gate/up weight, dequantize_to and the gated GEMV of the 70B-shaped FFN, the small-batch gemm (m = 2..16) and the
-prefill gemm (m = 512, 2048) in TFLOP/s.
+8B gate/up weight, the expert-indexed gemv over 8 experts of that shape (top-2
+routing, 1 and 4 tokens), dequantize_to and the gated GEMV of the 70B-shaped
+FFN, the small-batch gemm (m = 2..16) and the prefill gemm (m = 512, 2048) in
+TFLOP/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
        python bench.py --profile-only     # dominant kernel + calibration copy, for rocprofv3
@@ -36,7 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from weight_only_quantized_int8_amd import Int8Weight, binding, gemv_multi, load_library, synth  # noqa: E402
+from weight_only_quantized_int8_amd import Int8Weight, binding, gemv_multi, load_library, moe_gemv, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
@@ -235,6 +237,34 @@ def secondary(dev, quick):
     b = 2 * N * K + N * K + 4 * N * K // gs
     res["quantize_14336x4096_gs64"] = {"us": t * 1e6, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
     del wd, packed, sc, bi
+    torch.cuda.empty_cache()
+
+    # expert-indexed gemv: 8 experts of the 8B gate/up shape, top-2 routing.
+    # One token: consecutive calls name disjoint expert pairs, so every call
+    # streams its two experts from HBM.  Four tokens: random routing over two
+    # copies of the stacked experts; bytes count each distinct expert once.
+    E, N, K, gs = 8, 14336, 4096, 64
+    stacks = make_weights(4300, E * N, K, gs, 2, dev)
+    rng = np.random.Generator(np.random.PCG64(4301))
+    x1 = bits_dev(synth.gen_act(rng, (1, 1, K)), dev)
+    y1 = torch.empty((1, 2, N), dtype=torch.bfloat16, device=dev)
+    pairs = [torch.tensor([[2 * i, 2 * i + 1]], dtype=torch.int32, device=dev) for i in range(4)]
+    t = time_batches(lambda i: moe_gemv(stacks[0], E, x1, pairs[i % 4], y1), 40)
+    b = 2 * (N * K + 4 * N * K // gs) + 2 * K + 2 * 2 * N + 4 * 2
+    res["moe_gemv_8x14336x4096_gs64_top2_t1"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
+                                                 "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
+    T = 4
+    x4 = bits_dev(synth.gen_act(rng, (T, 1, K)), dev)
+    y4 = torch.empty((T, 2, N), dtype=torch.bfloat16, device=dev)
+    id_sets = [synth.gen_ids(rng, T, 2, E) for _ in range(8)]
+    distinct = float(np.mean([len(np.unique(s)) for s in id_sets]))
+    ids4 = [torch.from_numpy(s.view(np.int32)).to(dev) for s in id_sets]
+    t = time_batches(lambda i: moe_gemv(stacks[i % 2], E, x4, ids4[i % 8], y4), 40)
+    b = distinct * (N * K + 4 * N * K // gs) + 2 * T * K + 2 * T * 2 * N + 4 * T * 2
+    res["moe_gemv_8x14336x4096_gs64_top2_t4"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
+                                                 "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
+                                                 "distinct_experts": distinct}
+    del stacks
     torch.cuda.empty_cache()
 
     N, K, gs = 8192, 28672, 128  # 70B-shaped down projection, gated + residual

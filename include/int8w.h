@@ -117,6 +117,29 @@ int int8_quantize(const uint16_t *w, uint32_t out_features, uint32_t in_features
 int int8_gemv_multi(const int8w_weight *w, uint32_t count, const uint16_t *x, uint16_t *const *y,
                     uint64_t stream);
 
+/* moe_gemv: the expert-indexed product (rustdoc page of the DynQuantizedStorage
+ * trait, provided method indexed_moe_forward, which gives the signature only:
+ * the quantized tensor's shape, an input and the ids of the experts).  Read as:
+ *   - `experts` holds num_experts experts of [N, in_features] stacked along
+ *     rows: its out_features is num_experts * N, and expert e is rows
+ *     e*N .. e*N + N - 1 (validated like any weight);
+ *   - x is BF16 [tokens, x_rows, in_features], x_rows = 1 (every slot of a
+ *     token reads the token's row) or x_rows = topk (each slot its own row);
+ *   - ids is a DEVICE uint32 array [tokens, topk], 4-byte aligned, read by
+ *     the kernel (never on the host);
+ *   - y is BF16 [tokens, topk, N]: y[t, j, n] = sum_k w_e[n, k] x_(t,j)[k]
+ *     with e = ids[t, j], with int8_gemv's arithmetic and bound.
+ * A slot whose id is not below num_experts reads no weight and gets the BF16
+ * quiet NaN 0x7FC0 in all N outputs.  Each slot streams its expert's rows:
+ * an expert named by several slots (tokens > 1) is read once per slot.
+ * tokens = 0 or topk = 0 is a no-op.  Errors: INT8W_ERR_SHAPE for num_experts = 0 or not dividing
+ * out_features, x_rows not 1 or topk, or more than INT8W_MAX_MOE_SLOTS slots;
+ * INT8W_ERR_ALIGN for x not 16-byte or ids not 4-byte aligned; INT8W_ERR_ALIAS
+ * for y overlapping the experts, x or ids. */
+#define INT8W_MAX_MOE_SLOTS 65536
+int int8_moe_gemv(const int8w_weight *experts, uint32_t num_experts, const uint16_t *x, uint32_t x_rows,
+                  const uint32_t *ids, uint32_t tokens, uint32_t topk, uint16_t *y, uint64_t stream);
+
 /* gemv_silu_gate: y = W (silu(gate) * up) in one launch, silu(g) = g/(1+e^-g).
  * gate and up are BF16 [in_features]; the product silu(gate)*up is formed in
  * fp32 on chip and never written to memory.  y as for int8_gemv. */

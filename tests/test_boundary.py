@@ -202,3 +202,30 @@ def test_quantize_rejects():
     assert rc == B.INT8W_ERR_ALIAS and "packed" in msg
     rc, msg = err(B.int8_quantize(w, 64, 256, 64, pk, sc, sc + 64, 0))
     assert rc == B.INT8W_ERR_ALIAS and "scales" in msg and "biases" in msg
+
+
+def test_moe_gemv_rejects():
+    w = desc(N=64, K=256, gs=64)  # 4 experts of [16, 256] stacked
+    x, ids, y = 4 * A16, 5 * A16, 6 * A16
+    assert B.int8_moe_gemv(w, 4, x, 1, ids, 0, 2, y, 0) == B.INT8W_OK  # no slots: nothing to do
+    assert B.int8_moe_gemv(w, 4, x, 1, ids, 3, 0, y, 0) == B.INT8W_OK
+    rc, msg = err(B.int8_moe_gemv(w, 0, x, 1, ids, 1, 2, y, 0))
+    assert rc == B.INT8W_ERR_SHAPE and "experts" in msg
+    assert err(B.int8_moe_gemv(w, 3, x, 1, ids, 1, 2, y, 0))[0] == B.INT8W_ERR_SHAPE
+    assert err(B.int8_moe_gemv(desc(N=0), 4, x, 1, ids, 1, 2, y, 0))[0] == B.INT8W_ERR_SHAPE
+    rc, msg = err(B.int8_moe_gemv(w, 4, x, 1, ids, 40000, 2, y, 0))
+    assert rc == B.INT8W_ERR_SHAPE and "slots" in msg
+    rc, msg = err(B.int8_moe_gemv(w, 4, x, 3, ids, 1, 2, y, 0))
+    assert rc == B.INT8W_ERR_SHAPE and "x_rows" in msg
+    for args in ((0, ids, y), (x, 0, y), (x, ids, 0)):
+        assert err(B.int8_moe_gemv(w, 4, args[0], 1, args[1], 1, 2, args[2], 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8_moe_gemv(w, 4, x + 8, 1, ids, 1, 2, y, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8_moe_gemv(w, 4, x, 1, ids + 2, 1, 2, y, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8_moe_gemv(w, 4, x, 1, ids, 1, 2, y + 1, 0))[0] == B.INT8W_ERR_ALIGN
+    # y [tokens, topk, N] over x [tokens, x_rows, K], over ids, over the experts
+    rc, msg = err(B.int8_moe_gemv(w, 4, x, 2, ids, 3, 2, x + 6 * 256 * 2 - 2, 0))
+    assert rc == B.INT8W_ERR_ALIAS and "input x" in msg
+    rc, msg = err(B.int8_moe_gemv(w, 4, x, 1, ids, 3, 2, ids + 20, 0))
+    assert rc == B.INT8W_ERR_ALIAS and "ids" in msg
+    rc, msg = err(B.int8_moe_gemv(w, 4, x, 1, ids, 1, 2, 3 * A16 + 64, 0))
+    assert rc == B.INT8W_ERR_ALIAS and "biases" in msg

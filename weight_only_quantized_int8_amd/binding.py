@@ -37,9 +37,11 @@ ERROR_NAMES = {
 
 EXPORTED = (
     "int8w_validate", "int8w_storage_bytes", "int8_dequantize_to", "int8_gemv", "int8_gemv_silu_gate",
-    "int8_gemv_silu_gate_resid", "int8_gemm", "int8_gemv_multi", "int8_quantize", "int8w_last_error",
+    "int8_gemv_silu_gate_resid", "int8_gemm", "int8_gemv_multi", "int8_quantize", "int8_moe_gemv",
+    "int8w_last_error",
 )
 MAX_MULTI = 4  # INT8W_MAX_MULTI
+MAX_MOE_SLOTS = 65536  # INT8W_MAX_MOE_SLOTS
 
 
 class Int8wError(RuntimeError):
@@ -99,6 +101,8 @@ def load_library() -> ctypes.CDLL:
     u32 = ctypes.c_uint32
     lib.int8_quantize.argtypes = [P, u32, u32, u32, P, P, P, u64]
     lib.int8_quantize.restype = ctypes.c_int
+    lib.int8_moe_gemv.argtypes = [W, u32, P, u32, P, u32, u32, P, u64]
+    lib.int8_moe_gemv.restype = ctypes.c_int
     lib.int8w_last_error.argtypes = []
     lib.int8w_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -144,6 +148,11 @@ def int8_gemm(desc: WeightDesc, x: int, y: int, m: int, stream: int) -> int:
 def int8_quantize(w: int, out_features: int, in_features: int, group_size: int, packed: int, scales: int,
                   biases: int, stream: int) -> int:
     return load_library().int8_quantize(w, out_features, in_features, group_size, packed, scales, biases, stream)
+
+
+def int8_moe_gemv(desc: WeightDesc, num_experts: int, x: int, x_rows: int, ids: int, tokens: int, topk: int,
+                  y: int, stream: int) -> int:
+    return load_library().int8_moe_gemv(ctypes.byref(desc), num_experts, x, x_rows, ids, tokens, topk, y, stream)
 
 
 def int8_gemv_multi(descs, x: int, ys, stream: int) -> int:
@@ -299,3 +308,30 @@ def gemv_multi(weights, x: torch.Tensor, ys=None):
         _need_bf16(y, "y", w.out_features, dev)
     _check(int8_gemv_multi([w.desc for w in weights], x.data_ptr(), [y.data_ptr() for y in ys], _stream_of(dev)))
     return ys
+
+
+def moe_gemv(experts: Int8Weight, num_experts: int, x: torch.Tensor, ids: torch.Tensor, y=None):
+    """Expert-indexed gemv (int8_moe_gemv).
+
+    experts: E = num_experts experts of [N, K] stacked along rows (out_features = E*N)
+    x:       bfloat16 [tokens, 1 or topk, K]
+    ids:     int32/uint32 [tokens, topk] on the GPU (expert of each slot)
+    returns  bfloat16 [tokens, topk, N]; a slot whose id is not below E is NaN
+    """
+    dev = experts.device
+    E = int(num_experts)
+    if E <= 0 or experts.out_features % E:
+        raise ValueError(f"{experts.out_features} rows are not a whole number of {E} experts")
+    N, K = experts.out_features // E, experts.in_features
+    if ids.dim() != 2 or ids.dtype not in (torch.int32, torch.uint32) or ids.device != dev or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous 32-bit [tokens, topk] tensor on the weight's GPU")
+    T, topk = ids.shape
+    if x.dim() != 3 or x.shape[0] != T or x.shape[2] != K or x.shape[1] not in (1, topk):
+        raise ValueError(f"x must be [{T}, 1 or {topk}, {K}]")
+    _need_bf16(x, "x", x.numel(), dev)
+    if y is None:
+        y = torch.empty((T, topk, N), dtype=torch.bfloat16, device=dev)
+    _need_bf16(y, "y", T * topk * N, dev)
+    _check(int8_moe_gemv(experts.desc, E, x.data_ptr(), x.shape[1], ids.data_ptr(), T, topk, y.data_ptr(),
+                         _stream_of(dev)))
+    return y

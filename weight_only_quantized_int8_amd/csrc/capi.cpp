@@ -217,6 +217,36 @@ int int8_gemv_multi(const int8w_weight *w, uint32_t count, const uint16_t *x, ui
   return finish_launch(launch_gemv_multi(views, y, count, x, as_stream(stream)), as_stream(stream));
 }
 
+int int8_moe_gemv(const int8w_weight *experts, uint32_t num_experts, const uint16_t *x, uint32_t x_rows,
+                  const uint32_t *ids, uint32_t tokens, uint32_t topk, uint16_t *y, uint64_t stream) {
+  int rc = validate(experts);
+  if (rc) return rc;
+  if (num_experts == 0 || experts->out_features % num_experts != 0)
+    return fail(INT8W_ERR_SHAPE, "%u stacked rows are not a whole number of %u experts", experts->out_features,
+                num_experts);
+  const uint64_t slots = (uint64_t)tokens * topk;
+  if (slots > INT8W_MAX_MOE_SLOTS)
+    return fail(INT8W_ERR_SHAPE, "tokens*topk = %llu exceeds %d slots", (unsigned long long)slots,
+                INT8W_MAX_MOE_SLOTS);
+  if (slots == 0) return ok();
+  if (x_rows != 1 && x_rows != topk) return fail(INT8W_ERR_SHAPE, "x_rows %u is neither 1 nor topk %u", x_rows, topk);
+  if (!x || !ids || !y) return fail(INT8W_ERR_NULL, "x, ids or y is NULL");
+  if (!aligned(x, 16)) return fail(INT8W_ERR_ALIGN, "x is not 16-byte aligned");
+  if (!aligned(ids, 4)) return fail(INT8W_ERR_ALIGN, "ids is not 4-byte aligned");
+  if (!aligned(y, 2)) return fail(INT8W_ERR_ALIGN, "y is not 2-byte aligned");
+  const uint64_t N = experts->out_features / num_experts, K = experts->in_features;
+  Range ins[5];
+  weight_ranges(experts, ins);
+  ins[3] = range("x", x, (uint64_t)tokens * x_rows * K * 2);
+  ins[4] = range("ids", ids, slots * 4);
+  rc = check_alias(range("y", y, slots * N * 2), ins, 5);
+  if (rc) return rc;
+  (void)hipGetLastError();
+  return finish_launch(launch_moe_gemv(view(experts), num_experts, x, x_rows, ids, tokens, topk, y,
+                                       as_stream(stream)),
+                       as_stream(stream));
+}
+
 static int gemv_gated(const int8w_weight *w, const uint16_t *gate, const uint16_t *up, const uint16_t *x_resid,
                       uint16_t *y, uint64_t stream, bool with_resid) {
   int rc = validate(w);

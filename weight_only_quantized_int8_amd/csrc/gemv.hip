@@ -395,6 +395,43 @@ __global__ __launch_bounds__(64 * W) void k_gemv_multi(GemvTargets t, const uint
                                       tile_runs, max_rows);
 }
 
+// Expert-indexed gemv (the DynQuantizedStorage trait page, provided method
+// indexed_moe_forward): slot p of tokens x topk takes the weight of expert
+// ids[p] (rows ids[p]*N .. +N-1 of the stacked codes) and its token's input
+// row (or its own, x_rows == topk).  Workgroup b serves slot b % slots, part
+// b / slots of that slot's rows: every slot gets the same share of the GPU,
+// and each slot streams its expert once, so an expert named by several slots
+// is streamed once per slot.  A slot whose id is not below E writes NaN and
+// reads no weight.
+template <int W, int RP, int U, bool TAIL>
+__global__ __launch_bounds__(64 * W) void k_moe_gemv(const uint8_t *__restrict__ codes,
+                                                     const uint16_t *__restrict__ scales,
+                                                     const uint16_t *__restrict__ biases,
+                                                     const uint16_t *__restrict__ x, const uint32_t *__restrict__ ids,
+                                                     uint16_t *y, uint32_t N, uint32_t E, uint32_t topk,
+                                                     uint32_t x_rows, uint32_t slots, uint32_t K, uint32_t gs_log2,
+                                                     uint32_t tile_runs, uint32_t max_rows) {
+  const uint32_t p = blockIdx.x % slots;
+  const uint32_t part = blockIdx.x / slots;
+  const uint32_t TW = (gridDim.x / slots) * W;
+  const uint32_t lw = part * W + uniform(threadIdx.x >> 6);
+  const uint32_t e = uniform(ids[p]);
+  uint16_t *yp = y + (size_t)p * N;
+  if (e >= E) {
+    const uint32_t rq = N / TW, rr = N % TW;
+    const uint32_t rbeg = lw * rq + (lw < rr ? lw : rr);
+    const uint32_t nr = rq + (lw < rr ? 1u : 0u);
+    for (uint32_t r = threadIdx.x & 63u; r < nr; r += 64u) yp[rbeg + r] = 0x7FC0u;
+    return;
+  }
+  const uint32_t t = p / topk, j = p - t * topk;
+  const uint16_t *xp = x + ((size_t)t * x_rows + (x_rows == 1u ? 0u : j)) * K;
+  const size_t G = K >> gs_log2;
+  gemv_wave<kEpiNone, W, RP, U, TAIL>(codes + (size_t)e * N * K, scales + (size_t)e * N * G,
+                                      biases + (size_t)e * N * G, yp, N, lw, TW, xp, xp, nullptr, K, gs_log2,
+                                      tile_runs, max_rows);
+}
+
 template <typename Kern>
 hipError_t raise_lds_cap(Kern kern, bool &configured) {
   if (configured) return hipSuccess;
@@ -543,6 +580,49 @@ hipError_t launch_gemv_list(const WeightView *w, uint16_t *const *y, uint32_t co
   return launch_targets(cfg, t, w[0].K, w[0].gs, epi, x_or_gate, up, x_resid, stream);
 }
 
+template <int W, int RP, bool TAIL>
+hipError_t launch_moe_cfg(const GemvCfg &cfg, const WeightView &w, uint32_t E, const uint16_t *x, uint32_t x_rows,
+                          const uint32_t *ids, uint32_t topk, uint32_t slots, uint16_t *y, hipStream_t stream) {
+  static bool configured = false;
+  auto kern = k_moe_gemv<W, RP, kLoadsPerBlock / RP, TAIL>;
+  hipError_t e = raise_lds_cap(kern, configured);
+  if (e != hipSuccess) return e;
+  const uint32_t gs_log2 = (uint32_t)__builtin_ctz(w.gs);
+  const size_t lds = lds_bytes(cfg, w.gs);
+  hipLaunchKernelGGL(kern, dim3(cfg.blocks), dim3(64 * W), lds, stream, reinterpret_cast<const uint8_t *>(w.packed),
+                     w.scales, w.biases, x, ids, y, w.N / E, E, topk, x_rows, slots, w.K, gs_log2, cfg.ct,
+                     cfg.max_rows);
+  return hipGetLastError();
+}
+
+// Launch shape of the expert-indexed gemv: every slot gets the same number
+// of workgroups (the gemv's wave shape), enough for all slots together to
+// fill the GPU and for no wave to own more than kMaxRowsPerWave rows.
+GemvCfg choose_moe_cfg(uint32_t N, uint32_t K, uint32_t gs, uint32_t slots) {
+  const uint32_t cus = (uint32_t)device_cu_count();
+  GemvCfg c{};
+  c.waves = K <= 8192u ? 8 : 16;
+  const uint32_t per_cu = c.waves == 8 ? 2u : 1u;
+  const uint32_t W = (uint32_t)c.waves;
+  uint32_t per_slot = (per_cu * cus + slots - 1) / slots;
+  const uint32_t most = (N + W - 1) / W;                                  // no more waves than rows
+  const uint32_t least = (N + W * kMaxRowsPerWave - 1) / (W * kMaxRowsPerWave);
+  if (per_slot > most) per_slot = most;
+  if (per_slot < least) per_slot = least;
+  const uint32_t tw = per_slot * W;
+  c.blocks = per_slot * slots;
+  c.max_rows = (N + tw - 1) / tw;
+  c.rp = c.waves == 16 && N / tw >= 2u ? 2 : 1;
+  const uint32_t cpr = K / 16u;
+  const size_t budget = kLdsPerCu / per_cu;
+  for (uint32_t ntiles = (cpr + kTileRunsMax - 1) / kTileRunsMax;; ++ntiles) {
+    c.ct = ((cpr + ntiles - 1) / ntiles + 63u) / 64u * 64u;
+    if (lds_bytes(c, gs) <= budget || c.ct == 64u) break;
+  }
+  c.tail = (cpr % 64u) != 0;
+  return c;
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const WeightView &w, GemvEpilogue epi, const uint16_t *x_or_gate,
@@ -554,6 +634,21 @@ hipError_t launch_gemv(const WeightView &w, GemvEpilogue epi, const uint16_t *x_
 hipError_t launch_gemv_multi(const WeightView *w, uint16_t *const *y, uint32_t count, const uint16_t *x,
                              hipStream_t stream) {
   return launch_gemv_list(w, y, count, kEpiNone, x, nullptr, nullptr, stream);
+}
+
+hipError_t launch_moe_gemv(const WeightView &w, uint32_t E, const uint16_t *x, uint32_t x_rows, const uint32_t *ids,
+                           uint32_t tokens, uint32_t topk, uint16_t *y, hipStream_t stream) {
+  const uint32_t slots = tokens * topk;
+  const GemvCfg cfg = choose_moe_cfg(w.N / E, w.K, w.gs, slots);
+  if (cfg.waves == 16) {
+    if (cfg.rp == 2)
+      return cfg.tail ? launch_moe_cfg<16, 2, true>(cfg, w, E, x, x_rows, ids, topk, slots, y, stream)
+                      : launch_moe_cfg<16, 2, false>(cfg, w, E, x, x_rows, ids, topk, slots, y, stream);
+    return cfg.tail ? launch_moe_cfg<16, 1, true>(cfg, w, E, x, x_rows, ids, topk, slots, y, stream)
+                    : launch_moe_cfg<16, 1, false>(cfg, w, E, x, x_rows, ids, topk, slots, y, stream);
+  }
+  return cfg.tail ? launch_moe_cfg<8, 1, true>(cfg, w, E, x, x_rows, ids, topk, slots, y, stream)
+                  : launch_moe_cfg<8, 1, false>(cfg, w, E, x, x_rows, ids, topk, slots, y, stream);
 }
 
 }  // namespace int8w

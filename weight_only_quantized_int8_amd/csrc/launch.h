@@ -31,6 +31,13 @@ hipError_t launch_gemv(const WeightView &w, GemvEpilogue epi, const uint16_t *x_
 hipError_t launch_gemv_multi(const WeightView *w, uint16_t *const *y, uint32_t count, const uint16_t *x,
                              hipStream_t stream);
 
+// Expert-indexed gemv: w holds E experts of [w.N / E, K] stacked along rows;
+// y[p, :] = W_ids[p] x_row(p) for the tokens * topk slots p (x_row(p) is the
+// token's row, or the slot's own when x_rows == topk).  ids are read on the
+// device; a slot whose id is not below E gets NaN outputs.
+hipError_t launch_moe_gemv(const WeightView &w, uint32_t E, const uint16_t *x, uint32_t x_rows, const uint32_t *ids,
+                           uint32_t tokens, uint32_t topk, uint16_t *y, hipStream_t stream);
+
 // BF16 weight [N, K] -> codes (packed), scales, biases [N, K/gs] (affine min/max).
 hipError_t launch_quantize(const uint16_t *w, uint32_t N, uint32_t K, uint32_t gs, uint32_t *packed, uint16_t *scales,
                            uint16_t *biases, hipStream_t stream);

@@ -82,3 +82,14 @@ def gen_dense_weight(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
     spikes = rng.random((N, K)) < 1.0 / 512
     w[spikes] *= np.float32(16.0)
     return to_bf16_bits(w)
+
+
+def gen_ids(rng: np.random.Generator, tokens: int, topk: int, num_experts: int) -> np.ndarray:
+    """Synthetic routing: each token names topk distinct experts, uniformly at
+    random (what a top-k router yields), as uint32 [tokens, topk]."""
+    if topk > num_experts:
+        raise ValueError("topk exceeds the number of experts")
+    out = np.empty((tokens, topk), np.uint32)
+    for t in range(tokens):
+        out[t] = rng.permutation(num_experts)[:topk]
+    return out
