@@ -15,8 +15,11 @@ its reading (affine min/max in fp32) is stated in ``int8w_oracle.c``.
 ``moe_gemv`` (expert-indexed products) follows the same trait page, provided
 method indexed_moe_forward, which gives only a signature; its reading (stacked
 experts, per-slot ids, NaN for an id with no expert) is stated in
-``int8w_oracle.c``.  Readings the page leaves open (byte order, signedness, precision,
-rounding, silu) are stated in ``int8w_oracle.c``'s header.
+``int8w_oracle.c``.  ``fp8_gemv`` follows the rustdoc page "Fp8Weight" (E4M3
+bytes with per-row, per-block or single scales); its readings are stated in
+``int8w_oracle.c``.  Readings the MlxInt8Weight page leaves open (byte order,
+signedness, precision, rounding, silu) are stated in ``int8w_oracle.c``'s
+header.
 
 Pins: every function is checked against something other than itself in
 ``tests/test_oracle_pins.py`` (library routines, exact rational arithmetic,
@@ -71,6 +74,9 @@ def _load():
         lib.orc_gemv_silu_gate.argtypes = [p, p, p, i64, i64, i64, p, p, p, p]
         lib.orc_gemv_silu_gate_resid.argtypes = [p, p, p, i64, i64, i64, p, p, p, p, p]
         lib.orc_quantize.argtypes = [p, i64, i64, i64, p, p, p]
+        lib.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        lib.orc_e4m3_to_f64.restype = ctypes.c_double
+        lib.orc_fp8_gemv.argtypes = [p, p, i64, i64, ctypes.c_int, i64, ctypes.c_double, p, p, p]
         lib.orc_moe_gemv.argtypes = [p, p, p, i64, i64, i64, i64, p, i64, p, i64, i64, p, p]
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -261,6 +267,52 @@ def moe_gemv(packed, scales, biases, group_size, num_experts, x, ids):
     A = np.empty((T, topk, N), dtype=np.float64)
     _load().orc_moe_gemv(_ptr(packed), _ptr(scales), _ptr(biases), E, N, K, gs, _ptr(x), S, _ptr(ids), T, topk,
                          _ptr(y), _ptr(A))
+    return y, A
+
+
+FP8_PER_ROW, FP8_BLOCK_BF16, FP8_BLOCK_F32, FP8_SINGLE = 0, 1, 2, 3
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """E4M3 bytes -> fp64 values (NaN for 0x7F / 0xFF); see orc_e4m3_to_f64."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    lib = _load()
+    table = np.array([lib.orc_e4m3_to_f64(i) for i in range(256)], dtype=np.float64)
+    return table[c]
+
+
+def fp8_gemv(weight, scale, scale_format, x, block_size=128, single_scale=1.0):
+    """y = W x for an FP8 E4M3 weight [N, K] (uint8 bytes) with one of the
+    three scale layouts of the rustdoc page "Fp8Weight"; returns fp64 (y, A).
+
+    scale: float32 [N] (FP8_PER_ROW), BF16 bit patterns [ceil(N/BS), ceil(K/BS)]
+    (FP8_BLOCK_BF16), float32 of that shape (FP8_BLOCK_F32), or None with
+    single_scale (FP8_SINGLE)."""
+    w = _c(weight, np.uint8)
+    if w.ndim != 2:
+        raise ValueError("weight must be [N, K] bytes")
+    N, K = w.shape
+    bs = int(block_size)
+    fmt = int(scale_format)
+    nb, kb = -(-N // bs), -(-K // bs)
+    if fmt == FP8_PER_ROW:
+        sc = _c(scale, np.float32).reshape(-1)
+        if sc.size != N:
+            raise ValueError("per-row scale must be [N] f32")
+    elif fmt in (FP8_BLOCK_BF16, FP8_BLOCK_F32):
+        sc = _c(scale, np.uint16 if fmt == FP8_BLOCK_BF16 else np.float32)
+        if sc.shape != (nb, kb):
+            raise ValueError(f"block scale must be [{nb}, {kb}]")
+    elif fmt == FP8_SINGLE:
+        sc = np.zeros(1, np.float32)
+    else:
+        raise ValueError(f"unknown scale format {fmt}")
+    x = _c(x, np.uint16).reshape(-1)
+    if x.size != K:
+        raise ValueError("x must be [K]")
+    y = np.empty(N, dtype=np.float64)
+    A = np.empty(N, dtype=np.float64)
+    _load().orc_fp8_gemv(_ptr(w), _ptr(sc), N, K, fmt, bs, float(np.float32(single_scale)), _ptr(x), _ptr(y), _ptr(A))
     return y, A
 
 

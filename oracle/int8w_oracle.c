@@ -295,6 +295,69 @@ void orc_moe_gemv(const uint32_t *packed, const uint16_t *scales, const uint16_t
   }
 }
 
+/* ---- FP8 E4M3 weight: the rustdoc page "Fp8Weight" (spark_model::weight_map),
+ * struct description and fields weight, row_scale, n, k, scale_format.
+ *
+ * The page names the format (E4M3) and the three scale layouts but gives no
+ * formulas.  Readings taken here:
+ *   - E4M3 is the 8-bit floating-point format with sign bit 7, exponent bits
+ *     6..3 (bias 7) and mantissa bits 2..0: exponent 0 gives the subnormals
+ *     (m/8) * 2^-6, exponents 1..15 give (1 + m/8) * 2^(e-7), and the two codes
+ *     with all of exponent and mantissa set (0x7F, 0xFF) are NaN; there are no
+ *     infinities (largest finite value 448).
+ *   - The weight is w[n, k] = E4M3(q[n, k]) * scale, the scale taken from:
+ *       format 0, per-row:   f32 [N], scale[n];
+ *       format 1, per-block: BF16 [ceil(N/BS), ceil(K/BS)], scale[n/BS][k/BS];
+ *       format 2, per-block: the same shape in f32 (the page gives the block
+ *                            scales as BF16 in its format list and as FP32 in
+ *                            its transpose method; both are accepted);
+ *       format 3, single:    one global f32 value (the page bakes it into the
+ *                            kernel; here it is an argument).
+ *   - y[n] = sum_k w[n, k] x[k] for BF16 x, evaluated in fp64 ascending k; the
+ *     decoded value (4 significant bits) times an f32 or BF16 scale, and that
+ *     times a BF16 x, are exact in fp64, so only the sum rounds. */
+double orc_e4m3_to_f64(uint8_t c) {
+  const int sign = (c >> 7) & 1, e = (c >> 3) & 0xF, m = c & 7;
+  double v;
+  if (e == 0xF && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+static double fp8_scale(const void *scale, int fmt, int64_t bs, double single, int64_t n, int64_t k, int64_t K) {
+  switch (fmt) {
+    case 0: return (double)((const float *)scale)[n];
+    case 1: {
+      const int64_t kb = (K + bs - 1) / bs;
+      return (double)orc_bf16_to_f32(((const uint16_t *)scale)[(n / bs) * kb + k / bs]);
+    }
+    case 2: {
+      const int64_t kb = (K + bs - 1) / bs;
+      return (double)((const float *)scale)[(n / bs) * kb + k / bs];
+    }
+    default: return single;
+  }
+}
+
+void orc_fp8_gemv(const uint8_t *w, const void *scale, int64_t N, int64_t K, int fmt, int64_t bs, double single,
+                  const uint16_t *x, double *y, double *Aabs) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    double sum = 0.0, sum_abs = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double wv = orc_e4m3_to_f64(w[n * K + k]) * fp8_scale(scale, fmt, bs, single, n, k, K);
+      const double t = wv * (double)orc_bf16_to_f32(x[k]);
+      sum += t;
+      sum_abs += fabs(t);
+    }
+    y[n] = sum;
+    Aabs[n] = sum_abs;
+  }
+}
+
 int orc_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -623,3 +623,109 @@ def test_moe_gemv_per_slot_rows_equal_to_token_row_match_shared_row():
     assert np.array_equal(y1, yk) and np.array_equal(A1, Ak)
     y0, _ = oracle.moe_gemv(w.packed, w.scales, w.biases, gs, E, x1[:0], ids[:0])
     assert y0.shape == (0, topk, N)
+
+
+# ---------------------------------------------------------------- FP8 E4M3 weight
+#
+# The rustdoc page "Fp8Weight": [N, K] E4M3 bytes with a per-row f32 scale, a
+# per-block scale [N/BS, K/BS] (BF16 on the page's format list, FP32 in its
+# transpose method; the oracle takes both) or one global scale.
+
+E4M3_ONE = 0x38  # exponent 7, mantissa 0
+
+
+def test_e4m3_decode_matches_torch_float8_e4m3fn_on_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))  # -0 at 0x80
+
+
+def test_e4m3_decode_hand_values():
+    # from the bit layout: 0x38 = 2^(7-7); 0x7E = 1.75 * 2^8 (largest finite);
+    # 0x01 = (1/8) 2^-6 (smallest subnormal); 0x08 = 2^-6 (smallest normal);
+    # 0x07 = (7/8) 2^-6 (largest subnormal); 0xB8 = -1; 0x80 = -0; 0x7F, 0xFF NaN
+    table = {0x38: 1.0, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x08: 2.0 ** -6, 0x07: 7 * 2.0 ** -9,
+             0xB8: -1.0, 0x80: -0.0, 0x3C: 1.5, 0x40: 2.0, 0x30: 0.5}
+    got = oracle.e4m3_to_f64(np.array(list(table), np.uint8))
+    assert got.tolist() == list(table.values())
+    assert np.isnan(oracle.e4m3_to_f64(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def test_fp8_per_row_identity_gives_scaled_x():
+    N, K = 40, 96
+    rng = np.random.Generator(np.random.PCG64(720))
+    w = np.zeros((N, K), np.uint8)
+    w[np.arange(N), (np.arange(N) * 7) % K] = E4M3_ONE
+    scale = (2.0 ** rng.integers(-12, 3, N)).astype(np.float32)
+    x = synth.gen_act(rng, K)
+    y, A = oracle.fp8_gemv(w, scale, oracle.FP8_PER_ROW, x)
+    xv = oracle.bf16_to_f32(x).astype(np.float64)
+    want = scale.astype(np.float64) * xv[(np.arange(N) * 7) % K]
+    assert np.array_equal(y, want) and np.array_equal(A, np.abs(want))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f32"])
+@pytest.mark.parametrize("N,K,bs", [(300, 520, 128), (64, 256, 64), (129, 1000, 128)])
+def test_fp8_block_scales_index_by_row_and_column_block(fmt, N, K, bs):
+    # every code 1.0: y[n] = sum_kb s[n // bs, kb] * sum_{k in block kb} x[k]
+    rng = np.random.Generator(np.random.PCG64(721 + N))
+    nb, kb = -(-N // bs), -(-K // bs)
+    w = np.full((N, K), E4M3_ONE, np.uint8)
+    sv = rng.uniform(0.5, 2.0, (nb, kb)).astype(np.float32)
+    if fmt == "bf16":
+        scale = oracle.f32_to_bf16(sv)
+        sd = oracle.bf16_to_f32(scale).astype(np.float64)
+        x = synth.gen_act(rng, K)
+        y, _ = oracle.fp8_gemv(w, scale, oracle.FP8_BLOCK_BF16, x, bs)
+    else:
+        scale = sv
+        sd = sv.astype(np.float64)
+        x = synth.gen_act(rng, K)
+        y, _ = oracle.fp8_gemv(w, scale, oracle.FP8_BLOCK_F32, x, bs)
+    xv = oracle.bf16_to_f32(x).astype(np.float64)
+    xs = np.array([xv[j * bs:(j + 1) * bs].sum() for j in range(kb)])
+    want = np.array([(sd[n // bs] * xs).sum() for n in range(N)])
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_single_scale_equals_per_row_with_equal_scales():
+    rng = np.random.Generator(np.random.PCG64(722))
+    N, K = 50, 192
+    w = rng.integers(0, 256, (N, K), dtype=np.uint8)
+    w[(w & 0x7F) == 0x7F] = 0x00  # no NaN codes
+    x = synth.gen_act(rng, K)
+    y1, A1 = oracle.fp8_gemv(w, None, oracle.FP8_SINGLE, x, single_scale=0.0125)
+    y2, A2 = oracle.fp8_gemv(w, np.full(N, 0.0125, np.float32), oracle.FP8_PER_ROW, x)
+    assert np.array_equal(y1, y2) and np.array_equal(A1, A2)
+
+
+def test_fp8_brute_force_rationals():
+    rng = np.random.Generator(np.random.PCG64(723))
+    N, K, bs = 6, 40, 16
+    w = rng.integers(0, 256, (N, K), dtype=np.uint8)
+    w[(w & 0x7F) == 0x7F] = 0x3C
+    sv = oracle.f32_to_bf16(rng.uniform(0.001, 0.01, (-(-N // bs), -(-K // bs))).astype(np.float32))
+    x = synth.gen_act(rng, K)
+    y, A = oracle.fp8_gemv(w, sv, oracle.FP8_BLOCK_BF16, x, bs)
+    dec = torch.from_numpy(w.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for n in range(N):
+        tot = Fraction(0)
+        tot_abs = Fraction(0)
+        for k in range(K):
+            t = Fraction(float(dec[n, k])) * frac_of_bf16(int(sv[n // bs, k // bs])) * frac_of_bf16(int(x[k]))
+            tot += t
+            tot_abs += abs(t)
+        assert abs(Fraction(y[n]) - tot) <= tot_abs * Fraction(1, 1 << 50)
+        assert abs(Fraction(A[n]) - tot_abs) <= tot_abs * Fraction(1, 1 << 50)
+
+
+def test_fp8_nan_code_makes_its_row_nan():
+    w = np.full((3, 64), E4M3_ONE, np.uint8)
+    w[1, 17] = 0x7F
+    x = synth.gen_act(np.random.Generator(np.random.PCG64(724)), 64)
+    y, _ = oracle.fp8_gemv(w, np.ones(3, np.float32), oracle.FP8_PER_ROW, x)
+    assert np.isnan(y[1]) and np.isfinite(y[[0, 2]]).all()
