@@ -14,7 +14,8 @@ object reports the dominant kernel (the gate+up gemv_multi launch) from HIP
 events around a batched, graph-replayed run of that launch alone.  Secondary
 lines: the same layer as seven single-weight launches, the quantizer on an
 8B gate/up weight, the expert-indexed gemv over 8 experts of that shape (top-2
-routing, 1 and 4 tokens), dequantize_to and the gated GEMV of the 70B-shaped
+routing, 1 and 4 tokens), the FP8 E4M3 gemv (per-row and 128 x 128 block
+scales) on the 8B FFN shapes, dequantize_to and the gated GEMV of the 70B-shaped
 FFN, the small-batch gemm (m = 2..16) and the prefill gemm (m = 512, 2048) in
 TFLOP/s.
 
@@ -38,7 +39,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from weight_only_quantized_int8_amd import Int8Weight, binding, gemv_multi, load_library, moe_gemv, synth  # noqa: E402
+from weight_only_quantized_int8_amd import (Fp8Weight, Int8Weight, binding, gemv_multi, load_library,  # noqa: E402
+                                           moe_gemv, synth)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
@@ -265,6 +267,26 @@ def secondary(dev, quick):
                                                  "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
                                                  "distinct_experts": distinct}
     del stacks
+    torch.cuda.empty_cache()
+
+    # FP8 E4M3 weight gemv on the 8B gate/up and down shapes, per-row f32 and
+    # 128 x 128 block BF16 scales
+    for N, K in ((14336, 4096), (4096, 14336)):
+        for name, fmt in (("row", binding.FP8_PER_ROW), ("block128_bf16", binding.FP8_BLOCK_BF16)):
+            rng = np.random.Generator(np.random.PCG64(4400 + N))
+            codes = torch.from_numpy(synth.gen_fp8_codes(rng, N, K)).to(dev)
+            if fmt == binding.FP8_PER_ROW:
+                sc = torch.from_numpy(synth.gen_fp8_scale(rng, N, bf16=False)).to(dev)
+            else:
+                sc = bits_dev(synth.gen_fp8_scale(rng, (-(-N // 128), -(-K // 128)), bf16=True), dev)
+            ws = [Fp8Weight(codes.clone(), sc.clone(), fmt, 128) for _ in range(copies_for(N * K))]
+            x = bits_dev(synth.gen_act(rng, K), dev)
+            y = torch.empty(N, dtype=torch.bfloat16, device=dev)
+            t = time_batches(lambda i: ws[i % len(ws)].gemv(x, y), 30)
+            b = N * K + sc.numel() * sc.element_size() + 2 * K + 2 * N
+            res[f"fp8_gemv_{name}_{N}x{K}"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
+                                                "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
+            del ws, codes, sc
     torch.cuda.empty_cache()
 
     N, K, gs = 8192, 28672, 128  # 70B-shaped down projection, gated + residual

@@ -140,6 +140,42 @@ int int8_gemv_multi(const int8w_weight *w, uint32_t count, const uint16_t *x, ui
 int int8_moe_gemv(const int8w_weight *experts, uint32_t num_experts, const uint16_t *x, uint32_t x_rows,
                   const uint32_t *ids, uint32_t tokens, uint32_t topk, uint16_t *y, uint64_t stream);
 
+/* ---- FP8 E4M3 weights (rustdoc page "Fp8Weight": struct description and the
+ * fields weight, row_scale, n, k, scale_format).  The weight is n x k E4M3
+ * bytes, row-major (sign bit 7, exponent bits 6..3 with bias 7, mantissa bits
+ * 2..0; exponent 0 is subnormal; 0x7F and 0xFF are NaN; no infinities), and
+ * w[i,j] = E4M3(weight[i,j]) * scale with the scale laid out per the tag: */
+enum {
+  INT8W_FP8_PER_ROW = 0,    /* scale: device f32 [n], scale[i] */
+  INT8W_FP8_BLOCK_BF16 = 1, /* scale: device BF16 [ceil(n/BS), ceil(k/BS)], scale[i/BS][j/BS] */
+  INT8W_FP8_BLOCK_F32 = 2,  /* the same shape in f32 (the page gives block scales as BF16 in
+                               its format list and as FP32 in its transpose method) */
+  INT8W_FP8_SINGLE = 3      /* scale pointer NULL; single_scale is the one global value */
+};
+
+typedef struct {
+  const uint8_t *weight; /* device, [n, k] E4M3 bytes, 16-byte aligned */
+  const void *scale;     /* device, layout per scale_format (4-byte aligned f32, 2-byte BF16); NULL for SINGLE */
+  uint32_t n;            /* output features (rows) */
+  uint32_t k;            /* input features (columns), a multiple of 16 */
+  uint32_t scale_format; /* INT8W_FP8_* */
+  uint32_t block_size;   /* BS for the block formats: a power of two, 64..1024 (128 on the page) */
+  float single_scale;    /* the global scale for INT8W_FP8_SINGLE */
+} int8w_fp8_weight;
+
+/* fp8_gemv: y = W x.  x is BF16 [k], 16-byte aligned; y is BF16 with at least
+ * n elements, of which exactly n are written:
+ *   y[i] = RNE_bf16(sum_j E4M3(weight[i,j]) * scale * x[j]), accumulated in fp32
+ * (a block scale multiplies each 16-code run's partial sum, a row or global
+ * scale the row's total); a NaN code gives a NaN output.  The bound is
+ * int8_gemv's.  Errors: INT8W_ERR_NULL (weight, x, y, or the scale of a
+ * non-SINGLE format is NULL), INT8W_ERR_SHAPE (n or k zero, k not a multiple of
+ * 16, k > 2^24, n*k/16 >= 2^31, or a scale given with SINGLE),
+ * INT8W_ERR_UNSUPPORTED (unknown format, block_size not a power of two in
+ * 64..1024), INT8W_ERR_ALIGN, INT8W_ERR_ALIAS (y overlapping weight, scale or
+ * x). */
+int int8w_fp8_gemv(const int8w_fp8_weight *w, const uint16_t *x, uint16_t *y, uint64_t stream);
+
 /* gemv_silu_gate: y = W (silu(gate) * up) in one launch, silu(g) = g/(1+e^-g).
  * gate and up are BF16 [in_features]; the product silu(gate)*up is formed in
  * fp32 on chip and never written to memory.  y as for int8_gemv. */

@@ -229,3 +229,41 @@ def test_moe_gemv_rejects():
     assert rc == B.INT8W_ERR_ALIAS and "ids" in msg
     rc, msg = err(B.int8_moe_gemv(w, 4, x, 1, ids, 1, 2, 3 * A16 + 64, 0))
     assert rc == B.INT8W_ERR_ALIAS and "biases" in msg
+
+
+def fp8desc(n=64, k=256, fmt=B.FP8_PER_ROW, weight=A16, scale=2 * A16, bs=128, single=1.0):
+    return B.Fp8WeightDesc(weight, scale, n, k, fmt, bs, single)
+
+
+def test_fp8_gemv_rejects():
+    x, y = 4 * A16, 5 * A16
+    rc, msg = err(B.int8w_fp8_gemv(fp8desc(weight=0), x, y, 0))
+    assert rc == B.INT8W_ERR_NULL
+    assert err(B.int8w_fp8_gemv(fp8desc(n=0), x, y, 0))[0] == B.INT8W_ERR_SHAPE
+    rc, msg = err(B.int8w_fp8_gemv(fp8desc(k=200), x, y, 0))
+    assert rc == B.INT8W_ERR_SHAPE and "multiple of 16" in msg
+    rc, msg = err(B.int8w_fp8_gemv(fp8desc(fmt=7), x, y, 0))
+    assert rc == B.INT8W_ERR_UNSUPPORTED and "scale_format" in msg
+    for bs in (0, 32, 96, 2048):
+        rc, msg = err(B.int8w_fp8_gemv(fp8desc(fmt=B.FP8_BLOCK_BF16, bs=bs), x, y, 0))
+        assert rc == B.INT8W_ERR_UNSUPPORTED and "block_size" in msg
+    # the tag decides what the scale must be
+    assert err(B.int8w_fp8_gemv(fp8desc(scale=0), x, y, 0))[0] == B.INT8W_ERR_NULL
+    assert err(B.int8w_fp8_gemv(fp8desc(fmt=B.FP8_BLOCK_F32, scale=0), x, y, 0))[0] == B.INT8W_ERR_NULL
+    rc, msg = err(B.int8w_fp8_gemv(fp8desc(fmt=B.FP8_SINGLE), x, y, 0))
+    assert rc == B.INT8W_ERR_SHAPE and "NULL" in msg
+    assert err(B.int8w_fp8_gemv(fp8desc(scale=2 * A16 + 2), x, y, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8w_fp8_gemv(fp8desc(fmt=B.FP8_BLOCK_F32, scale=2 * A16 + 2), x, y, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8w_fp8_gemv(fp8desc(weight=A16 + 8), x, y, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8w_fp8_gemv(fp8desc(), x + 8, y, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8w_fp8_gemv(fp8desc(), x, y + 1, 0))[0] == B.INT8W_ERR_ALIGN
+    assert err(B.int8w_fp8_gemv(fp8desc(), 0, y, 0))[0] == B.INT8W_ERR_NULL
+    # y over the weight, the scale (its extent depends on the layout) or x
+    rc, msg = err(B.int8w_fp8_gemv(fp8desc(), x, A16 + 64 * 256 - 2, 0))
+    assert rc == B.INT8W_ERR_ALIAS and "weight" in msg
+    rc, msg = err(B.int8w_fp8_gemv(fp8desc(), x, 2 * A16 + 64 * 4 - 2, 0))
+    assert rc == B.INT8W_ERR_ALIAS and "scale" in msg
+    rc, msg = err(B.int8w_fp8_gemv(fp8desc(fmt=B.FP8_BLOCK_BF16, n=300, k=528), x, 2 * A16 + 3 * 5 * 2 - 2, 0))
+    assert rc == B.INT8W_ERR_ALIAS and "scale" in msg
+    rc, msg = err(B.int8w_fp8_gemv(fp8desc(), x, x + 2 * 255, 0))
+    assert rc == B.INT8W_ERR_ALIAS and "input x" in msg

@@ -8,5 +8,5 @@ hand-written HIP kernels for gfx950, reached through the C-ABI library
 ``libint8w.so`` (declared in include/int8w.h); this package only marshals
 arguments.  There is no CPU fallback: calls fail when the library is missing.
 """
-from .binding import (Int8Weight, Int8wError, gemv_multi, library_path, load_library, moe_gemv,  # noqa: F401
-                      storage_bytes)
+from .binding import (Fp8Weight, Int8Weight, Int8wError, gemv_multi, library_path, load_library,  # noqa: F401
+                      moe_gemv, storage_bytes)

@@ -38,8 +38,9 @@ ERROR_NAMES = {
 EXPORTED = (
     "int8w_validate", "int8w_storage_bytes", "int8_dequantize_to", "int8_gemv", "int8_gemv_silu_gate",
     "int8_gemv_silu_gate_resid", "int8_gemm", "int8_gemv_multi", "int8_quantize", "int8_moe_gemv",
-    "int8w_last_error",
+    "int8w_fp8_gemv", "int8w_last_error",
 )
+FP8_PER_ROW, FP8_BLOCK_BF16, FP8_BLOCK_F32, FP8_SINGLE = 0, 1, 2, 3  # INT8W_FP8_*
 MAX_MULTI = 4  # INT8W_MAX_MULTI
 MAX_MOE_SLOTS = 65536  # INT8W_MAX_MOE_SLOTS
 
@@ -60,6 +61,19 @@ class WeightDesc(ctypes.Structure):
         ("out_features", ctypes.c_uint32),
         ("in_features", ctypes.c_uint32),
         ("group_size", ctypes.c_uint32),
+    ]
+
+
+class Fp8WeightDesc(ctypes.Structure):
+    """Mirror of ``int8w_fp8_weight`` (include/int8w.h)."""
+    _fields_ = [
+        ("weight", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+        ("n", ctypes.c_uint32),
+        ("k", ctypes.c_uint32),
+        ("scale_format", ctypes.c_uint32),
+        ("block_size", ctypes.c_uint32),
+        ("single_scale", ctypes.c_float),
     ]
 
 
@@ -103,6 +117,8 @@ def load_library() -> ctypes.CDLL:
     lib.int8_quantize.restype = ctypes.c_int
     lib.int8_moe_gemv.argtypes = [W, u32, P, u32, P, u32, u32, P, u64]
     lib.int8_moe_gemv.restype = ctypes.c_int
+    lib.int8w_fp8_gemv.argtypes = [ctypes.POINTER(Fp8WeightDesc), P, P, u64]
+    lib.int8w_fp8_gemv.restype = ctypes.c_int
     lib.int8w_last_error.argtypes = []
     lib.int8w_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -153,6 +169,10 @@ def int8_quantize(w: int, out_features: int, in_features: int, group_size: int, 
 def int8_moe_gemv(desc: WeightDesc, num_experts: int, x: int, x_rows: int, ids: int, tokens: int, topk: int,
                   y: int, stream: int) -> int:
     return load_library().int8_moe_gemv(ctypes.byref(desc), num_experts, x, x_rows, ids, tokens, topk, y, stream)
+
+
+def int8w_fp8_gemv(desc: Fp8WeightDesc, x: int, y: int, stream: int) -> int:
+    return load_library().int8w_fp8_gemv(ctypes.byref(desc), x, y, stream)
 
 
 def int8_gemv_multi(descs, x: int, ys, stream: int) -> int:
@@ -335,3 +355,47 @@ def moe_gemv(experts: Int8Weight, num_experts: int, x: torch.Tensor, ids: torch.
     _check(int8_moe_gemv(experts.desc, E, x.data_ptr(), x.shape[1], ids.data_ptr(), T, topk, y.data_ptr(),
                          _stream_of(dev)))
     return y
+
+
+class Fp8Weight:
+    """An FP8 E4M3 weight on the GPU (borrowed tensors), after the rustdoc page "Fp8Weight".
+
+    weight: uint8 [n, k] E4M3 bytes (k a multiple of 16)
+    scale:  float32 [n] (FP8_PER_ROW); bfloat16 or float32 [ceil(n/BS), ceil(k/BS)]
+            (FP8_BLOCK_BF16 / FP8_BLOCK_F32); None (FP8_SINGLE, with single_scale)
+    """
+
+    def __init__(self, weight: torch.Tensor, scale, scale_format: int, block_size: int = 128,
+                 single_scale: float = 1.0):
+        if weight.dim() != 2 or weight.dtype != torch.uint8 or not weight.is_contiguous():
+            raise ValueError("weight must be a contiguous 2-D uint8 tensor of E4M3 bytes")
+        if weight.device.type != "cuda":
+            raise ValueError("weight must be on a GPU")
+        n, k = weight.shape
+        fmt = int(scale_format)
+        if fmt == FP8_SINGLE:
+            if scale is not None:
+                raise ValueError("FP8_SINGLE takes no scale tensor")
+        else:
+            want = {FP8_PER_ROW: torch.float32, FP8_BLOCK_BF16: torch.bfloat16, FP8_BLOCK_F32: torch.float32}.get(fmt)
+            if want is None:
+                raise ValueError(f"unknown scale format {fmt}")
+            if scale is None or scale.dtype != want or scale.device != weight.device or not scale.is_contiguous():
+                raise ValueError(f"scale must be a contiguous {want} tensor on the weight's GPU")
+            bs = int(block_size)
+            shape = (n,) if fmt == FP8_PER_ROW else (-(-n // bs), -(-k // bs))
+            if tuple(scale.shape) != shape:
+                raise ValueError(f"scale must have shape {shape}")
+        self.weight, self.scale = weight, scale
+        self.n, self.k, self.scale_format = n, k, fmt
+        self.device = weight.device
+        self.desc = Fp8WeightDesc(weight.data_ptr(), scale.data_ptr() if scale is not None else None, n, k, fmt,
+                                  int(block_size), float(single_scale))
+
+    def gemv(self, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+        _need_bf16(x, "x", self.k, self.device)
+        if y is None:
+            y = torch.empty(self.n, dtype=torch.bfloat16, device=self.device)
+        _need_bf16(y, "y", self.n, self.device)
+        _check(int8w_fp8_gemv(self.desc, x.data_ptr(), y.data_ptr(), _stream_of(self.device)))
+        return y

@@ -26,7 +26,8 @@ COMMON = [
     "-Wall", "-Wno-unused-result", "-Wno-unknown-pragmas",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["dequant.hip", "quantize.hip", "gemv.hip", "gemm_smallm.hip", "gemm_prefill.hip", "capi.cpp"]
+SOURCES = ["dequant.hip", "quantize.hip", "gemv.hip", "fp8_gemv.hip", "gemm_smallm.hip", "gemm_prefill.hip",
+           "capi.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -247,6 +247,51 @@ int int8_moe_gemv(const int8w_weight *experts, uint32_t num_experts, const uint1
                        as_stream(stream));
 }
 
+int int8w_fp8_gemv(const int8w_fp8_weight *w, const uint16_t *x, uint16_t *y, uint64_t stream) {
+  if (!w) return fail(INT8W_ERR_NULL, "weight descriptor is NULL");
+  if (!w->weight) return fail(INT8W_ERR_NULL, "weight is NULL");
+  if (w->n == 0 || w->k == 0) return fail(INT8W_ERR_SHAPE, "zero dimension (n=%u k=%u)", w->n, w->k);
+  if (w->k % 16 != 0) return fail(INT8W_ERR_SHAPE, "k %u is not a multiple of 16", w->k);
+  if ((uint64_t)w->n * (w->k / 16u) > 0x7FFFFFFFull || w->k > (1u << 24))
+    return fail(INT8W_ERR_SHAPE, "weight too large (%u x %u codes)", w->n, w->k);
+  if (w->scale_format > INT8W_FP8_SINGLE)
+    return fail(INT8W_ERR_UNSUPPORTED, "unknown scale_format %u", w->scale_format);
+  const uint64_t n = w->n, k = w->k;
+  uint64_t scale_bytes = 0;
+  switch (w->scale_format) {
+    case INT8W_FP8_PER_ROW:
+      if (!w->scale) return fail(INT8W_ERR_NULL, "per-row scale is NULL");
+      if (!aligned(w->scale, 4)) return fail(INT8W_ERR_ALIGN, "per-row scale is not 4-byte aligned");
+      scale_bytes = n * 4;
+      break;
+    case INT8W_FP8_BLOCK_BF16:
+    case INT8W_FP8_BLOCK_F32: {
+      const uint32_t bs = w->block_size;
+      if (bs < 64 || bs > 1024 || (bs & (bs - 1)) != 0)
+        return fail(INT8W_ERR_UNSUPPORTED, "block_size %u is not a power of two in 64..1024", bs);
+      if (!w->scale) return fail(INT8W_ERR_NULL, "block scale is NULL");
+      const uint64_t el = w->scale_format == INT8W_FP8_BLOCK_BF16 ? 2 : 4;
+      if (!aligned(w->scale, el)) return fail(INT8W_ERR_ALIGN, "block scale is not %llu-byte aligned",
+                                              (unsigned long long)el);
+      scale_bytes = ((n + bs - 1) / bs) * ((k + bs - 1) / bs) * el;
+      break;
+    }
+    default:
+      if (w->scale) return fail(INT8W_ERR_SHAPE, "scale_format SINGLE takes no scale buffer (scale must be NULL)");
+  }
+  if (!x || !y) return fail(INT8W_ERR_NULL, "x or y is NULL");
+  if (!aligned(w->weight, 16)) return fail(INT8W_ERR_ALIGN, "weight is not 16-byte aligned");
+  if (!aligned(x, 16)) return fail(INT8W_ERR_ALIGN, "x is not 16-byte aligned");
+  if (!aligned(y, 2)) return fail(INT8W_ERR_ALIGN, "y is not 2-byte aligned");
+  Range ins[3] = {range("weight", w->weight, n * k), range("scale", w->scale, scale_bytes), range("x", x, k * 2)};
+  int rc = check_alias(range("y", y, n * 2), ins, 3);
+  if (rc) return rc;
+  (void)hipGetLastError();
+  return finish_launch(launch_fp8_gemv(w->weight, w->scale, (Fp8ScaleKind)w->scale_format, w->block_size,
+                                       w->single_scale, w->n, w->k, x, y, as_stream(stream)),
+                       as_stream(stream));
+}
+
 static int gemv_gated(const int8w_weight *w, const uint16_t *gate, const uint16_t *up, const uint16_t *x_resid,
                       uint16_t *y, uint64_t stream, bool with_resid) {
   int rc = validate(w);

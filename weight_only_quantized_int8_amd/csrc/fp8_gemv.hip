@@ -1,0 +1,362 @@
+// fp8_gemv.hip -- y = W x for an FP8 E4M3 weight on gfx950 (rustdoc page
+// "Fp8Weight": struct description, fields weight, row_scale, n, k and
+// scale_format):
+//   w[n,k] = E4M3(q[n,k]) * scale, the scale per row (f32 [N]), per block of
+//   BS x BS (BF16 or f32 [ceil(N/BS), ceil(K/BS)]) or one global value.
+//
+// HBM-bound: one byte per weight, the scales are a few KB.  The design is
+// the int8 gemv's:
+//  * Activation.  x is widened to fp32 once per workgroup and K-tile into LDS.
+//  * Codes.  A lane owns runs of 16 consecutive codes (one 16-byte load); a
+//    wave-wide load streams 1 KiB of a row.  Each wave streams a balanced,
+//    contiguous range of rows (RP side by side), through bounded buffer
+//    resources, two blocks of loads in flight; past its last row a wave
+//    re-reads its last item.
+//  * Arithmetic.  The hardware converts two E4M3 codes to two fp32 values
+//    per instruction (v_cvt_pk_f32_fp8, OCP E4M3 on gfx950: exact), then one
+//    FMA per code.  A run never straddles a scale block (BS >= 64), so the
+//    scale factors out of the run: a block scale multiplies each run's
+//    partial; a row or global scale multiplies the row's total once.
+//  * Reduction.  Fixed DPP order, K-tiles meet in LDS in tile order; no
+//    atomics.
+#include "common.h"
+#include "launch.h"
+
+namespace int8w {
+
+namespace {
+
+constexpr uint32_t kFp8TileRunsMax = 1024;  // 16384 activations per LDS tile
+constexpr int kFp8LoadsPerBlock = 4;        // 1 KiB wave loads per pipeline block
+constexpr uint32_t kFp8MaxRowsPerWave = 16;
+constexpr size_t kFp8LdsPerCu = 156 * 1024;
+constexpr uint32_t kFp8MinBlock = 64;  // smallest block size: 2 row blocks x 16384/64 k-blocks per tile
+constexpr int kSbkPerLane = (int)(2u * (kFp8TileRunsMax * 16u / kFp8MinBlock) / 64u);
+
+enum Fp8Scale { kSfRow = 0, kSfBlockBf16 = 1, kSfBlockF32 = 2 };
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// sum_i E4M3(q_i) a_i over one lane's 16 codes
+__device__ __forceinline__ float fp8_run_dot(const u32x4 &w, const float4 &a0, const float4 &a1, const float4 &a2,
+                                             const float4 &a3) {
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  const float av[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                        a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+  float p = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], false);  // bytes 0, 1
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], true);   // bytes 2, 3
+    p = __builtin_fmaf(lo.x, av[4 * i + 0], p);
+    p = __builtin_fmaf(lo.y, av[4 * i + 1], p);
+    p = __builtin_fmaf(hi.x, av[4 * i + 2], p);
+    p = __builtin_fmaf(hi.y, av[4 * i + 3], p);
+  }
+  return p;
+}
+
+// Sum over the 64 lanes in a fixed order; the total lands in lane 63.
+__device__ __forceinline__ float sum_lane63(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));
+  return v;
+}
+
+template <int U, int RP>
+struct Fp8Block {
+  u32x4 q[U][RP];
+};
+
+struct Fp8Cfg {
+  int waves;          // per workgroup (8 or 16)
+  int rp;             // rows side by side (1 or 2)
+  uint32_t blocks;
+  uint32_t ct;        // 16-code runs per LDS tile (multiple of 64)
+  uint32_t max_rows;  // most rows any wave owns
+  bool tail;          // k not a multiple of 1024
+};
+
+// k-blocks of one tile, and the LDS bytes of one workgroup:
+//   act  [NSEG][4][64] float4   activations of lane l's 16 codes in segment s
+//   sbk  [W][2][TB] float       each wave's block scales (two row blocks)
+//   part [W][max_rows] float    row partials across K-tiles
+__host__ __device__ inline uint32_t tile_blocks(uint32_t ct, uint32_t bs_log2) { return ((ct << 4) + (1u << bs_log2) - 1u) >> bs_log2; }
+size_t fp8_lds_bytes(const Fp8Cfg &c, bool block, uint32_t bs_log2) {
+  return (size_t)c.ct * 64u + (block ? (size_t)c.waves * 2u * tile_blocks(c.ct, bs_log2) * 4u : 0u) +
+         (size_t)c.waves * c.max_rows * 4u;
+}
+
+template <int SF, int W, int RP, int U, bool TAIL>
+__global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__ codes, const void *__restrict__ scale,
+                                                     float single, const uint16_t *__restrict__ xg, uint16_t *y,
+                                                     uint32_t N, uint32_t K, uint32_t bs_log2, uint32_t tile_runs,
+                                                     uint32_t max_rows) {
+  constexpr int kThreads = 64 * W;
+  constexpr int kStage = (int)(kFp8TileRunsMax + kThreads - 1) / kThreads;
+  constexpr bool kBlock = SF != kSfRow;
+  extern __shared__ float4 lds4[];
+  const uint32_t CT = tile_runs;
+  const uint32_t NSEG = CT >> 6;
+  const uint32_t TB = tile_blocks(CT, bs_log2);
+  float4 *act = lds4;
+  float *sbk_all = reinterpret_cast<float *>(lds4 + NSEG * 256);
+  float *part_all = sbk_all + (kBlock ? W * 2u * TB : 0u);
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave = uni(tid >> 6);
+  const uint32_t lw = blockIdx.x * W + wave;
+  const uint32_t TW = gridDim.x * W;
+  const uint32_t rq = N / TW, rr = N % TW;
+  const uint32_t rbeg = lw * rq + (lw < rr ? lw : rr);
+  const uint32_t nr = rq + (lw < rr ? 1u : 0u);
+  const uint32_t ngrp = (nr + RP - 1) / RP;
+  const uint32_t cpr = K >> 4;
+  const uint32_t KB = (K + (1u << bs_log2) - 1u) >> bs_log2;  // scale blocks along k
+  const uint32_t NB = (N + (1u << bs_log2) - 1u) >> bs_log2;  // and along n
+  const uint32_t rb0 = rbeg >> bs_log2;
+
+  const auto rw = make_rsrc(codes + (size_t)rbeg * K, nr * K);
+  const auto rx = make_rsrc(xg, K * 2u);
+  float *sbk = sbk_all + wave * 2u * TB;
+  float *part = part_all + wave * max_rows;
+
+  const uint32_t vo_w = lane << 4;
+  const uint32_t v_act = lane << 4;
+  const uint32_t v_kb = kBlock ? (((lane << 4) >> bs_log2) << 2) : 0u;  // this lane's k-block in a segment, bytes
+
+  float acc[RP];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) acc[r] = 0.f;
+  Fp8Block<U, RP> A, B;
+
+  for (uint32_t t0 = 0; t0 < cpr; t0 += CT) {
+    const uint32_t ct = (cpr - t0) < CT ? (cpr - t0) : CT;
+    const bool last_tile = t0 + ct == cpr;
+    const uint32_t nseg = (ct + 63u) >> 6;
+    const uint32_t nitems = ngrp * nseg;
+    const uint32_t nblk = (nitems + U - 1) / U;
+    const uint32_t last_lanes = ct - ((nseg - 1u) << 6);
+    const uint32_t vo_w_last = TAIL && lane >= last_lanes ? kOutOfRange : vo_w;
+    // lanes past the end of the last segment read a staged (finite) scale
+    const uint32_t v_kb_last = TAIL && lane >= last_lanes ? 0u : v_kb;
+    const uint32_t grp_skip = RP * K - (nseg << 10);
+    const uint32_t last_off = (nr ? nr - 1u : 0u) * K + (t0 << 4) + ((nseg - 1u) << 10);
+    const uint32_t kb0 = (t0 << 4) >> bs_log2;
+    const uint32_t seg_kb = kBlock ? (1024u >> bs_log2) : 0u;  // k-blocks per segment
+
+    uint32_t i_off = t0 << 4, i_seg = 0, i_grp = 0;
+    auto issue = [&](Fp8Block<U, RP> &blk) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        uint32_t vw = vo_w;
+        if constexpr (TAIL) vw = (i_seg == nseg - 1u) ? vo_w_last : vo_w;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          const bool live = i_grp < ngrp && i_grp * RP + r < nr;
+          const uint32_t sw = uni(live ? i_off + r * K : last_off);
+          const uint32_t vwr = live ? vw : vo_w_last;
+          blk.q[u][r] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vwr, (int)sw, kAuxNontemporal);
+        }
+        i_off += 1024u;
+        if (++i_seg == nseg) { i_seg = 0; ++i_grp; i_off += grp_skip; }
+      }
+    };
+    uint32_t c_grp = 0, c_seg = 0;
+    auto consume = [&](const Fp8Block<U, RP> &blk) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (c_grp < ngrp) {
+          const float4 *ap = reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(act) +
+                                                              uni(c_seg << 12) + v_act);
+          const float4 a0 = ap[0], a1 = ap[64], a2 = ap[128], a3 = ap[192];
+          uint32_t vk = v_kb;
+          if constexpr (TAIL) vk = (c_seg == nseg - 1u) ? v_kb_last : v_kb;
+#pragma unroll
+          for (int r = 0; r < RP; ++r) {
+            const float p = fp8_run_dot(blk.q[u][r], a0, a1, a2, a3);
+            if constexpr (kBlock) {
+              const uint32_t row = c_grp * RP + r;
+              const uint32_t rs = row < nr ? row : 0u;
+              const uint32_t rbi = ((rbeg + rs) >> bs_log2) - rb0;
+              const float s = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(sbk) +
+                                                               uni((rbi * TB + c_seg * seg_kb) << 2) + vk);
+              acc[r] = __builtin_fmaf(s, p, acc[r]);
+            } else {
+              acc[r] += p;
+            }
+          }
+          if (c_seg == nseg - 1u) {
+#pragma unroll
+            for (int r = 0; r < RP; ++r) {
+              const uint32_t row = c_grp * RP + r;
+              if (row < nr) {
+                const float tot = sum_lane63(acc[r]);
+                if (lane == 63u) {
+                  float v = t0 ? part[row] + tot : tot;
+                  if (last_tile) {
+                    if constexpr (!kBlock) v *= scale ? reinterpret_cast<const float *>(scale)[rbeg + row] : single;
+                    y[rbeg + row] = to_bf16_bits(v);
+                  } else {
+                    part[row] = v;
+                  }
+                }
+              }
+              acc[r] = 0.f;
+            }
+          }
+        }
+        if (++c_seg == nseg) { c_seg = 0; ++c_grp; }
+      }
+    };
+
+    // 1. activation loads, the first weight block and the tile's block scales
+    u32x4 xv[kStage][2];
+#pragma unroll
+    for (int s = 0; s < kStage; ++s) {
+      const uint32_t e = tid + s * kThreads;
+      const uint32_t off = e < ct ? (t0 + e) * 32u : kOutOfRange;
+      xv[s][0] = buf_load_b128(rx, off);
+      xv[s][1] = buf_load_b128(rx, off + 16u);
+    }
+    if (nblk) issue(A);
+    if (t0) __syncthreads();  // everyone is done with the previous tile
+    // 2. the activation tile; runs past the end are zeros
+#pragma unroll
+    for (int s = 0; s < kStage; ++s) {
+      const uint32_t e = tid + s * kThreads;
+      if (e < (nseg << 6)) {
+        const uint32_t wv[8] = {xv[s][0].x, xv[s][0].y, xv[s][0].z, xv[s][0].w,
+                                xv[s][1].x, xv[s][1].y, xv[s][1].z, xv[s][1].w};
+        float4 *dst = act + (e >> 6) * 256u + (e & 63u);
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          dst[f * 64] = make_float4(bf16_lo(wv[2 * f]), bf16_hi(wv[2 * f]), bf16_lo(wv[2 * f + 1]),
+                                    bf16_hi(wv[2 * f + 1]));
+      }
+    }
+    if constexpr (kBlock) {
+      // this wave's scales: row blocks rb0 and rb0 + 1 (a wave owns at most
+      // 16 <= BS rows), k-blocks kb0 .. kb0 + TB - 1; missing ones are 0.
+      // All loads first, then the stores.
+      float sv[kSbkPerLane];
+#pragma unroll
+      for (int j = 0; j < kSbkPerLane; ++j) {
+        const uint32_t e = lane + 64u * j;
+        const uint32_t rbi = e >= TB ? 1u : 0u;
+        const uint32_t rb = rb0 + rbi, kb = kb0 + e - rbi * TB;
+        sv[j] = 0.f;
+        if (e < 2u * TB && rb < NB && kb < KB) {
+          const size_t idx = (size_t)rb * KB + kb;
+          sv[j] = SF == kSfBlockBf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(scale)[idx])
+                                     : reinterpret_cast<const float *>(scale)[idx];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kSbkPerLane; ++j) {
+        const uint32_t e = lane + 64u * j;
+        if (e < 2u * TB) sbk[e] = sv[j];
+      }
+    }
+    __syncthreads();
+    // 3. two-stage pipeline; the only branches are the loop exits
+    for (uint32_t b = 0; b < nblk;) {
+      if (b + 1 >= nblk) { consume(A); break; }
+      issue(B);
+      consume(A);
+      ++b;
+      if (b + 1 >= nblk) { consume(B); break; }
+      issue(A);
+      consume(B);
+      ++b;
+    }
+  }
+}
+
+template <typename Kern>
+hipError_t lds_cap(Kern kern, bool &configured) {
+  if (configured) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) configured = true;
+  return e;
+}
+
+template <int SF, int W, int RP, bool TAIL>
+hipError_t launch_fp8_cfg(const Fp8Cfg &c, const uint8_t *codes, const void *scale, float single, uint32_t bs_log2,
+                          const uint16_t *x, uint16_t *y, uint32_t N, uint32_t K, hipStream_t stream) {
+  static bool configured = false;
+  auto kern = k_fp8_gemv<SF, W, RP, kFp8LoadsPerBlock / RP, TAIL>;
+  hipError_t e = lds_cap(kern, configured);
+  if (e != hipSuccess) return e;
+  const size_t lds = fp8_lds_bytes(c, SF != kSfRow, bs_log2);
+  hipLaunchKernelGGL(kern, dim3(c.blocks), dim3(64 * W), lds, stream, codes, scale, single, x, y, N, K, bs_log2,
+                     c.ct, c.max_rows);
+  return hipGetLastError();
+}
+
+template <int SF>
+hipError_t launch_fp8_sf(const Fp8Cfg &c, const uint8_t *codes, const void *scale, float single, uint32_t bs_log2,
+                         const uint16_t *x, uint16_t *y, uint32_t N, uint32_t K, hipStream_t stream) {
+  if (c.waves == 16) {
+    if (c.rp == 2)
+      return c.tail ? launch_fp8_cfg<SF, 16, 2, true>(c, codes, scale, single, bs_log2, x, y, N, K, stream)
+                    : launch_fp8_cfg<SF, 16, 2, false>(c, codes, scale, single, bs_log2, x, y, N, K, stream);
+    return c.tail ? launch_fp8_cfg<SF, 16, 1, true>(c, codes, scale, single, bs_log2, x, y, N, K, stream)
+                  : launch_fp8_cfg<SF, 16, 1, false>(c, codes, scale, single, bs_log2, x, y, N, K, stream);
+  }
+  return c.tail ? launch_fp8_cfg<SF, 8, 1, true>(c, codes, scale, single, bs_log2, x, y, N, K, stream)
+                : launch_fp8_cfg<SF, 8, 1, false>(c, codes, scale, single, bs_log2, x, y, N, K, stream);
+}
+
+// Launch shape, as for the int8 gemv: short rows (K <= 8192) two 8-wave
+// workgroups per CU, long rows one 16-wave workgroup per CU with two rows
+// side by side when every wave owns at least two.
+Fp8Cfg choose_fp8_cfg(uint32_t N, uint32_t K, bool block, uint32_t bs_log2) {
+  const uint32_t cus = (uint32_t)device_cu_count();
+  Fp8Cfg c{};
+  c.waves = K <= 8192u ? 8 : 16;
+  const uint32_t per_cu = c.waves == 8 ? 2u : 1u;
+  const uint32_t W = (uint32_t)c.waves;
+  c.blocks = per_cu * cus;
+  const uint32_t need = (N + W - 1) / W;
+  const uint32_t enough = (N + W * kFp8MaxRowsPerWave - 1) / (W * kFp8MaxRowsPerWave);
+  if (c.blocks > need) c.blocks = need;
+  if (c.blocks < enough) c.blocks = enough;
+  const uint32_t tw = c.blocks * W;
+  c.max_rows = (N + tw - 1) / tw;
+  c.rp = c.waves == 16 && N / tw >= 2u ? 2 : 1;
+  const uint32_t cpr = K / 16u;
+  const size_t budget = kFp8LdsPerCu / per_cu;
+  for (uint32_t ntiles = (cpr + kFp8TileRunsMax - 1) / kFp8TileRunsMax;; ++ntiles) {
+    c.ct = ((cpr + ntiles - 1) / ntiles + 63u) / 64u * 64u;
+    if (fp8_lds_bytes(c, block, bs_log2) <= budget || c.ct == 64u) break;
+  }
+  c.tail = (cpr % 64u) != 0;
+  return c;
+}
+
+}  // namespace
+
+hipError_t launch_fp8_gemv(const uint8_t *codes, const void *scale, Fp8ScaleKind kind, uint32_t block_size,
+                           float single, uint32_t N, uint32_t K, const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  const bool block = kind == kFp8BlockBf16 || kind == kFp8BlockF32;
+  const uint32_t bs_log2 = block ? (uint32_t)__builtin_ctz(block_size) : 10u;
+  const Fp8Cfg c = choose_fp8_cfg(N, K, block, bs_log2);
+  switch (kind) {
+    case kFp8BlockBf16: return launch_fp8_sf<kSfBlockBf16>(c, codes, scale, single, bs_log2, x, y, N, K, stream);
+    case kFp8BlockF32: return launch_fp8_sf<kSfBlockF32>(c, codes, scale, single, bs_log2, x, y, N, K, stream);
+    default:  // per-row (scale [N]) or one global value (scale NULL)
+      return launch_fp8_sf<kSfRow>(c, codes, kind == kFp8PerRow ? scale : nullptr, single, bs_log2, x, y, N, K,
+                                   stream);
+  }
+}
+
+}  // namespace int8w

@@ -38,6 +38,13 @@ hipError_t launch_gemv_multi(const WeightView *w, uint16_t *const *y, uint32_t c
 hipError_t launch_moe_gemv(const WeightView &w, uint32_t E, const uint16_t *x, uint32_t x_rows, const uint32_t *ids,
                            uint32_t tokens, uint32_t topk, uint16_t *y, hipStream_t stream);
 
+// y = W x for an FP8 E4M3 weight [N, K] (bytes, K a multiple of 16) with a
+// per-row f32 scale [N], per-block BF16 or f32 scales [ceil(N/BS),
+// ceil(K/BS)] (BS a power of two, 64..1024) or one global scale.
+enum Fp8ScaleKind { kFp8PerRow = 0, kFp8BlockBf16 = 1, kFp8BlockF32 = 2, kFp8Single = 3 };
+hipError_t launch_fp8_gemv(const uint8_t *codes, const void *scale, Fp8ScaleKind kind, uint32_t block_size,
+                           float single, uint32_t N, uint32_t K, const uint16_t *x, uint16_t *y, hipStream_t stream);
+
 // BF16 weight [N, K] -> codes (packed), scales, biases [N, K/gs] (affine min/max).
 hipError_t launch_quantize(const uint16_t *w, uint32_t N, uint32_t K, uint32_t gs, uint32_t *packed, uint16_t *scales,
                            uint16_t *biases, hipStream_t stream);

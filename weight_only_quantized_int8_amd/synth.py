@@ -14,6 +14,11 @@ Value distributions (the decode/prefill workloads of these layers):
   dense BF16 weights (the quantizer's input): BF16 of fp32 N(0, 0.02^2), with
   one row in 64 scaled by 8 (outlier rows) and one value in 512 by 16
   (outlier values).
+  FP8 E4M3 weights: E4M3 (torch's float8_e4m3fn conversion) of fp32
+  N(0, 96^2) clipped to +-448, so that the codes span the format's range;
+  per-row scales f32 uniform[1e-4, 4e-4]; block scales the same, as BF16 or
+  f32.
+  routing ids: each token names topk distinct experts, uniformly.
 Generator: NumPy PCG64, seed = 1000 * workload_index + shape_index, draws in
 the fixed order codes, scales, bias jitter, then activations.
 """
@@ -93,3 +98,15 @@ def gen_ids(rng: np.random.Generator, tokens: int, topk: int, num_experts: int) 
     for t in range(tokens):
         out[t] = rng.permutation(num_experts)[:topk]
     return out
+
+
+def gen_fp8_codes(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """E4M3 bytes [N, K]: fp32 N(0, 96^2) clipped to +-448, converted by torch."""
+    v = np.clip(rng.standard_normal((N, K)).astype(np.float32) * np.float32(96.0), -448.0, 448.0)
+    return torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def gen_fp8_scale(rng: np.random.Generator, shape, bf16: bool) -> np.ndarray:
+    """Scales f32 uniform[1e-4, 4e-4]: float32, or BF16 bit patterns."""
+    s = rng.uniform(1e-4, 4e-4, size=shape).astype(np.float32)
+    return to_bf16_bits(s) if bf16 else s
