@@ -94,3 +94,23 @@ def test_quantize_writes_only_its_outputs():
     torch.cuda.synchronize()
     assert (packed[N * K // 4:].cpu() == -7).all()
     assert (scales[N * G:].float().cpu() == 3.0).all() and (biases[N * G:].float().cpu() == 5.0).all()
+
+
+def test_quantize_exact_ties_take_the_division_path():
+    # every value after the first two of each group is exactly halfway between
+    # two codes (scale 1/16): the kernel's reciprocal shortcut must defer to
+    # the IEEE division and round to even, like the oracle
+    log("quantize exact ties")
+    k = np.arange(62)
+    grp = np.concatenate([[0.0, 255 / 16], (2 * k + 1) / 32.0]).astype(np.float32)
+    rng = np.random.Generator(np.random.PCG64(70_300))
+    N, K, gs = 64, 1024, 64
+    w = synth.gen_dense_weight(rng, N, K)
+    tie_bits = oracle.f32_to_bf16(grp)
+    for n in range(0, N, 3):
+        for g in range(n % 4, K // gs, 4):
+            w[n, g * gs:(g + 1) * gs] = rng.permutation(tie_bits)
+    p_ref, s_ref, b_ref = oracle.quantize(w, gs)
+    p, s, b, _ = gpu_quantize(w, gs)
+    assert np.array_equal(s, s_ref) and np.array_equal(b, b_ref)
+    assert np.array_equal(p, p_ref)

@@ -729,3 +729,17 @@ def test_fp8_nan_code_makes_its_row_nan():
     x = synth.gen_act(np.random.Generator(np.random.PCG64(724)), 64)
     y, _ = oracle.fp8_gemv(w, np.ones(3, np.float32), oracle.FP8_PER_ROW, x)
     assert np.isnan(y[1]) and np.isfinite(y[[0, 2]]).all()
+
+
+def test_quantize_ties_round_to_even():
+    # lo = 0, hi = 255/16 gives scale exactly 1/16; the values (2k+1)/32 then
+    # sit exactly halfway between codes k and k+1 and take the even one
+    k = np.arange(62)
+    vals = np.concatenate([[0.0, 255 / 16], (2 * k + 1) / 32.0]).astype(np.float32)
+    bits = oracle.f32_to_bf16(vals)
+    assert np.array_equal(oracle.bf16_to_f32(bits), vals)  # all exact in BF16
+    packed, s, b = oracle.quantize(bits.reshape(1, 64), 64)
+    assert s[0, 0] == 0x3D80 and b[0, 0] == 0  # 1/16 and +0
+    codes = _codes_of(packed)[0].astype(np.int64)
+    assert codes[0] == 0 and codes[1] == 255
+    assert np.array_equal(codes[2:], np.where(k % 2 == 0, k, k + 1))
