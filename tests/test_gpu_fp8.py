@@ -51,7 +51,9 @@ def upload(codes, scale, fmt, bs, single=2.5e-4):
     (300, 1040, 64),       # ragged k (tail segment), n not a multiple of the block
     (77, 4112, 256),
     (5, 36864, 1024),      # several K-tiles
-    (1000, 3072, 128),
+    (1000, 3072, 128),     # register-resident form, three segments
+    (600, 2048, 64),       # two segments, several row blocks per wave
+    (65, 1024, 128),       # one segment, ragged rows
 ])
 def test_fp8_gemv_matches_oracle(fmt, N, K, bs):
     log(f"fp8_gemv {fmt} N={N} K={K} bs={bs}")

@@ -19,6 +19,10 @@
 //    partial; a row or global scale multiplies the row's total once.
 //  * Reduction.  Fixed DPP order, K-tiles meet in LDS in tile order; no
 //    atomics.
+//  * Short rows (k = 1024..4096, a multiple of 1024): a lane's activations
+//    (16 per 1 KiB segment) stay in its registers and a block scale is loaded
+//    with the codes, so a wave needs no LDS, no barrier and no staging before
+//    its first block (one block = one row, two rows in flight).
 #include "common.h"
 #include "launch.h"
 
@@ -280,6 +284,129 @@ __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__
   }
 }
 
+// The register-resident form for k = NS * 1024.  Same row partition,
+// decode, scale placement and reduction as k_fp8_gemv.
+template <int SF, int NS>
+__global__ __launch_bounds__(512) void k_fp8_gemv_rx(const uint8_t *__restrict__ codes,
+                                                     const void *__restrict__ scale, float single,
+                                                     const uint16_t *__restrict__ xg, uint16_t *y, uint32_t N,
+                                                     uint32_t bs_log2) {
+  constexpr uint32_t K = NS * 1024u;
+  constexpr bool kBlock = SF != kSfRow;
+  constexpr uint32_t kEl = SF == kSfBlockBf16 ? 2u : 4u;  // block scale entry bytes
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t lw = blockIdx.x * 8u + uni(threadIdx.x >> 6);
+  const uint32_t TW = gridDim.x * 8u;
+  const uint32_t rq = N / TW, rr = N % TW;
+  const uint32_t rbeg = lw * rq + (lw < rr ? lw : rr);
+  const uint32_t nr = rq + (lw < rr ? 1u : 0u);
+  const uint32_t KB = (K + (1u << bs_log2) - 1u) >> bs_log2;
+  const uint32_t NB = (N + (1u << bs_log2) - 1u) >> bs_log2;
+  const auto rw = make_rsrc(codes + (size_t)rbeg * K, nr * K);
+  const auto rx = make_rsrc(xg, K * 2u);
+  const auto rs = make_rsrc(scale, kBlock ? NB * KB * kEl : 0u);
+  const uint32_t vo_w = lane << 4;
+  const uint32_t v_kb = kBlock ? ((lane << 4) >> bs_log2) * kEl : 0u;  // the lane's k-block in a segment, bytes
+
+  struct RowBlock {
+    u32x4 q[NS];
+    uint32_t s[kBlock ? NS : 1];  // block scale bits of each segment's run
+  };
+  u32x4 xw[NS][2];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    xw[u][0] = buf_load_b128(rx, (u << 11) + (lane << 5));
+    xw[u][1] = buf_load_b128(rx, (u << 11) + (lane << 5) + 16u);
+  }
+  uint32_t i_row = 0;
+  auto issue = [&](RowBlock &blk) {
+    // past the wave's rows a block re-reads its last row
+    const uint32_t row = i_row < nr ? i_row : (nr ? nr - 1u : 0u);
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      blk.q[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vo_w, (int)uni(row * K + (u << 10)), kAuxNontemporal);
+      if constexpr (kBlock) {
+        const uint32_t so = uni((((rbeg + row) >> bs_log2) * KB + (((uint32_t)u << 10) >> bs_log2)) * kEl);
+        if constexpr (SF == kSfBlockBf16)
+          blk.s[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)v_kb, (int)so, 0);
+        else
+          blk.s[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)v_kb, (int)so, 0);
+      }
+    }
+    ++i_row;
+  };
+  RowBlock A, B;
+  issue(A);
+  float a[NS][16];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const uint32_t wv[8] = {xw[u][0].x, xw[u][0].y, xw[u][0].z, xw[u][0].w,
+                            xw[u][1].x, xw[u][1].y, xw[u][1].z, xw[u][1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[u][2 * i] = bf16_lo(wv[i]);
+      a[u][2 * i + 1] = bf16_hi(wv[i]);
+    }
+  }
+  uint32_t c_row = 0;
+  auto consume = [&](const RowBlock &blk) {
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const float p = fp8_run_dot(blk.q[u], make_float4(a[u][0], a[u][1], a[u][2], a[u][3]),
+                                  make_float4(a[u][4], a[u][5], a[u][6], a[u][7]),
+                                  make_float4(a[u][8], a[u][9], a[u][10], a[u][11]),
+                                  make_float4(a[u][12], a[u][13], a[u][14], a[u][15]));
+      if constexpr (kBlock) {
+        const float sc = SF == kSfBlockBf16 ? bf16_bits_to_f32((uint16_t)blk.s[u]) : __uint_as_float(blk.s[u]);
+        acc = __builtin_fmaf(sc, p, acc);
+      } else {
+        acc += p;
+      }
+    }
+    const float tot = sum_lane63(acc);
+    if (lane == 63u) {
+      float v = tot;
+      if constexpr (!kBlock) v *= scale ? reinterpret_cast<const float *>(scale)[rbeg + c_row] : single;
+      y[rbeg + c_row] = to_bf16_bits(v);
+    }
+    ++c_row;
+  };
+  for (uint32_t b = 0; b < nr;) {
+    if (b + 1 >= nr) { consume(A); break; }
+    issue(B);
+    consume(A);
+    ++b;
+    if (b + 1 >= nr) { consume(B); break; }
+    issue(A);
+    consume(B);
+    ++b;
+  }
+}
+
+template <int SF>
+hipError_t launch_fp8_rx(const Fp8Cfg &c, const uint8_t *codes, const void *scale, float single, uint32_t bs_log2,
+                         const uint16_t *x, uint16_t *y, uint32_t N, uint32_t K, hipStream_t stream) {
+  switch (K / 1024u) {
+    case 1:
+      hipLaunchKernelGGL((k_fp8_gemv_rx<SF, 1>), dim3(c.blocks), dim3(512), 0, stream, codes, scale, single, x, y, N,
+                         bs_log2);
+      break;
+    case 2:
+      hipLaunchKernelGGL((k_fp8_gemv_rx<SF, 2>), dim3(c.blocks), dim3(512), 0, stream, codes, scale, single, x, y, N,
+                         bs_log2);
+      break;
+    case 3:
+      hipLaunchKernelGGL((k_fp8_gemv_rx<SF, 3>), dim3(c.blocks), dim3(512), 0, stream, codes, scale, single, x, y, N,
+                         bs_log2);
+      break;
+    default:
+      hipLaunchKernelGGL((k_fp8_gemv_rx<SF, 4>), dim3(c.blocks), dim3(512), 0, stream, codes, scale, single, x, y, N,
+                         bs_log2);
+  }
+  return hipGetLastError();
+}
+
 template <typename Kern>
 hipError_t lds_cap(Kern kern, bool &configured) {
   if (configured) return hipSuccess;
@@ -305,6 +432,8 @@ hipError_t launch_fp8_cfg(const Fp8Cfg &c, const uint8_t *codes, const void *sca
 template <int SF>
 hipError_t launch_fp8_sf(const Fp8Cfg &c, const uint8_t *codes, const void *scale, float single, uint32_t bs_log2,
                          const uint16_t *x, uint16_t *y, uint32_t N, uint32_t K, hipStream_t stream) {
+  if (c.waves == 8 && c.rp == 1 && K % 1024u == 0 && K >= 1024u && K <= 4096u)
+    return launch_fp8_rx<SF>(c, codes, scale, single, bs_log2, x, y, N, K, stream);
   if (c.waves == 16) {
     if (c.rp == 2)
       return c.tail ? launch_fp8_cfg<SF, 16, 2, true>(c, codes, scale, single, bs_log2, x, y, N, K, stream)
