@@ -445,14 +445,15 @@ hipError_t launch_fp8_sf(const Fp8Cfg &c, const uint8_t *codes, const void *scal
                 : launch_fp8_cfg<SF, 8, 1, false>(c, codes, scale, single, bs_log2, x, y, N, K, stream);
 }
 
-// Launch shape, as for the int8 gemv: short rows (K <= 8192) two 8-wave
-// workgroups per CU, long rows one 16-wave workgroup per CU with two rows
-// side by side when every wave owns at least two.
+// Launch shape, as for the int8 gemv: short rows (K <= 8192) 8-wave
+// workgroups, two per CU above 16384 rows and one per CU below; long rows
+// one 16-wave workgroup per CU with two rows side by side when every wave
+// owns at least two.
 Fp8Cfg choose_fp8_cfg(uint32_t N, uint32_t K, bool block, uint32_t bs_log2) {
   const uint32_t cus = (uint32_t)device_cu_count();
   Fp8Cfg c{};
   c.waves = K <= 8192u ? 8 : 16;
-  const uint32_t per_cu = c.waves == 8 ? 2u : 1u;
+  const uint32_t per_cu = c.waves == 8 && N > 16384u ? 2u : 1u;
   const uint32_t W = (uint32_t)c.waves;
   c.blocks = per_cu * cus;
   const uint32_t need = (N + W - 1) / W;

@@ -626,10 +626,12 @@ uint32_t deal_waves(uint32_t tw, const uint32_t *n, uint32_t count, uint32_t *wa
   return max_rows;
 }
 
-// Launch shape (measured on MI355X): short rows (K <= 8192) run two 8-wave
-// workgroups per CU; long rows one 16-wave workgroup per CU, so one
-// activation tile serves 16 waves, with two rows side by side when every
-// wave owns at least two.
+// Launch shape (measured on MI355X): short rows (K <= 8192) run 8-wave
+// workgroups, two per CU when the launch has more than 16384 rows and one
+// per CU otherwise (a small launch is latency-bound: fewer waves with two
+// rows each beat more waves with one); long rows one 16-wave workgroup per
+// CU, so one activation tile serves 16 waves, with two rows side by side
+// when every wave owns at least two.
 GemvCfg choose_cfg(const uint32_t *n, uint32_t count, uint32_t K, uint32_t gs, uint32_t *wave_end, int waves = 0,
                    int rp = 0, uint32_t wg_per_cu = 0) {
   const uint32_t cus = (uint32_t)device_cu_count();
@@ -637,7 +639,7 @@ GemvCfg choose_cfg(const uint32_t *n, uint32_t count, uint32_t K, uint32_t gs, u
   for (uint32_t i = 0; i < count; ++i) N += n[i];
   GemvCfg c{};
   c.waves = waves ? waves : (K <= 8192u ? 8 : 16);
-  const uint32_t per_cu = wg_per_cu ? wg_per_cu : (c.waves == 8 ? 2u : 1u);
+  const uint32_t per_cu = wg_per_cu ? wg_per_cu : (c.waves == 8 && N > 16384u ? 2u : 1u);
   const uint32_t W = (uint32_t)c.waves;
   c.blocks = per_cu * cus;
   const uint32_t need = (N + W - 1) / W;
@@ -731,7 +733,7 @@ GemvCfg choose_moe_cfg(uint32_t N, uint32_t K, uint32_t gs, uint32_t slots) {
   const uint32_t cus = (uint32_t)device_cu_count();
   GemvCfg c{};
   c.waves = K <= 8192u ? 8 : 16;
-  const uint32_t per_cu = c.waves == 8 ? 2u : 1u;
+  const uint32_t per_cu = c.waves == 8 && (uint64_t)N * slots > 16384u ? 2u : 1u;  // as choose_cfg
   const uint32_t W = (uint32_t)c.waves;
   uint32_t per_slot = (per_cu * cus + slots - 1) / slots;
   const uint32_t most = (N + W - 1) / W;                                  // no more waves than rows
