@@ -11,7 +11,9 @@
 //    wave-wide load streams 1 KiB of a row.  Each wave streams a balanced,
 //    contiguous range of rows (RP side by side), through bounded buffer
 //    resources, two blocks of loads in flight; past its last row a wave
-//    re-reads its last item.
+//    re-reads its last item.  The first block goes out after the activation
+//    and scale loads (vmcnt counts in order: waiting for those never waits
+//    for it).
 //  * Arithmetic.  The hardware converts two E4M3 codes to two fp32 values
 //    per instruction (v_cvt_pk_f32_fp8, OCP E4M3 on gfx950: exact), then one
 //    FMA per code.  A run never straddles a scale block (BS >= 64), so the
@@ -230,7 +232,26 @@ __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__
       xv[s][0] = buf_load_b128(rx, off);
       xv[s][1] = buf_load_b128(rx, off + 16u);
     }
-    if (nblk) issue(A);
+    // this wave's block scales: row blocks rb0 and rb0 + 1 (a wave owns at
+    // most 16 <= BS rows), k-blocks kb0 .. kb0 + TB - 1; missing ones are 0
+    float sv[kBlock ? kSbkPerLane : 1];
+    if constexpr (kBlock) {
+#pragma unroll
+      for (int j = 0; j < kSbkPerLane; ++j) {
+        const uint32_t e = lane + 64u * j;
+        const uint32_t rbi = e >= TB ? 1u : 0u;
+        const uint32_t rb = rb0 + rbi, kb = kb0 + e - rbi * TB;
+        sv[j] = 0.f;
+        if (e < 2u * TB && rb < NB && kb < KB) {
+          const size_t idx = (size_t)rb * KB + kb;
+          sv[j] = SF == kSfBlockBf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(scale)[idx])
+                                     : reinterpret_cast<const float *>(scale)[idx];
+        }
+      }
+    }
+    // the first weight block goes out after the small loads and
+    // unconditionally, so that waiting for them never waits for it
+    issue(A);
     if (t0) __syncthreads();  // everyone is done with the previous tile
     // 2. the activation tile; runs past the end are zeros
 #pragma unroll
@@ -247,22 +268,6 @@ __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__
       }
     }
     if constexpr (kBlock) {
-      // this wave's scales: row blocks rb0 and rb0 + 1 (a wave owns at most
-      // 16 <= BS rows), k-blocks kb0 .. kb0 + TB - 1; missing ones are 0.
-      // All loads first, then the stores.
-      float sv[kSbkPerLane];
-#pragma unroll
-      for (int j = 0; j < kSbkPerLane; ++j) {
-        const uint32_t e = lane + 64u * j;
-        const uint32_t rbi = e >= TB ? 1u : 0u;
-        const uint32_t rb = rb0 + rbi, kb = kb0 + e - rbi * TB;
-        sv[j] = 0.f;
-        if (e < 2u * TB && rb < NB && kb < KB) {
-          const size_t idx = (size_t)rb * KB + kb;
-          sv[j] = SF == kSfBlockBf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(scale)[idx])
-                                     : reinterpret_cast<const float *>(scale)[idx];
-        }
-      }
 #pragma unroll
       for (int j = 0; j < kSbkPerLane; ++j) {
         const uint32_t e = lane + 64u * j;

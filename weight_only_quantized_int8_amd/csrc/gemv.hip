@@ -26,7 +26,8 @@
 //    FMA.  (scale, bias - 1024 scale) pairs are staged per wave in LDS as fp32.
 //  * Pipeline.  Loads run two blocks of U items ahead (the next block is
 //    issued before the current one is consumed); the first block goes out
-//    before the activation staging, so staging hides under its latency.
+//    right after the activation and scale/bias loads, so the staging hides
+//    under its latency without waiting for it.
 //  * Reduction.  A row's lane partials are summed with a fixed DPP sequence as
 //    soon as its last segment is consumed; with several K-tiles the partials
 //    meet in LDS in tile order.  No atomics: results are deterministic.
@@ -50,7 +51,7 @@ constexpr uint32_t kTileRunsMax = 1024;    // 16384 activations per LDS tile
 constexpr int kLoadsPerBlock = 4;          // 1 KiB wave loads per pipeline block (U items x RP rows)
 constexpr uint32_t kMaxRowsPerWave = 16;   // rows a wave may own
 constexpr size_t kLdsPerCu = 156 * 1024;   // dynamic LDS budget of one CU
-constexpr int kSbPerLane = 4;              // scale/bias entries a lane prefetches per tile
+constexpr int kSbPerLane = 8;              // scale/bias entries a lane prefetches per tile
 
 struct GemvCfg {
   int waves;           // waves per workgroup (8 or 16)
@@ -278,7 +279,6 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
         uv[s][1] = buf_load_b128(ru, off + 16u);
       }
     }
-    if (nblk) issue(A);
     const uint32_t nsb = nr * tg;
     const uint32_t tg_inv = (uint32_t)(0xFFFFFFFFu / tg) + 1u;  // e / tg == umulhi(e, tg_inv) for e < 2^16
     uint16_t sv[kSbPerLane], bv[kSbPerLane];
@@ -290,6 +290,10 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
       sv[j] = srow[src];
       bv[j] = brow[src];
     }
+    // the first weight block goes out after the small loads and unconditionally
+    // (a wave without items loads out of range): vmcnt counts in order, so
+    // waiting for the activation and the scales then never waits for it
+    issue(A);
     if (t0) __syncthreads();  // everyone is done with the previous tile's activation
     // 2. form the activation tile; runs past the end are written as zeros
 #pragma unroll
