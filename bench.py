@@ -195,16 +195,28 @@ def time_graph_steps(graphs, steps):
 
 
 def time_batches(fn, iters, reps=5):
-    """Median over reps of (batch of `iters` calls) / iters, in seconds, via HIP events."""
+    """Seconds per call: `iters` calls (fn(0) .. fn(iters-1), which rotate
+    their inputs) captured in one HIP graph after a warm-up, the graph replayed
+    `reps` times between two HIP events on the capturing stream; median over
+    the replays.  Graph replay keeps host launch cost out of the kernel time."""
+    for i in range(min(iters, 3)):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
     times = []
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for i in range(iters):
-            fn(i)
+        g.replay()
         b.record()
         b.synchronize()
         times.append(a.elapsed_time(b) / 1e3 / iters)
+    del g
     return float(np.median(times))
 
 
@@ -229,11 +241,10 @@ def secondary(dev, quick):
     packed = torch.empty((N, K // 4), dtype=torch.int32, device=dev)
     sc = torch.empty((N, K // gs), dtype=torch.bfloat16, device=dev)
     bi = torch.empty((N, K // gs), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream().cuda_stream
-
-    def quant(i):
+    def quant(i):  # the current stream at call time (the capturing one inside a graph)
         w_ = wd[i % len(wd)]
-        binding.int8_quantize(w_.data_ptr(), N, K, gs, packed.data_ptr(), sc.data_ptr(), bi.data_ptr(), stream)
+        binding.int8_quantize(w_.data_ptr(), N, K, gs, packed.data_ptr(), sc.data_ptr(), bi.data_ptr(),
+                              torch.cuda.current_stream().cuda_stream)
 
     t = time_batches(quant, 10)
     b = 2 * N * K + N * K + 4 * N * K // gs

@@ -178,7 +178,7 @@ template <int LPG>
 hipError_t launch_lpg(const uint16_t *w, uint64_t chunks, uint32_t *packed, uint16_t *scales, uint16_t *biases,
                       hipStream_t stream) {
   const uint64_t items = (chunks + 63u) / 64u;
-  uint64_t blocks = 2u * (uint64_t)device_cu_count();
+  uint64_t blocks = 4u * (uint64_t)device_cu_count();  // four 8-wave workgroups per CU (measured best)
   const uint64_t need = (items + kQWaves - 1) / kQWaves;
   if (blocks > need) blocks = need;
   if (blocks == 0) blocks = 1;
