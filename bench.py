@@ -21,6 +21,7 @@ TFLOP/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
        python bench.py --profile-only     # dominant kernel + calibration copy, for rocprofv3
+       python bench.py --profile-prefill  # the m = 2048 prefill gemm alone, for rocprofv3 counters
 """
 from __future__ import annotations
 
@@ -465,6 +466,24 @@ def profile_only(dev, replays=2):
                       "calibration_copy_bytes": src.numel()}), flush=True)
 
 
+def profile_prefill(dev, launches=12):
+    """For rocprofv3 counters of the prefill kernel: the m = 2048 gemm on the
+    8B gate/up weight [14336, 4096] gs64, launched `launches` times (after a
+    warm-up of the same launch) on two rotated weights."""
+    N, K, gs, m = 14336, 4096, 64, 2048
+    ws = make_weights(2000 + N + gs, N, K, gs, 2, dev)
+    rng = np.random.default_rng(N + gs)
+    X = bits_dev(synth.gen_act(rng, (m, K)), dev)
+    Y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+    ws[0].gemm(X, Y)
+    torch.cuda.synchronize()
+    for i in range(launches):
+        ws[i % 2].gemm(X, Y)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_prefill": True, "m": m, "N": N, "K": K, "launches": launches + 1,
+                      "flops_per_launch": 2 * m * N * K}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -474,6 +493,8 @@ def main():
     ap.add_argument("--full-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true")
+    ap.add_argument("--profile-prefill", action="store_true",
+                    help="only the m = 2048 prefill gemm, for rocprofv3 counters")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic record from two rocprofv3 --pmc runs of --profile-only, then exit")
     args = ap.parse_args()
@@ -486,6 +507,9 @@ def main():
     load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile_prefill:
+        profile_prefill(dev)
+        return
     if args.profile_only:
         profile_only(dev)
         return
