@@ -25,6 +25,12 @@
 //  * Work order: the M tiles of one N tile are consecutive, and consecutive
 //    work items are kept on one XCD (workgroups are dealt round-robin over
 //    the 8 XCDs), so the blocks sharing a weight tile share an L2.
+//  * The large shape (256 x 128) specialises waves: 8 MFMA waves consume step
+//    k from one LDS buffer while 8 producer waves load, dequantize and store
+//    step k + 1 into the other, with one barrier per step.  With one
+//    workgroup per CU (96 KiB of LDS) the waves of the other design moved in
+//    lockstep between an MFMA phase and a dequantize-and-store phase; here the
+//    two phases overlap (measured +10 % at m = 2048, MFMA busy 30 % before).
 #include "common.h"
 #include "launch.h"
 
@@ -215,6 +221,191 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_prefill(
   }
 }
 
+// Wave-specialised variant: WGM x WGN MFMA waves and NP producer waves.  The
+// producers load, dequantize and store step k+1 into one LDS buffer while
+// the MFMA waves consume step k from the other; one workgroup barrier per
+// step.  Each role runs its own loop with the same number of barriers.
+template <int BM, int BN, int WGM, int WGN, int NP>
+__global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_ws(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ X, uint16_t *__restrict__ Y,
+    uint32_t N, uint32_t K, uint32_t m, uint32_t gs_log2, uint32_t mtiles, uint32_t nwork) {
+  constexpr int kMma = WGM * WGN;          // MFMA waves
+  constexpr int kPT = 64 * NP;             // producer threads
+  constexpr int XR = kPT / 8;              // X rows per producer pass
+  constexpr int WR = kPT / 4;              // weight rows per producer pass
+  constexpr int XP = BM / XR;
+  constexpr int WP = BN / WR;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TI = WTM / 16, TJ = WTN / 16;
+  static_assert(XP >= 1 && WP >= 1 && BM % XR == 0 && BN % WR == 0, "whole load passes");
+  constexpr uint32_t kStage = (BM + BN) * BK * 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_pf[];
+  auto lds = [&](uint32_t i) { return lds_pf + (i ? kStage : 0u); };
+
+  uint32_t bid = blockIdx.x;
+  if (nwork % kXcds == 0) bid = (bid % kXcds) * (nwork / kXcds) + bid / kXcds;
+  const uint32_t mt = bid % mtiles, nt = bid / mtiles;
+  const uint32_t m0 = mt * BM, n0 = nt * BN;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u, wave = uniform_pf(tid >> 6);
+  const uint32_t ksteps = (K + BK - 1) / BK;
+
+  if (wave >= (uint32_t)kMma) {
+    // ---------------- producer waves
+    const uint32_t ptid = tid - 64u * kMma;
+    const uint32_t G = K >> gs_log2;
+    const uint32_t mrows = m - m0 < (uint32_t)BM ? m - m0 : (uint32_t)BM;
+    const uint32_t nrows = N - n0 < (uint32_t)BN ? N - n0 : (uint32_t)BN;
+    const auto rx = make_rsrc(X + (size_t)m0 * K, mrows * K * 2u);
+    const auto rw = make_rsrc(codes + (size_t)n0 * K, nrows * K);
+    const auto rs = make_rsrc(scales + (size_t)n0 * G, nrows * G * 2u);
+    const auto rb = make_rsrc(biases + (size_t)n0 * G, nrows * G * 2u);
+    const uint32_t xr = ptid >> 3, xc = ptid & 7u;
+    const uint32_t wr = ptid >> 2, wp = ptid & 3u;
+    uint32_t vx[XP], vw[WP], vsb[WP];
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+      const uint32_t row = p * XR + xr;
+      vx[p] = row < mrows ? row * K * 2u + xc * 16u : kOutOfRange;
+    }
+#pragma unroll
+    for (int p = 0; p < WP; ++p) {
+      const uint32_t row = p * WR + wr;
+      vw[p] = row < nrows ? row * K + wp * 16u : kOutOfRange;
+      vsb[p] = row < nrows ? row * G * 2u : kOutOfRange;
+    }
+    using Regs = PfRegs<XP, WP>;
+    auto issue = [&](Regs &r, uint32_t ks) {
+      const bool live = ks < ksteps;
+      const uint32_t k0 = live ? ks * BK : 0u;
+      const bool xin = live && k0 + xc * 8u < K;
+      const bool win = live && k0 + wp * 16u < K;
+#pragma unroll
+      for (int p = 0; p < XP; ++p)
+        r.x[p] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xin ? vx[p] : kOutOfRange), (int)uniform_pf(2u * k0), 0);
+#pragma unroll
+      for (int p = 0; p < WP; ++p) {
+        r.w[p] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(win ? vw[p] : kOutOfRange), (int)uniform_pf(k0),
+                                                       kAuxNontemporal);
+        const uint32_t go = win ? vsb[p] + 2u * ((k0 + wp * 16u) >> gs_log2) : kOutOfRange;
+        r.s[p] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)go, 0, 0);
+        r.b[p] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)go, 0, 0);
+      }
+    };
+    auto store = [&](const Regs &r, uint8_t *buf) {
+      uint8_t *xs = buf;
+      uint8_t *ws = buf + BM * BK * 2;
+#pragma unroll
+      for (int p = 0; p < XP; ++p) *reinterpret_cast<u32x4 *>(xs + swz(p * XR + xr, xc)) = r.x[p];
+#pragma unroll
+      for (int p = 0; p < WP; ++p) {
+        const float sc = bf16_bits_to_f32(r.s[p]), bi = bf16_bits_to_f32(r.b[p]);
+        const uint32_t word[4] = {r.w[p].x, r.w[p].y, r.w[p].z, r.w[p].w};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = pack_bf16x2(__builtin_fmaf(code_f32(word[i], 0), sc, bi), __builtin_fmaf(code_f32(word[i], 1), sc, bi));
+          o[2 * i + 1] =
+              pack_bf16x2(__builtin_fmaf(code_f32(word[i], 2), sc, bi), __builtin_fmaf(code_f32(word[i], 3), sc, bi));
+        }
+        const uint32_t row = p * WR + wr;
+        *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp)) = u32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp + 1u)) = u32x4{o[4], o[5], o[6], o[7]};
+      }
+    };
+    Regs R0, R1;
+    issue(R0, 0);
+    issue(R1, 1);
+    store(R0, lds(0u));
+    __syncthreads();  // step 0 is in LDS
+    issue(R0, 2);
+    // while the MFMA waves consume step k, store step k + 1 and request k + 3
+    for (uint32_t k = 0;;) {
+      if (k + 1u >= ksteps) break;
+      store(R1, lds((k + 1u) & 1u));
+      issue(R1, k + 3u);
+      __syncthreads();
+      ++k;
+      if (k + 1u >= ksteps) break;
+      store(R0, lds((k + 1u) & 1u));
+      issue(R0, k + 3u);
+      __syncthreads();
+      ++k;
+    }
+    return;
+  }
+
+  // ---------------- MFMA waves
+  const uint32_t wm = wave / WGN, wn = wave % WGN;
+  f32x4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t lr = lane & 15u, lg = lane >> 4;
+  auto compute = [&](const uint8_t *buf) {
+    const uint8_t *xs = buf;
+    const uint8_t *ws = buf + BM * BK * 2;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const uint32_t chunk = 4u * kh + lg;
+      bf16x8 a[TI], b[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8 *>(xs + swz(wm * WTM + 16u * i + lr, chunk));
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        b[j] = *reinterpret_cast<const bf16x8 *>(ws + swz(wn * WTN + 16u * j + lr, chunk));
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  __syncthreads();  // step 0 is in LDS
+  for (uint32_t k = 0;;) {
+    compute(lds(k & 1u));
+    if (k + 1u >= ksteps) break;
+    __syncthreads();  // step k + 1 is in LDS, and everyone is done with step k's buffer
+    ++k;
+  }
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const uint32_t n = n0 + wn * WTN + 16u * j + lr;
+      if (n >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t row = m0 + wm * WTM + 16u * i + 4u * lg + r;
+        if (row < m) Y[(size_t)row * N + n] = to_bf16_bits(acc[i][j][r]);
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int NP>
+hipError_t launch_tile_ws(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream) {
+  auto kern = k_gemm_prefill_ws<BM, BN, WGM, WGN, NP>;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const uint32_t mtiles = (m + BM - 1) / BM;
+  const uint32_t ntiles = (w.N + BN - 1) / BN;
+  const uint32_t nwork = mtiles * ntiles;
+  const size_t lds = 2u * (BM + BN) * BK * 2u;
+  hipLaunchKernelGGL(kern, dim3(nwork), dim3(64 * (WGM * WGN + NP)), lds, stream,
+                     reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m,
+                     (uint32_t)__builtin_ctz(w.gs), mtiles, nwork);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_tile(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream) {
   auto kern = k_gemm_prefill<BM, BN, WGM, WGN>;
@@ -237,14 +428,14 @@ hipError_t launch_tile(const WeightView &w, const uint16_t *X, uint16_t *Y, uint
 }  // namespace
 
 // Tile shapes (BM x BN, waves): 0 = 128 x 128 (2 x 2), 1 = 128 x 64 (2 x 2),
-// 2 = 256 x 128 (2 x 2), 3 = 256 x 128 (4 x 2), 4 = 256 x 256 (4 x 2),
-// 5 = 128 x 128 (4 x 2).
+// 2 = 256 x 128 (2 x 2), 3 = 256 x 128 (4 x 2 MFMA waves + 8 producer waves),
+// 4 = 256 x 256 (4 x 2), 5 = 128 x 128 (4 x 2).
 hipError_t launch_gemm_prefill_tile(int t, const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                                     hipStream_t stream) {
   switch (t) {
     case 1: return launch_tile<128, 64, 2, 2>(w, X, Y, m, stream);
     case 2: return launch_tile<256, 128, 2, 2>(w, X, Y, m, stream);
-    case 3: return launch_tile<256, 128, 4, 2>(w, X, Y, m, stream);
+    case 3: return launch_tile_ws<256, 128, 4, 2, 8>(w, X, Y, m, stream);
     case 4: return launch_tile<256, 256, 4, 2>(w, X, Y, m, stream);
     case 5: return launch_tile<128, 128, 4, 2>(w, X, Y, m, stream);
     default: return launch_tile<128, 128, 2, 2>(w, X, Y, m, stream);
