@@ -130,9 +130,11 @@ int int8_gemv_multi(const int8w_weight *w, uint32_t count, const uint16_t *x, ui
  *   - y is BF16 [tokens, topk, N]: y[t, j, n] = sum_k w_e[n, k] x_(t,j)[k]
  *     with e = ids[t, j], with int8_gemv's arithmetic and bound.
  * A slot whose id is not below num_experts reads no weight and gets the BF16
- * quiet NaN 0x7FC0 in all N outputs.  Each slot streams its expert's rows:
- * an expert named by several slots (tokens > 1) is read once per slot.
- * tokens = 0 or topk = 0 is a no-op.  Errors: INT8W_ERR_SHAPE for num_experts = 0 or not dividing
+ * quiet NaN 0x7FC0 in all N outputs.  One token: each slot streams its
+ * expert's rows.  Several tokens with tokens * topk >= num_experts (at most
+ * 256 slots, 512 experts, in_features 1024..4096 a multiple of 1024): each
+ * named expert is streamed once for all the slots naming it; the results are
+ * the same bits either way.  tokens = 0 or topk = 0 is a no-op.  Errors: INT8W_ERR_SHAPE for num_experts = 0 or not dividing
  * out_features, x_rows not 1 or topk, or more than INT8W_MAX_MOE_SLOTS slots;
  * INT8W_ERR_ALIGN for x not 16-byte or ids not 4-byte aligned; INT8W_ERR_ALIAS
  * for y overlapping the experts, x or ids. */

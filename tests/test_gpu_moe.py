@@ -99,3 +99,25 @@ def test_moe_gemv_equals_gemv_of_the_selected_expert():
         assert np.array_equal(y[0, j], ye), j
     y_ref, A = oracle.moe_gemv(w.packed, w.scales, w.biases, gs, E, x, ids)
     assert_close(y, y_ref, A, "moe_gemv 8 x [14336, 4096] top-2")
+
+
+@pytest.mark.parametrize("E,N,K,gs,T,topk,per_slot", [
+    (2, 640, 4096, 64, 6, 2, False),   # every token names both experts: 6 slots each, two passes of 4
+    (8, 512, 2048, 32, 5, 3, True),    # own input rows per slot
+    (64, 96, 1024, 128, 16, 8, False), # many experts, many slots
+])
+def test_moe_gemv_several_tokens_each_slot_equals_gemv_of_its_expert(E, N, K, gs, T, topk, per_slot):
+    # the expert-grouped form streams each named expert once for all its
+    # slots; every slot's outputs are still bit-identical to int8_gemv of its
+    # expert on its input row (same per-row arithmetic), and within tolerance
+    log(f"moe_gemv grouped E={E} N={N} K={K} gs={gs} T={T} topk={topk} per_slot={per_slot}")
+    w, W, x, ids, y = run_case(81_000 + E + N + K + T, E, N, K, gs, T, topk, per_slot)
+    y_ref, A = oracle.moe_gemv(w.packed, w.scales, w.biases, gs, E, x, ids)
+    assert_close(y, y_ref, A, f"moe_gemv grouped E={E} T={T}")
+    for t in range(T):
+        for j in range(topk):
+            e = int(ids[t, j])
+            sl = slice(e * N, (e + 1) * N)
+            We = Int8Weight(W.packed[sl], W.scales[sl], W.biases[sl], gs)
+            xe = bits_to_dev(np.ascontiguousarray(x[t, j if per_slot else 0]))
+            assert np.array_equal(y[t, j], dev_to_bits(We.gemv(xe))), (t, j)

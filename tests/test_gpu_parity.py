@@ -90,6 +90,14 @@ GEMV_SHAPES = [
     (300, 1056, 32),      # two segments, the second with two runs
     (3, 16384, 128),      # the largest K of one LDS tile
     (77, 8224, 32),       # 16-wave workgroups, ragged segment
+    # in_features 1024..4096 (a multiple of 1024) take the register-resident
+    # form: every segment count and group size
+    (2000, 4096, 32),
+    (600, 4096, 128),
+    (999, 1024, 64),
+    (513, 2048, 128),
+    (250, 3072, 32),
+    (20000, 4096, 64),    # more than 16384 rows: two workgroups per CU
 ]
 
 
@@ -126,6 +134,8 @@ MULTI_CASES = [
     ([300, 5], 20480, 128),           # two LDS tiles
     ([77, 3000], 4128, 32),           # partial last segment
     ([1], 32, 32),
+    ([700, 300], 2048, 32),           # register-resident form, two weights
+    ([9000, 9000, 100], 4096, 128),   # register-resident form, three weights over 16384 rows
 ]
 
 
