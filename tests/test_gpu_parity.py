@@ -284,6 +284,31 @@ def test_gemm_prefill_small(m, N, K, gs):
     assert_close(dev_to_bits(Y), Y_ref, A, f"gemm m={m} {N}x{K} gs{gs}")
 
 
+@pytest.mark.parametrize("m,N,K,gs", [
+    (513, 8200, 1024, 128),   # one scale/bias block (16 steps), ragged rows and columns
+    (300, 24000, 1536, 64),   # three blocks of 8 steps, last column tile half full
+    (1030, 6500, 2048, 32),   # eight blocks of 4 steps
+    (700, 9000, 512, 64),     # a single block, K of 8 steps
+])
+def test_gemm_prefill_staged_sampled_rows(m, N, K, gs):
+    """Shapes that take the DMA-staged 256 x 128 kernel (enough tiles, K a
+    multiple of 8 group sizes), compared on sampled rows including the last
+    (ragged) row tile."""
+    log(f"gemm prefill staged m={m} N={N} K={K} gs={gs}")
+    w, rng = make_weight(3_700 + m + N + K, N, K, gs)
+    X = synth.gen_act(rng, (m, K))
+    W = upload(w)
+    Y = W.gemm(bits_to_dev(X))
+    _sync()
+    Yb = dev_to_bits(Y)
+    tail = np.arange((m // 256) * 256, m)
+    rows = np.unique(np.concatenate([[0, 255, m - 1], tail[:: max(1, len(tail) // 8)],
+                                     np.random.default_rng(m + N).choice(m, 16, replace=False)]))
+    Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X[rows])
+    assert_close(Yb[rows], Y_ref, A, f"gemm m={m} {N}x{K} gs{gs} rows {rows.tolist()[:6]}...")
+    assert np.isfinite(oracle.bf16_to_f32(Yb)).all()
+
+
 @pytest.mark.parametrize("m", [512, 2048])
 @pytest.mark.parametrize("N,K", SMALLM_SHAPES)
 def test_gemm_prefill_full_size_sampled_rows(m, N, K):

@@ -26,11 +26,13 @@
 //    work items are kept on one XCD (workgroups are dealt round-robin over
 //    the 8 XCDs), so the blocks sharing a weight tile share an L2.
 //  * The large shape (256 x 128) specialises waves: 8 MFMA waves consume step
-//    k from one LDS buffer while 8 producer waves load, dequantize and store
-//    step k + 1 into the other, with one barrier per step.  With one
-//    workgroup per CU (96 KiB of LDS) the waves of the other design moved in
-//    lockstep between an MFMA phase and a dequantize-and-store phase; here the
-//    two phases overlap (measured +10 % at m = 2048, MFMA busy 30 % before).
+//    k while producer waves load, dequantize and store a later step, with one
+//    barrier per step.  With one workgroup per CU the waves of the
+//    single-role design moved in lockstep between an MFMA phase and a
+//    dequantize-and-store phase; here the two phases overlap (measured +10 %
+//    at m = 2048, MFMA busy 30 % before).  k_gemm_prefill_dma (the usual
+//    case, K % (8 gs) == 0) stages X and the scales/biases by DMA over three
+//    LDS stages; k_gemm_prefill_ws (any K) loads through registers.
 #include "common.h"
 #include "launch.h"
 
@@ -386,6 +388,262 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_ws(
   }
 }
 
+// The main prefill kernel: wave-specialised like k_gemm_prefill_ws, with the
+// operands staged by DMA (buffer_load_dwordx4 ... lds: memory straight into
+// LDS, no registers, no LDS stores).
+//  * LDS holds three K steps.  Between barriers k - 1 and k the producers
+//    request step k + 2's X tile into stage (k + 2) % 3 (it held step k - 1,
+//    whose readers passed barrier k - 1), dequantize step k + 1's weight tile
+//    into stage (k + 1) % 3 from codes loaded three steps ahead into
+//    registers, and wait for step k + 1's X DMA, issued one iteration
+//    earlier; barrier k then publishes step k + 1 while the MFMA waves
+//    consume step k.
+//  * Scales and biases arrive by DMA in blocks of 8 groups per row (16
+//    bytes; gs / 8 steps), double-buffered in LDS: per step a producer reads
+//    one scale and one bias per row it dequantizes from LDS instead of
+//    issuing two 2-byte global loads.  Needs K % (8 gs) == 0.
+//  * Measured on MI355X (m = 2048, 14336 x 4096): per-instruction costs of
+//    the producers' global loads set the pace, not the MFMAs; staging X and
+//    the scales/biases by DMA took 292 us to about 268 us.
+template <int BM, int BN, int WGM, int WGN, int NP>
+__global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ X, uint16_t *__restrict__ Y,
+    uint32_t N, uint32_t K, uint32_t m, uint32_t gs_log2, uint32_t mtiles, uint32_t nwork) {
+  constexpr int kMma = WGM * WGN;          // MFMA waves
+  constexpr int kPT = 64 * NP;             // producer threads
+  constexpr int XR = kPT / 8;              // X rows per producer pass
+  constexpr int WR = kPT / 4;              // weight rows per producer pass
+  constexpr int XP = BM / XR;
+  constexpr int WP = BN / WR;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TI = WTM / 16, TJ = WTN / 16;
+  static_assert(XP >= 1 && WP >= 1 && BM % XR == 0 && BN % WR == 0, "whole load passes");
+  static_assert(BN == 128 && NP == 4, "scale/bias staging: 4 waves x 64 lanes cover 128 rows x {scales, biases}");
+  constexpr uint32_t kStage = (BM + BN) * BK * 2;
+  constexpr uint32_t kSbBytes = BN * 16u * 2u;  // one block: 8 groups of scales and of biases per row
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_pf[];
+  auto stage = [&](uint32_t i) { return lds_pf + i * kStage; };
+  auto next3 = [](uint32_t i) { return i == 2u ? 0u : i + 1u; };
+
+  uint32_t bid = blockIdx.x;
+  if (nwork % kXcds == 0) bid = (bid % kXcds) * (nwork / kXcds) + bid / kXcds;
+  const uint32_t mt = bid % mtiles, nt = bid / mtiles;
+  const uint32_t m0 = mt * BM, n0 = nt * BN;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u, wave = uniform_pf(tid >> 6);
+  const uint32_t ksteps = (K + BK - 1) / BK;
+
+  if (wave >= (uint32_t)kMma) {
+    // ---------------- producer waves
+    const uint32_t ptid = tid - 64u * kMma;
+    const uint32_t G = K >> gs_log2;
+    const uint32_t mrows = m - m0 < (uint32_t)BM ? m - m0 : (uint32_t)BM;
+    const uint32_t nrows = N - n0 < (uint32_t)BN ? N - n0 : (uint32_t)BN;
+    const auto rx = make_rsrc(X + (size_t)m0 * K, mrows * K * 2u);
+    const auto rw = make_rsrc(codes + (size_t)n0 * K, nrows * K);
+    const auto rs = make_rsrc(scales + (size_t)n0 * G, nrows * G * 2u);
+    const auto rb = make_rsrc(biases + (size_t)n0 * G, nrows * G * 2u);
+    const uint32_t wr = ptid >> 2, wp = ptid & 3u;
+    // X by DMA: one instruction fills 8 LDS rows (1 KiB, lane i -> byte 16 i);
+    // lane i carries row r0 + i / 8 and, through the swizzle, logical chunk
+    // (i % 8) ^ (i / 8).  Producer wave pw fills rows 8 (j NP + pw) .. + 7.
+    constexpr int XJ = BM / (8 * NP);
+    const uint32_t pw = wave - (uint32_t)kMma, plane = lane;
+    const uint32_t xchunk = (plane & 7u) ^ (plane >> 3);
+    uint32_t vxd[XJ];
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+      const uint32_t row = (j * NP + pw) * 8u + (plane >> 3);
+      vxd[j] = row < mrows ? row * K * 2u + xchunk * 16u : kOutOfRange;
+    }
+    auto xdma = [&](uint32_t ks, uint32_t st) {
+      const bool live = ks < ksteps;
+      const uint32_t k0 = live ? ks * BK : 0u;
+      const bool xin = live && k0 + xchunk * 8u < K;
+#pragma unroll
+      for (int j = 0; j < XJ; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (__attribute__((address_space(3))) void *)(stage(st) + (j * NP + pw) * 8u * (BK * 2)), 16,
+            (int)(xin ? vxd[j] : kOutOfRange), (int)uniform_pf(2u * k0), 0, 0);
+    };
+    // Scales and biases by DMA, a block of 8 groups (8 gs codes, gs / 8
+    // steps) at a time, double-buffered: wave pw copies 16 bytes per row for
+    // rows 64 (pw % 2) .. + 63 of the scales (pw < 2) or biases (pw >= 2).
+    // Needs K % (8 gs) == 0, so that every row's block is 16 whole bytes.
+    const uint32_t sbs_log2 = gs_log2 - 3u;  // steps per block, log2
+    const uint32_t nblk = K >> (gs_log2 + 3u);
+    auto sbuf = [&](uint32_t i) { return lds_pf + 3u * kStage + i * kSbBytes; };
+    const uint32_t sbrow = (pw & 1u) * 64u + plane;
+    const uint32_t vsbd = sbrow < nrows ? sbrow * G * 2u : kOutOfRange;
+    auto sbdma = [&](uint32_t blk) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            pw >= 2u ? rb : rs,
+            (__attribute__((address_space(3))) void *)(sbuf(blk & 1u) + (pw >> 1) * (BN * 16u) + (pw & 1u) * 1024u),
+            16, (int)vsbd, (int)uniform_pf(blk * 16u), 0, 0);
+    };
+    uint32_t vw[WP];
+#pragma unroll
+    for (int p = 0; p < WP; ++p) {
+      const uint32_t row = p * WR + wr;
+      vw[p] = row < nrows ? row * K + wp * 16u : kOutOfRange;
+    }
+    struct Regs {
+      u32x4 w[WP];
+    };
+    auto issue = [&](Regs &r, uint32_t ks) {
+      const bool live = ks < ksteps;
+      const uint32_t k0 = live ? ks * BK : 0u;
+      const bool win = live && k0 + wp * 16u < K;
+#pragma unroll
+      for (int p = 0; p < WP; ++p)
+        r.w[p] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(win ? vw[p] : kOutOfRange), (int)uniform_pf(k0),
+                                                       kAuxNontemporal);
+    };
+    auto store = [&](const Regs &r, uint8_t *buf, uint32_t ks) {
+      uint8_t *ws = buf + BM * BK * 2;
+      const uint8_t *sb = sbuf((ks >> sbs_log2) & 1u);
+      const uint32_t g = ((ks * BK + wp * 16u) >> gs_log2) & 7u;
+#pragma unroll
+      for (int p = 0; p < WP; ++p) {
+        const uint32_t srow = p * WR + wr;
+        const float sc = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + srow * 16u + 2u * g));
+        const float bi = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + BN * 16u + srow * 16u + 2u * g));
+        const uint32_t word[4] = {r.w[p].x, r.w[p].y, r.w[p].z, r.w[p].w};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = pack_bf16x2(__builtin_fmaf(code_f32(word[i], 0), sc, bi), __builtin_fmaf(code_f32(word[i], 1), sc, bi));
+          o[2 * i + 1] =
+              pack_bf16x2(__builtin_fmaf(code_f32(word[i], 2), sc, bi), __builtin_fmaf(code_f32(word[i], 3), sc, bi));
+        }
+        const uint32_t row = p * WR + wr;
+        *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp)) = u32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp + 1u)) = u32x4{o[4], o[5], o[6], o[7]};
+      }
+    };
+    // vmcnt(n) with expcnt and lgkmcnt left open
+#define INT8W_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
+    Regs R0, R1, R2;
+    // Iteration k (between barriers k - 1 and k): the X DMA of step k + 2
+    // goes to stage (k + 2) % 3 (it held step k - 1, read before barrier
+    // k - 1); step k + 1's weights are dequantized into stage (k + 1) % 3;
+    // step k + 4's codes are requested; and the X DMA of step k + 1, issued
+    // one iteration earlier, is awaited.  Barrier k thus publishes step k + 1
+    // and every X DMA has two iterations to land.
+    sbdma(0u);
+    if (1u < nblk) sbdma(1u);
+    issue(R0, 0);
+    issue(R1, 1);
+    issue(R2, 2);
+    xdma(0u, 0u);
+    xdma(1u, 1u);
+    INT8W_VMCNT(3 * WP + 2 * XJ);  // scale/bias blocks 0 and 1 have landed
+    __syncthreads();  // ... for every producer wave
+    store(R0, stage(0u), 0u);
+    issue(R0, 3);
+    INT8W_VMCNT(XJ + WP);  // the X DMA of step 0 has landed
+    __syncthreads();  // step 0 is in LDS
+    auto step = [&](Regs &r, uint32_t k, uint32_t sx, uint32_t sw) {
+      const uint32_t s = k + 1u;
+      xdma(k + 2u, sx);
+      store(r, stage(sw), s);
+      issue(r, k + 4u);
+      // at the first step of scale/bias block b, block b + 1 goes into the
+      // buffer that held block b - 1
+      if (s != 0u && (s & ((1u << sbs_log2) - 1u)) == 0u && (s >> sbs_log2) + 1u < nblk) sbdma((s >> sbs_log2) + 1u);
+      INT8W_VMCNT(XJ + 2 * WP);  // the X DMA of step k + 1 has landed
+      __syncthreads();
+    };
+#undef INT8W_VMCNT
+    for (uint32_t k = 0;;) {
+      if (k + 1u >= ksteps) break;
+      step(R1, k, 2u, 1u);
+      if (++k + 1u >= ksteps) break;
+      step(R2, k, 0u, 2u);
+      if (++k + 1u >= ksteps) break;
+      step(R0, k, 1u, 0u);
+      ++k;
+    }
+    return;
+  }
+
+  // ---------------- MFMA waves
+  const uint32_t wm = wave / WGN, wn = wave % WGN;
+  f32x4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t lr = lane & 15u, lg = lane >> 4;
+  // operand fragments of one half step (32 of the 64 K positions)
+  auto load_frags = [&](bf16x8 *a, bf16x8 *b, const uint8_t *buf, uint32_t kh) {
+    const uint8_t *xs = buf;
+    const uint8_t *ws = buf + BM * BK * 2;
+    const uint32_t chunk = 4u * kh + lg;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(xs + swz(wm * WTM + 16u * i + lr, chunk));
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(ws + swz(wn * WTN + 16u * j + lr, chunk));
+  };
+  auto mma = [&](const bf16x8 *a, const bf16x8 *b) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  // one half step's operands at a time: the other MFMA wave on the SIMD
+  // covers the LDS latency (measured equal to or faster than reading both
+  // halves ahead, with fewer registers)
+  bf16x8 a[TI], b[TJ];
+  __syncthreads();  // the producers' scale/bias staging
+  __syncthreads();  // step 0 is in LDS
+  uint32_t s = 0;
+  for (uint32_t k = 0;;) {
+    load_frags(a, b, stage(s), 0u);
+    mma(a, b);
+    load_frags(a, b, stage(s), 1u);
+    mma(a, b);
+    if (k + 1u >= ksteps) break;
+    __syncthreads();  // step k + 1 is in LDS; everyone is done with step k
+    s = next3(s);
+    ++k;
+  }
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const uint32_t n = n0 + wn * WTN + 16u * j + lr;
+      if (n >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t row = m0 + wm * WTM + 16u * i + 4u * lg + r;
+        if (row < m) Y[(size_t)row * N + n] = to_bf16_bits(acc[i][j][r]);
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int NP>
+hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream) {
+  auto kern = k_gemm_prefill_dma<BM, BN, WGM, WGN, NP>;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const uint32_t mtiles = (m + BM - 1) / BM;
+  const uint32_t ntiles = (w.N + BN - 1) / BN;
+  const uint32_t nwork = mtiles * ntiles;
+  const size_t lds = 3u * (BM + BN) * BK * 2u + BN * 16u * 2u * 2u;
+  hipLaunchKernelGGL(kern, dim3(nwork), dim3(64 * (WGM * WGN + NP)), lds, stream,
+                     reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m,
+                     (uint32_t)__builtin_ctz(w.gs), mtiles, nwork);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN, int NP>
 hipError_t launch_tile_ws(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream) {
   auto kern = k_gemm_prefill_ws<BM, BN, WGM, WGN, NP>;
@@ -428,16 +686,16 @@ hipError_t launch_tile(const WeightView &w, const uint16_t *X, uint16_t *Y, uint
 }  // namespace
 
 // Tile shapes (BM x BN, waves): 0 = 128 x 128 (2 x 2), 1 = 128 x 64 (2 x 2),
-// 2 = 256 x 128 (2 x 2), 3 = 256 x 128 (4 x 2 MFMA waves + 8 producer waves),
-// 4 = 256 x 256 (4 x 2), 5 = 128 x 128 (4 x 2).
+// 2 = 256 x 128 (4 x 2 MFMA waves + 8 producer waves), 3 = 256 x 128 staged
+// by DMA (4 x 2 MFMA waves + 4 producer waves; K % (8 gs) == 0).
 hipError_t launch_gemm_prefill_tile(int t, const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                                     hipStream_t stream) {
   switch (t) {
     case 1: return launch_tile<128, 64, 2, 2>(w, X, Y, m, stream);
-    case 2: return launch_tile<256, 128, 2, 2>(w, X, Y, m, stream);
-    case 3: return launch_tile_ws<256, 128, 4, 2, 8>(w, X, Y, m, stream);
-    case 4: return launch_tile<256, 256, 4, 2>(w, X, Y, m, stream);
-    case 5: return launch_tile<128, 128, 4, 2>(w, X, Y, m, stream);
+    case 2: return launch_tile_ws<256, 128, 4, 2, 8>(w, X, Y, m, stream);
+    case 3:
+      if (w.K % (8u * w.gs) != 0u) return hipErrorInvalidValue;
+      return launch_tile_dma<256, 128, 4, 2, 4>(w, X, Y, m, stream);
     default: return launch_tile<128, 128, 2, 2>(w, X, Y, m, stream);
   }
 }
@@ -449,7 +707,8 @@ hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t 
   const uint32_t cus = (uint32_t)device_cu_count();
   const uint32_t t256 = ((m + 255u) / 256u) * ((w.N + 127u) / 128u);
   const uint32_t t128 = ((m + 127u) / 128u) * ((w.N + 127u) / 128u);
-  const int shape = 4u * t256 >= 3u * cus ? 3 : (4u * t128 >= 3u * cus ? 0 : 1);
+  const int big = w.K % (8u * w.gs) == 0u ? 3 : 2;
+  const int shape = 4u * t256 >= 3u * cus ? big : (4u * t128 >= 3u * cus ? 0 : 1);
   return launch_gemm_prefill_tile(shape, w, X, Y, m, stream);
 }
 
