@@ -21,15 +21,17 @@
 //    each 32-code half, one group each.
 //  * A workgroup of KS waves owns RT tiles of 16 weight rows and walks K in
 //    blocks of KB = 64*KS*SPW codes.  Each block (the tiles' codes and the 16
-//    X rows, rows past m zero) is loaded with every load reading whole 16-byte
-//    chunks of one row in contiguous runs (the weight stream stays sequential
-//    in HBM), written to LDS with the 16-byte chunks of row r XOR-swizzled by
-//    r mod 16 (so the 16 rows an MFMA operand read touches sit in distinct
-//    banks), and read back in MFMA operand layout.  Wave w takes the SPW steps
-//    [w*SPW, (w+1)*SPW) of every block for all RT tiles.
-//  * Pipeline: D blocks are in flight in registers while the LDS copy of
-//    another is consumed; one workgroup barrier per block.  Every global load
-//    goes through a bounded buffer resource: past the end it reads zeros.
+//    X rows, rows past m zero) is copied by DMA (buffer_load_dwordx4 ... lds)
+//    with every load reading whole 16-byte chunks of one row in contiguous
+//    runs (the weight stream stays sequential in HBM) and landing in LDS with
+//    the 16-byte chunks of row r XOR-swizzled by r mod 16 (so the 16 rows an
+//    MFMA operand read touches sit in distinct banks), then read back in MFMA
+//    operand layout.  Wave w takes the SPW steps [w*SPW, (w+1)*SPW) of every
+//    block for all RT tiles.
+//  * Pipeline: NS LDS block buffers; the DMA of NS - 1 blocks is in flight
+//    while one is consumed; one workgroup barrier per block.  Every global
+//    load goes through a bounded buffer resource: past the end it reads (or
+//    writes to LDS) zeros.
 //  * Scales and biases of the workgroup's rows are staged in LDS once, packed
 //    as BF16 pairs.  The KS partial sums meet in LDS in wave order (no
 //    atomics: deterministic).
@@ -54,14 +56,6 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Loads of one block held in registers: NC code chunks and NX X chunks of
-// 64 x 16 bytes per wave.
-template <int NC, int NX>
-struct SmRegs {
-  u32x4 c[NC];
-  u32x4 x[NX];
-};
-
 template <int KS, int RT, int SPW, bool G32>
 struct SmShape {
   static constexpr int kThreads = 64 * KS;
@@ -77,9 +71,9 @@ struct SmShape {
   static_assert(CPR >= 16, "swizzle needs 16 chunks per row");
 };
 
-// LDS (dynamic): two block buffers [codes | X], then sb [16*RT][G+1] packed
-// (scale | bias << 16).  The partial-sum exchange reuses buffer 0.
-template <int KS, int RT, int SPW, int D, bool G32>
+// LDS (dynamic): NS block buffers [codes | X], then sb [16*RT][G+1] packed
+// (scale | bias << 16).  The partial-sum exchange reuses the block buffers.
+template <int KS, int RT, int SPW, int NS, bool G32>
 __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ X, uint16_t *__restrict__ Y,
@@ -88,7 +82,7 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_sm[];
   const uint32_t G = K >> gs_log2;
   const uint32_t SBP = G + 1u;  // odd pitch: the 16 rows of a read hit distinct banks
-  uint32_t *sb = reinterpret_cast<uint32_t *>(lds_sm + 2u * S::BUF_BYTES);
+  uint32_t *sb = reinterpret_cast<uint32_t *>(lds_sm + NS * S::BUF_BYTES);
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
@@ -126,45 +120,40 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
     vx[j] = row < m ? row * K * 2u + 16u * c : kOutOfRange;
   }
 
-  using Regs = SmRegs<S::NC, S::NX>;
-  auto issue = [&](Regs &r, uint32_t blk) {
+  // Block blk goes straight from memory into LDS buffer `buf` by DMA
+  // (buffer_load_dwordx4 ... lds: lane i of a wave's load j writes the 16
+  // bytes at (wave NC + j) 1024 + 16 i, the layout above); past the end of a
+  // row or of X a lane writes zeros.
+  auto dma = [&](uint32_t blk, uint32_t buf) {
     const bool live = blk < nb;
     const uint32_t kb = live ? blk * S::KB : 0u;
+    uint8_t *base = lds_sm + buf * S::BUF_BYTES;
 #pragma unroll
     for (int j = 0; j < S::NC; ++j) {
       const bool in = live && kb + 16u * cchunk[j] < K;
-      r.c[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(in ? vc[j] : kOutOfRange), (int)uniform_sm(kb),
-                                                     kAuxNontemporal);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void *)(base + (wave * S::NC + j) * 1024u), 16,
+          (int)(in ? vc[j] : kOutOfRange), (int)uniform_sm(kb), 0, kAuxNontemporal);
     }
 #pragma unroll
     for (int j = 0; j < S::NX; ++j) {
       const bool in = live && 2u * kb + 16u * xchunk[j] < 2u * K;
-      r.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(in ? vx[j] : kOutOfRange), (int)uniform_sm(2u * kb),
-                                                     0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void *)(base + S::CODE_BYTES + (wave * S::NX + j) * 1024u), 16,
+          (int)(in ? vx[j] : kOutOfRange), (int)uniform_sm(2u * kb), 0, 0);
     }
-  };
-  auto stage = [&](const Regs &r, uint32_t buf) {
-    uint8_t *base = lds_sm + buf * S::BUF_BYTES;
-#pragma unroll
-    for (int j = 0; j < S::NC; ++j)
-      *reinterpret_cast<u32x4 *>(base + (wave * S::NC + j) * 1024u + 16u * lane) = r.c[j];
-#pragma unroll
-    for (int j = 0; j < S::NX; ++j)
-      *reinterpret_cast<u32x4 *>(base + S::CODE_BYTES + (wave * S::NX + j) * 1024u + 16u * lane) = r.x[j];
   };
 
   // ---- scales and biases of the workgroup's rows, all groups, packed as
-  // (scale | bias << 16).  Entries past the first kSbPre per thread are staged
-  // first (long rows only); the first kSbPre are loaded, then the first D
-  // blocks are issued, and only then are those entries written, so the
-  // pipeline starts full and the loop sees the same loads in flight on entry
-  // as on every later iteration.
+  // (scale | bias << 16); the first NS - 1 blocks are requested first so that
+  // they stream in meanwhile.
   const auto rs = make_rsrc(scales + (size_t)n0 * G, rows * G * 2u);
   const auto rb = make_rsrc(biases + (size_t)n0 * G, rows * G * 2u);
   const uint32_t total = 16u * RT * G;
   const uint32_t spare = 16u * RT * SBP;  // slot for entries past the end (branch-free writes)
-  constexpr int kSbPre = 8;
-  for (uint32_t e0 = kSbPre * S::kThreads; e0 < total; e0 += 4u * S::kThreads) {
+#pragma unroll
+  for (int d = 0; d < NS - 1; ++d) dma((uint32_t)d, (uint32_t)d);
+  for (uint32_t e0 = 0; e0 < total; e0 += 4u * S::kThreads) {
     uint16_t sv[4], bv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -180,27 +169,6 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
       sb[e < total ? r * SBP + g : spare] = (uint32_t)sv[j] | ((uint32_t)bv[j] << 16);
     }
   }
-  uint16_t sv0[kSbPre], bv0[kSbPre];
-#pragma unroll
-  for (int j = 0; j < kSbPre; ++j) {
-    const uint32_t e = tid + (uint32_t)j * S::kThreads;
-    const uint32_t off = e < total ? e * 2u : kOutOfRange;
-    sv0[j] = buf_load_b16(rs, off);
-    bv0[j] = buf_load_b16(rb, off);
-  }
-
-  Regs R[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) issue(R[d], (uint32_t)d);
-#pragma unroll
-  for (int j = 0; j < kSbPre; ++j) {
-    const uint32_t e = tid + (uint32_t)j * S::kThreads;
-    const uint32_t r = e / G, g = e - r * G;
-    sb[e < total ? r * SBP + g : spare] = (uint32_t)sv0[j] | ((uint32_t)bv0[j] << 16);
-  }
-  stage(R[0], 0);
-  __syncthreads();
-  issue(R[0], (uint32_t)D);
 
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -208,8 +176,8 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = zero;
 
-  auto compute = [&](uint32_t blk) {
-    const uint8_t *cb = lds_sm + (blk & 1u) * S::BUF_BYTES;
+  auto compute = [&](uint32_t blk, uint32_t buf) {
+    const uint8_t *cb = lds_sm + buf * S::BUF_BYTES;
     const uint8_t *xbp = cb + S::CODE_BYTES;
 #pragma unroll
     for (int st = 0; st < SPW; ++st) {
@@ -270,24 +238,38 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
     }
   };
 
-  // ---- pipeline: while block b is consumed from LDS, blocks b+1 .. b+D are
-  // in flight in the D register sets; the set holding block b+1 is then
-  // written to the other LDS buffer and refilled with block b+1+D.  The only
-  // branches are the loop exits.
+  // ---- pipeline: NS LDS buffers.  At the top of step b, block b's DMA (the
+  // oldest in flight) is awaited and a barrier makes every wave's part of it
+  // visible -- and frees buffer (b - 1) % NS, which the DMA of block
+  // b + NS - 1 then refills while block b is consumed.  The explicit wait
+  // counts only this wave's DMA: the loop issues no other memory loads.
+#define INT8W_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
+  constexpr int kPerBlock = S::NC + S::NX;
+  static_assert((NS - 2) * kPerBlock < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the scale/bias stores are done before the first barrier
+  // Unrolled NS times so that every buffer index is a constant: the
+  // compiler can then tell the DMA's LDS writes from this step's LDS reads
+  // and does not wait for the DMA before reading.
   for (uint32_t b = 0;;) {
 #pragma unroll
-    for (int d = 1; d <= D; ++d) {
-      compute(b);
-      if (b + 1u >= nb) goto pipeline_done;
-      stage(R[d % D], (b + 1u) & 1u);
-      __syncthreads();
-      issue(R[d % D], b + 1u + D);
-      ++b;
+    for (int u = 0; u < NS; ++u) {
+      // A bare barrier: a fenced one would also wait for the DMA still in
+      // flight into the other buffers.  What it must order is explicit: this
+      // wave's part of block b has landed, and its reads of block b - 1 have
+      // returned (the compiler may place their last uses after this point).
+      INT8W_VMCNT((NS - 2) * kPerBlock);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+      dma(b + NS - 1u, (uint32_t)((u + NS - 1) % NS));
+      compute(b, (uint32_t)u);
+      if (++b >= nb) goto pipeline_done;
     }
   }
 pipeline_done:
+#undef INT8W_VMCNT
 
   // ---- combine the KS partial sums in wave order and store
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the look-ahead DMA (zeros past the end) has landed
   __syncthreads();  // every wave is done with the block buffers
   f32x4 *red = reinterpret_cast<f32x4 *>(lds_sm);
 #pragma unroll
@@ -313,23 +295,18 @@ pipeline_done:
   }
 }
 
-// Register sets in flight.  Two: with more, the compiler's wait-count
-// tracking drains every set once per pass of the unrolled loop (measured no
-// faster on MI355X).
-constexpr int kSmDepth = 2;
-
-template <int KS, int RT, int SPW>
+template <int KS, int RT, int SPW, int NS>
 size_t smallm_lds_bytes(uint32_t K, uint32_t gs) {
   using S = SmShape<KS, RT, SPW, false>;
   const size_t G = K / gs;
-  size_t bytes = 2u * S::BUF_BYTES + (16u * RT * (G + 1u) + 1u) * 4u;  // + the spare slot
+  size_t bytes = NS * S::BUF_BYTES + (16u * RT * (G + 1u) + 1u) * 4u;  // + the spare slot
   const size_t red = (size_t)KS * RT * 64u * 16u;
   return bytes > red ? bytes : red;
 }
 
-template <int KS, int RT, int SPW, int D, bool G32>
+template <int KS, int RT, int SPW, int NS, bool G32>
 hipError_t launch_sm(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream) {
-  auto kern = k_gemm_smallm<KS, RT, SPW, D, G32>;
+  auto kern = k_gemm_smallm<KS, RT, SPW, NS, G32>;
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -338,7 +315,7 @@ hipError_t launch_sm(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32
     configured = true;
   }
   const uint32_t blocks = (w.N + 16u * RT - 1u) / (16u * RT);
-  const size_t lds = smallm_lds_bytes<KS, RT, SPW>(w.K, w.gs);
+  const size_t lds = smallm_lds_bytes<KS, RT, SPW, NS>(w.K, w.gs);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * KS), lds, stream,
                      reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m,
                      (uint32_t)__builtin_ctz(w.gs));
@@ -348,17 +325,21 @@ hipError_t launch_sm(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32
 }  // namespace
 
 // Launch shapes (ks waves per workgroup, rt tiles of 16 rows, spw steps of 64
-// codes per wave per block).  Shape 0: 4/2/1 (many rows: two tiles share each
-// X block); shape 1: 16/1/1 (few rows, long K: more waves per tile); shape 2:
-// 8/1/1; shape 3: 4/1/2.
+// codes per wave per block, ns LDS block buffers).  Shape 0: 4/2/1/3 (many
+// rows: two tiles share each X block); shape 1: 16/1/1/3 (few rows, long K:
+// more waves per tile); shape 2: 8/1/1/3; shape 3: 4/1/2/3.
 constexpr int kSmShapes = 4;
+#define INT8W_SM_SHAPE0 4, 2, 1, 3
+#define INT8W_SM_SHAPE1 16, 1, 1, 3
+#define INT8W_SM_SHAPE2 8, 1, 1, 3
+#define INT8W_SM_SHAPE3 4, 1, 2, 3
 
 size_t smallm_shape_lds(int shape, uint32_t K, uint32_t gs) {
   switch (shape) {
-    case 0: return smallm_lds_bytes<4, 2, 1>(K, gs);
-    case 1: return smallm_lds_bytes<16, 1, 1>(K, gs);
-    case 2: return smallm_lds_bytes<8, 1, 1>(K, gs);
-    default: return smallm_lds_bytes<4, 1, 2>(K, gs);
+    case 0: return smallm_lds_bytes<INT8W_SM_SHAPE0>(K, gs);
+    case 1: return smallm_lds_bytes<INT8W_SM_SHAPE1>(K, gs);
+    case 2: return smallm_lds_bytes<INT8W_SM_SHAPE2>(K, gs);
+    default: return smallm_lds_bytes<INT8W_SM_SHAPE3>(K, gs);
   }
 }
 
@@ -385,10 +366,10 @@ hipError_t launch_gemm_smallm_shape(int shape, const WeightView &w, const uint16
                                     hipStream_t stream) {
   const bool g32 = w.gs == 32;
   switch (shape) {
-    case 0: return g32 ? launch_sm<4, 2, 1, kSmDepth, true>(w, X, Y, m, stream) : launch_sm<4, 2, 1, kSmDepth, false>(w, X, Y, m, stream);
-    case 1: return g32 ? launch_sm<16, 1, 1, kSmDepth, true>(w, X, Y, m, stream) : launch_sm<16, 1, 1, kSmDepth, false>(w, X, Y, m, stream);
-    case 2: return g32 ? launch_sm<8, 1, 1, kSmDepth, true>(w, X, Y, m, stream) : launch_sm<8, 1, 1, kSmDepth, false>(w, X, Y, m, stream);
-    default: return g32 ? launch_sm<4, 1, 2, kSmDepth, true>(w, X, Y, m, stream) : launch_sm<4, 1, 2, kSmDepth, false>(w, X, Y, m, stream);
+    case 0: return g32 ? launch_sm<INT8W_SM_SHAPE0, true>(w, X, Y, m, stream) : launch_sm<INT8W_SM_SHAPE0, false>(w, X, Y, m, stream);
+    case 1: return g32 ? launch_sm<INT8W_SM_SHAPE1, true>(w, X, Y, m, stream) : launch_sm<INT8W_SM_SHAPE1, false>(w, X, Y, m, stream);
+    case 2: return g32 ? launch_sm<INT8W_SM_SHAPE2, true>(w, X, Y, m, stream) : launch_sm<INT8W_SM_SHAPE2, false>(w, X, Y, m, stream);
+    default: return g32 ? launch_sm<INT8W_SM_SHAPE3, true>(w, X, Y, m, stream) : launch_sm<INT8W_SM_SHAPE3, false>(w, X, Y, m, stream);
   }
 }
 
