@@ -289,6 +289,7 @@ def test_gemm_prefill_small(m, N, K, gs):
     (300, 24000, 1536, 64),   # three blocks of 8 steps, last column tile half full
     (1030, 6500, 2048, 32),   # eight blocks of 4 steps
     (700, 9000, 512, 64),     # a single block, K of 8 steps
+    (1100, 7643, 512, 64),    # 300 full tiles: the last 9 column tiles as ragged half-height tiles
 ])
 def test_gemm_prefill_staged_sampled_rows(m, N, K, gs):
     """Shapes that take the DMA-staged 256 x 128 kernel (enough tiles, K a
@@ -302,7 +303,7 @@ def test_gemm_prefill_staged_sampled_rows(m, N, K, gs):
     _sync()
     Yb = dev_to_bits(Y)
     tail = np.arange((m // 256) * 256, m)
-    rows = np.unique(np.concatenate([[0, 255, m - 1], tail[:: max(1, len(tail) // 8)],
+    rows = np.unique(np.concatenate([[0, 127, 128, 255, m - 1], tail[:: max(1, len(tail) // 8)],
                                      np.random.default_rng(m + N).choice(m, 16, replace=False)]))
     Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X[rows])
     assert_close(Yb[rows], Y_ref, A, f"gemm m={m} {N}x{K} gs{gs} rows {rows.tolist()[:6]}...")

@@ -33,6 +33,8 @@
 //    at m = 2048, MFMA busy 30 % before).  k_gemm_prefill_dma (the usual
 //    case, K % (8 gs) == 0) stages X and the scales/biases by DMA over three
 //    LDS stages; k_gemm_prefill_ws (any K) loads through registers.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -409,7 +411,8 @@ template <int BM, int BN, int WGM, int WGN, int NP>
 __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ X, uint16_t *__restrict__ Y,
-    uint32_t N, uint32_t K, uint32_t m, uint32_t gs_log2, uint32_t mtiles, uint32_t nwork) {
+    uint32_t N, uint32_t K, uint32_t m, uint32_t gs_log2, uint32_t mtiles, uint32_t nbig, uint32_t mt_half,
+    uint32_t nt_big, uint32_t nwork) {
   constexpr int kMma = WGM * WGN;          // MFMA waves
   constexpr int kPT = 64 * NP;             // producer threads
   constexpr int XR = kPT / 8;              // X rows per producer pass
@@ -426,10 +429,28 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
   auto stage = [&](uint32_t i) { return lds_pf + i * kStage; };
   auto next3 = [](uint32_t i) { return i == 2u ? 0u : i + 1u; };
 
+  // Work items: nbig tiles of BM x BN (N tiles 0 .. nt_big - 1), then tiles of
+  // BM/2 x BN for the remaining N tiles.  The half tiles are dispatched last,
+  // so that a grid of 3.5 rounds of full tiles ends in one round of half tiles
+  // instead of half a round of full ones.  Within each kind, consecutive
+  // items (the M tiles of one N tile) stay on one XCD.
   uint32_t bid = blockIdx.x;
-  if (nwork % kXcds == 0) bid = (bid % kXcds) * (nwork / kXcds) + bid / kXcds;
-  const uint32_t mt = bid % mtiles, nt = bid / mtiles;
-  const uint32_t m0 = mt * BM, n0 = nt * BN;
+  bool half;
+  uint32_t m0, n0;
+  if (bid < nbig) {
+    if (nbig % kXcds == 0) bid = (bid % kXcds) * (nbig / kXcds) + bid / kXcds;
+    half = false;
+    m0 = (bid % mtiles) * BM;
+    n0 = (bid / mtiles) * BN;
+  } else {
+    uint32_t h = bid - nbig;
+    const uint32_t nh = nwork - nbig;
+    if (nh % kXcds == 0) h = (h % kXcds) * (nh / kXcds) + h / kXcds;
+    half = true;
+    m0 = (h % mt_half) * (BM / 2);
+    n0 = (nt_big + h / mt_half) * BN;
+  }
+  const uint32_t tile_rows = half ? (uint32_t)BM / 2u : (uint32_t)BM;
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u, wave = uniform_pf(tid >> 6);
   const uint32_t ksteps = (K + BK - 1) / BK;
@@ -438,133 +459,160 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
     // ---------------- producer waves
     const uint32_t ptid = tid - 64u * kMma;
     const uint32_t G = K >> gs_log2;
-    const uint32_t mrows = m - m0 < (uint32_t)BM ? m - m0 : (uint32_t)BM;
+    const uint32_t mrows = m - m0 < tile_rows ? m - m0 : tile_rows;
     const uint32_t nrows = N - n0 < (uint32_t)BN ? N - n0 : (uint32_t)BN;
     const auto rx = make_rsrc(X + (size_t)m0 * K, mrows * K * 2u);
     const auto rw = make_rsrc(codes + (size_t)n0 * K, nrows * K);
     const auto rs = make_rsrc(scales + (size_t)n0 * G, nrows * G * 2u);
     const auto rb = make_rsrc(biases + (size_t)n0 * G, nrows * G * 2u);
     const uint32_t wr = ptid >> 2, wp = ptid & 3u;
-    // X by DMA: one instruction fills 8 LDS rows (1 KiB, lane i -> byte 16 i);
-    // lane i carries row r0 + i / 8 and, through the swizzle, logical chunk
-    // (i % 8) ^ (i / 8).  Producer wave pw fills rows 8 (j NP + pw) .. + 7.
-    constexpr int XJ = BM / (8 * NP);
-    const uint32_t pw = wave - (uint32_t)kMma, plane = lane;
-    const uint32_t xchunk = (plane & 7u) ^ (plane >> 3);
-    uint32_t vxd[XJ];
+    // The producer schedule, for XJN X loads per wave and step (the wait
+    // counts below are compile-time immediates, hence a template).
+    auto run = [&](auto xjn) {
+      constexpr int XJN = decltype(xjn)::value;
+      // X by DMA: one instruction fills 8 LDS rows (1 KiB, lane i -> byte 16 i);
+      // lane i carries row r0 + i / 8 and, through the swizzle, logical chunk
+      // (i % 8) ^ (i / 8).  Producer wave pw fills rows 8 (j NP + pw) .. + 7.
+      constexpr int XJ = XJN;  // X loads per wave and step (half for a half tile)
+      const uint32_t pw = wave - (uint32_t)kMma, plane = lane;
+      const uint32_t xchunk = (plane & 7u) ^ (plane >> 3);
+      uint32_t vxd[XJ];
 #pragma unroll
-    for (int j = 0; j < XJ; ++j) {
-      const uint32_t row = (j * NP + pw) * 8u + (plane >> 3);
-      vxd[j] = row < mrows ? row * K * 2u + xchunk * 16u : kOutOfRange;
-    }
-    auto xdma = [&](uint32_t ks, uint32_t st) {
-      const bool live = ks < ksteps;
-      const uint32_t k0 = live ? ks * BK : 0u;
-      const bool xin = live && k0 + xchunk * 8u < K;
+      for (int j = 0; j < XJ; ++j) {
+        const uint32_t row = (j * NP + pw) * 8u + (plane >> 3);
+        vxd[j] = row < mrows ? row * K * 2u + xchunk * 16u : kOutOfRange;
+      }
+      auto xdma = [&](uint32_t ks, uint32_t st) {
+        const bool live = ks < ksteps;
+        const uint32_t k0 = live ? ks * BK : 0u;
+        const bool xin = live && k0 + xchunk * 8u < K;
 #pragma unroll
-      for (int j = 0; j < XJ; ++j)
+        for (int j = 0; j < XJ; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rx, (__attribute__((address_space(3))) void *)(stage(st) + (j * NP + pw) * 8u * (BK * 2)), 16,
+              (int)(xin ? vxd[j] : kOutOfRange), (int)uniform_pf(2u * k0), 0, 0);
+      };
+      // Scales and biases by DMA, a block of 8 groups (8 gs codes, gs / 8
+      // steps) at a time, double-buffered: wave pw copies 16 bytes per row for
+      // rows 64 (pw % 2) .. + 63 of the scales (pw < 2) or biases (pw >= 2).
+      // Needs K % (8 gs) == 0, so that every row's block is 16 whole bytes.
+      const uint32_t sbs_log2 = gs_log2 - 3u;  // steps per block, log2
+      const uint32_t nblk = K >> (gs_log2 + 3u);
+      auto sbuf = [&](uint32_t i) { return lds_pf + 3u * kStage + i * kSbBytes; };
+      const uint32_t sbrow = (pw & 1u) * 64u + plane;
+      const uint32_t vsbd = sbrow < nrows ? sbrow * G * 2u : kOutOfRange;
+      auto sbdma = [&](uint32_t blk) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rx, (__attribute__((address_space(3))) void *)(stage(st) + (j * NP + pw) * 8u * (BK * 2)), 16,
-            (int)(xin ? vxd[j] : kOutOfRange), (int)uniform_pf(2u * k0), 0, 0);
-    };
-    // Scales and biases by DMA, a block of 8 groups (8 gs codes, gs / 8
-    // steps) at a time, double-buffered: wave pw copies 16 bytes per row for
-    // rows 64 (pw % 2) .. + 63 of the scales (pw < 2) or biases (pw >= 2).
-    // Needs K % (8 gs) == 0, so that every row's block is 16 whole bytes.
-    const uint32_t sbs_log2 = gs_log2 - 3u;  // steps per block, log2
-    const uint32_t nblk = K >> (gs_log2 + 3u);
-    auto sbuf = [&](uint32_t i) { return lds_pf + 3u * kStage + i * kSbBytes; };
-    const uint32_t sbrow = (pw & 1u) * 64u + plane;
-    const uint32_t vsbd = sbrow < nrows ? sbrow * G * 2u : kOutOfRange;
-    auto sbdma = [&](uint32_t blk) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            pw >= 2u ? rb : rs,
-            (__attribute__((address_space(3))) void *)(sbuf(blk & 1u) + (pw >> 1) * (BN * 16u) + (pw & 1u) * 1024u),
-            16, (int)vsbd, (int)uniform_pf(blk * 16u), 0, 0);
-    };
-    uint32_t vw[WP];
-#pragma unroll
-    for (int p = 0; p < WP; ++p) {
-      const uint32_t row = p * WR + wr;
-      vw[p] = row < nrows ? row * K + wp * 16u : kOutOfRange;
-    }
-    struct Regs {
-      u32x4 w[WP];
-    };
-    auto issue = [&](Regs &r, uint32_t ks) {
-      const bool live = ks < ksteps;
-      const uint32_t k0 = live ? ks * BK : 0u;
-      const bool win = live && k0 + wp * 16u < K;
-#pragma unroll
-      for (int p = 0; p < WP; ++p)
-        r.w[p] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(win ? vw[p] : kOutOfRange), (int)uniform_pf(k0),
-                                                       kAuxNontemporal);
-    };
-    auto store = [&](const Regs &r, uint8_t *buf, uint32_t ks) {
-      uint8_t *ws = buf + BM * BK * 2;
-      const uint8_t *sb = sbuf((ks >> sbs_log2) & 1u);
-      const uint32_t g = ((ks * BK + wp * 16u) >> gs_log2) & 7u;
+              pw >= 2u ? rb : rs,
+              (__attribute__((address_space(3))) void *)(sbuf(blk & 1u) + (pw >> 1) * (BN * 16u) + (pw & 1u) * 1024u),
+              16, (int)vsbd, (int)uniform_pf(blk * 16u), 0, 0);
+      };
+      uint32_t vw[WP];
 #pragma unroll
       for (int p = 0; p < WP; ++p) {
-        const uint32_t srow = p * WR + wr;
-        const float sc = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + srow * 16u + 2u * g));
-        const float bi = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + BN * 16u + srow * 16u + 2u * g));
-        const uint32_t word[4] = {r.w[p].x, r.w[p].y, r.w[p].z, r.w[p].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[2 * i] = pack_bf16x2(__builtin_fmaf(code_f32(word[i], 0), sc, bi), __builtin_fmaf(code_f32(word[i], 1), sc, bi));
-          o[2 * i + 1] =
-              pack_bf16x2(__builtin_fmaf(code_f32(word[i], 2), sc, bi), __builtin_fmaf(code_f32(word[i], 3), sc, bi));
-        }
         const uint32_t row = p * WR + wr;
-        *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp)) = u32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp + 1u)) = u32x4{o[4], o[5], o[6], o[7]};
+        vw[p] = row < nrows ? row * K + wp * 16u : kOutOfRange;
       }
-    };
-    // vmcnt(n) with expcnt and lgkmcnt left open
+      struct Regs {
+        u32x4 w[WP];
+      };
+      auto issue = [&](Regs &r, uint32_t ks) {
+        const bool live = ks < ksteps;
+        const uint32_t k0 = live ? ks * BK : 0u;
+        const bool win = live && k0 + wp * 16u < K;
+#pragma unroll
+        for (int p = 0; p < WP; ++p)
+          r.w[p] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(win ? vw[p] : kOutOfRange), (int)uniform_pf(k0),
+                                                         kAuxNontemporal);
+      };
+      auto store = [&](const Regs &r, uint8_t *buf, uint32_t ks) {
+        uint8_t *ws = buf + BM * BK * 2;
+        const uint8_t *sb = sbuf((ks >> sbs_log2) & 1u);
+        const uint32_t g = ((ks * BK + wp * 16u) >> gs_log2) & 7u;
+        // every pass's scale and bias first: one LDS round trip, not one per
+        // pass (the stores below could alias them as far as the compiler knows)
+        float scv[WP], biv[WP];
+#pragma unroll
+        for (int p = 0; p < WP; ++p) {
+          const uint32_t srow = p * WR + wr;
+          scv[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + srow * 16u + 2u * g));
+          biv[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + BN * 16u + srow * 16u + 2u * g));
+        }
+#pragma unroll
+        for (int p = 0; p < WP; ++p) {
+          const float sc = scv[p], bi = biv[p];
+          const uint32_t word[4] = {r.w[p].x, r.w[p].y, r.w[p].z, r.w[p].w};
+          uint32_t o[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[2 * i] = pack_bf16x2(__builtin_fmaf(code_f32(word[i], 0), sc, bi), __builtin_fmaf(code_f32(word[i], 1), sc, bi));
+            o[2 * i + 1] =
+                pack_bf16x2(__builtin_fmaf(code_f32(word[i], 2), sc, bi), __builtin_fmaf(code_f32(word[i], 3), sc, bi));
+          }
+          const uint32_t row = p * WR + wr;
+          *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp)) = u32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp + 1u)) = u32x4{o[4], o[5], o[6], o[7]};
+        }
+      };
+      // vmcnt(n) with expcnt and lgkmcnt left open
 #define INT8W_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
-    Regs R0, R1, R2;
-    // Iteration k (between barriers k - 1 and k): the X DMA of step k + 2
-    // goes to stage (k + 2) % 3 (it held step k - 1, read before barrier
-    // k - 1); step k + 1's weights are dequantized into stage (k + 1) % 3;
-    // step k + 4's codes are requested; and the X DMA of step k + 1, issued
-    // one iteration earlier, is awaited.  Barrier k thus publishes step k + 1
-    // and every X DMA has two iterations to land.
-    sbdma(0u);
-    if (1u < nblk) sbdma(1u);
-    issue(R0, 0);
-    issue(R1, 1);
-    issue(R2, 2);
-    xdma(0u, 0u);
-    xdma(1u, 1u);
-    INT8W_VMCNT(3 * WP + 2 * XJ);  // scale/bias blocks 0 and 1 have landed
-    __syncthreads();  // ... for every producer wave
-    store(R0, stage(0u), 0u);
-    issue(R0, 3);
-    INT8W_VMCNT(XJ + WP);  // the X DMA of step 0 has landed
-    __syncthreads();  // step 0 is in LDS
-    auto step = [&](Regs &r, uint32_t k, uint32_t sx, uint32_t sw) {
-      const uint32_t s = k + 1u;
-      xdma(k + 2u, sx);
-      store(r, stage(sw), s);
-      issue(r, k + 4u);
-      // at the first step of scale/bias block b, block b + 1 goes into the
-      // buffer that held block b - 1
-      if (s != 0u && (s & ((1u << sbs_log2) - 1u)) == 0u && (s >> sbs_log2) + 1u < nblk) sbdma((s >> sbs_log2) + 1u);
-      INT8W_VMCNT(XJ + 2 * WP);  // the X DMA of step k + 1 has landed
-      __syncthreads();
-    };
+      // vmcnt(n) and lgkmcnt(0)
+#define INT8W_VMCNT_LGKM0(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0070 | ((n) & 15))
+      Regs R0, R1, R2;
+      // Iteration k (between barriers k - 1 and k): the X DMA of step k + 2
+      // goes to stage (k + 2) % 3 (it held step k - 1, read before barrier
+      // k - 1); step k + 1's weights are dequantized into stage (k + 1) % 3;
+      // step k + 4's codes are requested; and the X DMA of step k + 1, issued
+      // one iteration earlier, is awaited.  Barrier k thus publishes step k + 1
+      // and every X DMA has two iterations to land.
+      sbdma(0u);
+      if (1u < nblk) sbdma(1u);
+      issue(R0, 0);
+      issue(R1, 1);
+      issue(R2, 2);
+      xdma(0u, 0u);
+      xdma(1u, 1u);
+      INT8W_VMCNT(3 * WP + 2 * XJ);  // scale/bias blocks 0 and 1 have landed
+      __syncthreads();  // ... for every producer wave
+      store(R0, stage(0u), 0u);
+      issue(R0, 3);
+      INT8W_VMCNT(XJ + WP);  // the X DMA of step 0 has landed
+      __syncthreads();  // step 0 is in LDS
+      auto step = [&](Regs &r, uint32_t k, uint32_t sx, uint32_t sw) {
+        const uint32_t s = k + 1u;
+        xdma(k + 2u, sx);
+        store(r, stage(sw), s);
+        issue(r, k + 4u);
+        // at the first step of scale/bias block b, block b + 1 goes into the
+        // buffer that held block b - 1
+        if (s != 0u && (s & ((1u << sbs_log2) - 1u)) == 0u && (s >> sbs_log2) + 1u < nblk) sbdma((s >> sbs_log2) + 1u);
+        // The X DMA of step k + 1 has landed and this wave's LDS stores are
+        // done; then a bare barrier.  A fenced barrier would also wait for
+        // every load still in flight -- step k + 2's X and the codes of step
+        // k + 4 -- and so expose their latency on every step.  (A scale/bias
+        // block requested here is older than step k + 3's X, so the wait two
+        // iterations on covers it, before its first reader, gs / 8 >= 4
+        // steps on.)
+        INT8W_VMCNT_LGKM0(XJ + 2 * WP);
+        asm volatile("s_barrier" ::: "memory");
+      };
 #undef INT8W_VMCNT
-    for (uint32_t k = 0;;) {
-      if (k + 1u >= ksteps) break;
-      step(R1, k, 2u, 1u);
-      if (++k + 1u >= ksteps) break;
-      step(R2, k, 0u, 2u);
-      if (++k + 1u >= ksteps) break;
-      step(R0, k, 1u, 0u);
-      ++k;
-    }
+#undef INT8W_VMCNT_LGKM0
+      for (uint32_t k = 0;;) {
+        if (k + 1u >= ksteps) break;
+        step(R1, k, 2u, 1u);
+        if (++k + 1u >= ksteps) break;
+        step(R2, k, 0u, 2u);
+        if (++k + 1u >= ksteps) break;
+        step(R0, k, 1u, 0u);
+        ++k;
+      }
+
+    };
+    if (half)
+      run(std::integral_constant<int, BM / (16 * NP)>{});
+    else
+      run(std::integral_constant<int, BM / (8 * NP)>{});
     return;
   }
 
@@ -598,6 +646,12 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
   bf16x8 a[TI], b[TJ];
   __syncthreads();  // the producers' scale/bias staging
   __syncthreads();  // step 0 is in LDS
+  // on a half tile the waves of the lower rows have nothing to multiply (but
+  // keep the barrier count)
+  if (wm * (uint32_t)WTM >= tile_rows) {
+    for (uint32_t k = 1; k < ksteps; ++k) __syncthreads();
+    return;
+  }
   uint32_t s = 0;
   for (uint32_t k = 0;;) {
     load_frags(a, b, stage(s), 0u);
@@ -636,11 +690,24 @@ hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, 
   }
   const uint32_t mtiles = (m + BM - 1) / BM;
   const uint32_t ntiles = (w.N + BN - 1) / BN;
-  const uint32_t nwork = mtiles * ntiles;
+  // When the full tiles leave a last round at most half full, the N tiles of
+  // that round are done as half-height tiles (twice as many, about half the
+  // time each) in one last round.
+  const uint32_t cus = (uint32_t)device_cu_count();
+  const uint32_t full = mtiles * ntiles, rem = full % cus;
+  uint32_t nt_half = 0;
+  if (full > cus && rem != 0 && 2u * rem <= cus) {
+    nt_half = (rem + mtiles - 1) / mtiles;
+    if (nt_half >= ntiles) nt_half = 0;
+  }
+  const uint32_t nt_big = ntiles - nt_half;
+  const uint32_t mt_half = (m + BM / 2 - 1) / (BM / 2);
+  const uint32_t nbig = mtiles * nt_big;
+  const uint32_t nwork = nbig + mt_half * nt_half;
   const size_t lds = 3u * (BM + BN) * BK * 2u + BN * 16u * 2u * 2u;
   hipLaunchKernelGGL(kern, dim3(nwork), dim3(64 * (WGM * WGN + NP)), lds, stream,
                      reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m,
-                     (uint32_t)__builtin_ctz(w.gs), mtiles, nwork);
+                     (uint32_t)__builtin_ctz(w.gs), mtiles, nbig, mt_half, nt_big, nwork);
   return hipGetLastError();
 }
 
