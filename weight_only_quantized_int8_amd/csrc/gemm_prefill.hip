@@ -525,22 +525,29 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
           r.w[p] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(win ? vw[p] : kOutOfRange), (int)uniform_pf(k0),
                                                          kAuxNontemporal);
       };
-      auto store = [&](const Regs &r, uint8_t *buf, uint32_t ks) {
-        uint8_t *ws = buf + BM * BK * 2;
+      // Every pass's scale and bias of step ks, read from LDS in one round
+      // trip before the step's DMA and stores are issued (the compiler keeps
+      // LDS reads behind LDS writes that might alias them).
+      struct SbVals {
+        float sc[WP], bi[WP];
+      };
+      auto read_sb = [&](uint32_t ks) {
+        SbVals v;
         const uint8_t *sb = sbuf((ks >> sbs_log2) & 1u);
         const uint32_t g = ((ks * BK + wp * 16u) >> gs_log2) & 7u;
-        // every pass's scale and bias first: one LDS round trip, not one per
-        // pass (the stores below could alias them as far as the compiler knows)
-        float scv[WP], biv[WP];
 #pragma unroll
         for (int p = 0; p < WP; ++p) {
           const uint32_t srow = p * WR + wr;
-          scv[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + srow * 16u + 2u * g));
-          biv[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + BN * 16u + srow * 16u + 2u * g));
+          v.sc[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + srow * 16u + 2u * g));
+          v.bi[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + BN * 16u + srow * 16u + 2u * g));
         }
+        return v;
+      };
+      auto store = [&](const Regs &r, uint8_t *buf, const SbVals &v) {
+        uint8_t *ws = buf + BM * BK * 2;
 #pragma unroll
         for (int p = 0; p < WP; ++p) {
-          const float sc = scv[p], bi = biv[p];
+          const float sc = v.sc[p], bi = v.bi[p];
           const uint32_t word[4] = {r.w[p].x, r.w[p].y, r.w[p].z, r.w[p].w};
           uint32_t o[8];
 #pragma unroll
@@ -574,14 +581,15 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
       xdma(1u, 1u);
       INT8W_VMCNT(3 * WP + 2 * XJ);  // scale/bias blocks 0 and 1 have landed
       __syncthreads();  // ... for every producer wave
-      store(R0, stage(0u), 0u);
+      store(R0, stage(0u), read_sb(0u));
       issue(R0, 3);
       INT8W_VMCNT(XJ + WP);  // the X DMA of step 0 has landed
       __syncthreads();  // step 0 is in LDS
       auto step = [&](Regs &r, uint32_t k, uint32_t sx, uint32_t sw) {
         const uint32_t s = k + 1u;
+        const SbVals v = read_sb(s);
         xdma(k + 2u, sx);
-        store(r, stage(sw), s);
+        store(r, stage(sw), v);
         issue(r, k + 4u);
         // at the first step of scale/bias block b, block b + 1 goes into the
         // buffer that held block b - 1
