@@ -46,23 +46,25 @@ __device__ __forceinline__ uint32_t quant_code(float v, float b, float s) {
 // t = (v - b) * rcp(s) serves where it is clearly on one side of one: rcp is
 // within 1 ulp and the product within half an ulp, so for quotients below 256
 // t is within 2^-14 of the correctly rounded quotient, and a t farther than
-// 2^-13 from every half-integer gives the same code.  Returns true when some
-// code needs the IEEE division (t near a half-integer, or not finite).
-// v - b >= 0 (b is the group's minimum), so codes are only clamped at 255.
-__device__ __forceinline__ bool quant_codes_fast(const float (&f)[8], float b, float s, uint32_t &q0, uint32_t &q1) {
+// 2^-13 from every half-integer gives the same code.  Returns a mask of the
+// codes (bit i for code i) that need the IEEE division (t near a
+// half-integer, or not finite).  v - b >= 0 (b is the group's minimum), so
+// codes are only clamped at 255.
+__device__ __forceinline__ uint32_t quant_codes_fast(const float (&f)[8], float b, float s, uint32_t &q0,
+                                                     uint32_t &q1) {
   const float rs = __builtin_amdgcn_rcpf(s);
-  bool near = false;
+  uint32_t near = 0u;
   uint32_t w[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float t = (f[i] - b) * rs;
     const float r = __builtin_rintf(t);
-    near |= !(__builtin_fabsf(t - r) < 0.5f - 0x1p-13f);
+    near |= __builtin_fabsf(t - r) < 0.5f - 0x1p-13f ? 0u : (1u << i);
     w[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fminf(r, 255.0f), i & 3, w[i >> 2]);
   }
   q0 = w[0];
   q1 = w[1];
-  return near && s != 0.0f;
+  return s != 0.0f ? near : 0u;
 }
 
 template <int U>
@@ -133,15 +135,24 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(const uint16_t *__restri
         const uint16_t b_bits = to_bf16_bits(lo);  // exact
         const float s = bf16_bits_to_f32(s_bits), b = bf16_bits_to_f32(b_bits);
         uint32_t q0, q1;
-        const bool near = quant_codes_fast(f, b, s, q0, q1);
+        const uint32_t near = quant_codes_fast(f, b, s, q0, q1);
         if (s == 0.0f) q0 = q1 = 0u;
-        if (__builtin_amdgcn_ballot_w64(near) != 0u) {  // wave-uniform: rare
-          if (near) {
-            q0 = q1 = 0u;
+        // The IEEE division, per code position, only where some lane of the
+        // wave needs it there (each test is wave-uniform; usually none does,
+        // and when one does it is usually one position of one lane).
+        if (__builtin_amdgcn_ballot_w64(near != 0u) != 0u) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              q0 |= quant_code(f[i], b, s) << (8 * i);
-              q1 |= quant_code(f[4 + i], b, s) << (8 * i);
+          for (int i = 0; i < 8; ++i) {
+            const bool here = (near >> i) & 1u;
+            if (__builtin_amdgcn_ballot_w64(here) != 0u) {
+              if (here) {
+                const uint32_t c = quant_code(f[i], b, s) << (8 * (i & 3));
+                const uint32_t keep = ~(0xFFu << (8 * (i & 3)));
+                if (i < 4)
+                  q0 = (q0 & keep) | c;
+                else
+                  q1 = (q1 & keep) | c;
+              }
             }
           }
         }
