@@ -290,11 +290,13 @@ def test_gemm_prefill_small(m, N, K, gs):
     (1030, 6500, 2048, 32),   # eight blocks of 4 steps
     (700, 9000, 512, 64),     # a single block, K of 8 steps
     (1100, 7643, 512, 64),    # 300 full tiles: the last 9 column tiles as ragged half-height tiles
+    (600, 3790, 1024, 64),    # 128 x 64 staged tiles, 300 of them: the last 9 columns as half-height tiles
+    (200, 2000, 2048, 32),    # 128 x 64 staged tiles, ragged rows and columns
 ])
 def test_gemm_prefill_staged_sampled_rows(m, N, K, gs):
-    """Shapes that take the DMA-staged 256 x 128 kernel (enough tiles, K a
-    multiple of 8 group sizes), compared on sampled rows including the last
-    (ragged) row tile."""
+    """Shapes that take the DMA-staged kernel (K a multiple of 8 group sizes;
+    256 x 128 tiles when there are enough of them, else 128 x 64), compared on
+    sampled rows including the last (ragged) row tile."""
     log(f"gemm prefill staged m={m} N={N} K={K} gs={gs}")
     w, rng = make_weight(3_700 + m + N + K, N, K, gs)
     X = synth.gen_act(rng, (m, K))
@@ -305,6 +307,7 @@ def test_gemm_prefill_staged_sampled_rows(m, N, K, gs):
     tail = np.arange((m // 256) * 256, m)
     rows = np.unique(np.concatenate([[0, 127, 128, 255, m - 1], tail[:: max(1, len(tail) // 8)],
                                      np.random.default_rng(m + N).choice(m, 16, replace=False)]))
+    rows = rows[rows < m]
     Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X[rows])
     assert_close(Yb[rows], Y_ref, A, f"gemm m={m} {N}x{K} gs{gs} rows {rows.tolist()[:6]}...")
     assert np.isfinite(oracle.bf16_to_f32(Yb)).all()

@@ -422,7 +422,8 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TI = WTM / 16, TJ = WTN / 16;
   static_assert(XP >= 1 && WP >= 1 && BM % XR == 0 && BN % WR == 0, "whole load passes");
-  static_assert(BN == 128 && NP == 4, "scale/bias staging: 4 waves x 64 lanes cover 128 rows x {scales, biases}");
+  constexpr uint32_t kSbW = BN / 64;  // waves per array in the scale/bias DMA (64 rows each)
+  static_assert(BN % 64 == 0 && 2 * (BN / 64) <= NP, "scale/bias staging: 64 rows of scales or biases per wave");
   constexpr uint32_t kStage = (BM + BN) * BK * 2;
   constexpr uint32_t kSbBytes = BN * 16u * 2u;  // one block: 8 groups of scales and of biases per row
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_pf[];
@@ -494,17 +495,19 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
       };
       // Scales and biases by DMA, a block of 8 groups (8 gs codes, gs / 8
       // steps) at a time, double-buffered: wave pw copies 16 bytes per row for
-      // rows 64 (pw % 2) .. + 63 of the scales (pw < 2) or biases (pw >= 2).
+      // rows 64 (pw % kSbW) .. + 63 of the scales (pw < kSbW) or biases.
       // Needs K % (8 gs) == 0, so that every row's block is 16 whole bytes.
       const uint32_t sbs_log2 = gs_log2 - 3u;  // steps per block, log2
       const uint32_t nblk = K >> (gs_log2 + 3u);
       auto sbuf = [&](uint32_t i) { return lds_pf + 3u * kStage + i * kSbBytes; };
-      const uint32_t sbrow = (pw & 1u) * 64u + plane;
+      const uint32_t sbrow = (pw % kSbW) * 64u + plane;
       const uint32_t vsbd = sbrow < nrows ? sbrow * G * 2u : kOutOfRange;
       auto sbdma = [&](uint32_t blk) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              pw >= 2u ? rb : rs,
-              (__attribute__((address_space(3))) void *)(sbuf(blk & 1u) + (pw >> 1) * (BN * 16u) + (pw & 1u) * 1024u),
+        if (pw < 2u * kSbW)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              pw >= kSbW ? rb : rs,
+              (__attribute__((address_space(3))) void *)(sbuf(blk & 1u) + (pw / kSbW) * (BN * 16u) +
+                                                         (pw % kSbW) * 1024u),
               16, (int)vsbd, (int)uniform_pf(blk * 16u), 0, 0);
       };
       uint32_t vw[WP];
@@ -762,7 +765,8 @@ hipError_t launch_tile(const WeightView &w, const uint16_t *X, uint16_t *Y, uint
 
 // Tile shapes (BM x BN, waves): 0 = 128 x 128 (2 x 2), 1 = 128 x 64 (2 x 2),
 // 2 = 256 x 128 (4 x 2 MFMA waves + 8 producer waves), 3 = 256 x 128 staged
-// by DMA (4 x 2 MFMA waves + 4 producer waves; K % (8 gs) == 0).
+// by DMA (4 x 2 MFMA waves + 4 producer waves; K % (8 gs) == 0), 4 = 128 x 64
+// staged by DMA (2 x 2 MFMA waves + 4 producer waves; K % (8 gs) == 0).
 hipError_t launch_gemm_prefill_tile(int t, const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                                     hipStream_t stream) {
   switch (t) {
@@ -771,19 +775,26 @@ hipError_t launch_gemm_prefill_tile(int t, const WeightView &w, const uint16_t *
     case 3:
       if (w.K % (8u * w.gs) != 0u) return hipErrorInvalidValue;
       return launch_tile_dma<256, 128, 4, 2, 4>(w, X, Y, m, stream);
+    case 4:
+      if (w.K % (8u * w.gs) != 0u) return hipErrorInvalidValue;
+      return launch_tile_dma<128, 64, 2, 2, 4>(w, X, Y, m, stream);
     default: return launch_tile<128, 128, 2, 2>(w, X, Y, m, stream);
   }
 }
 
 hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                                hipStream_t stream) {
-  // Measured on MI355X: 256 x 128 tiles over 8 waves when they give at least
-  // ~3/4 of a tile per CU, else 128 x 128, else 128 x 64 (fewer idle CUs).
+  // Measured on MI355X: 256 x 128 tiles when they give at least ~3/4 of a
+  // tile per CU, else 128 x 128, else 128 x 64 (fewer idle CUs); staged by DMA
+  // where K allows (the 128 x 64 staged tiles: m = 512 on 4096 x 14336 in
+  // 107 us against 135 us unstaged).
   const uint32_t cus = (uint32_t)device_cu_count();
   const uint32_t t256 = ((m + 255u) / 256u) * ((w.N + 127u) / 128u);
   const uint32_t t128 = ((m + 127u) / 128u) * ((w.N + 127u) / 128u);
-  const int big = w.K % (8u * w.gs) == 0u ? 3 : 2;
-  const int shape = 4u * t256 >= 3u * cus ? big : (4u * t128 >= 3u * cus ? 0 : 1);
+  const bool staged = w.K % (8u * w.gs) == 0u;
+  const int shape = 4u * t256 >= 3u * cus ? (staged ? 3 : 2)
+                    : 4u * t128 >= 3u * cus ? 0
+                    : staged ? 4 : 1;
   return launch_gemm_prefill_tile(shape, w, X, Y, m, stream);
 }
 
