@@ -195,7 +195,10 @@ int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const
  * both contiguous row-major.  Y[i,n] = RNE_bf16(sum_k w[n,k] * X[i,k]) with fp32
  * accumulation; for m > 16 the weight enters the matrix cores as
  * RNE_bf16(w[n,k]) (the dequantize_to value).  m == 0 enqueues nothing and
- * returns INT8W_OK. */
+ * returns INT8W_OK.  INT8W_ERR_SHAPE also when m * in_features or
+ * m * out_features exceeds 2^32 - 1, or when in_features >= 2^23 for an m
+ * that takes the tiled kernel (m > 16, or an m >= 2 whose scale/bias rows do
+ * not fit the small-m kernel's LDS). */
 int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, uint64_t stream);
 
 /* Human-readable description of the calling thread's most recent error

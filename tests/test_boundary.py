@@ -136,6 +136,12 @@ def test_gemm_m_zero_is_a_no_op():
     assert B.int8_gemm(desc(), 0, 0, 0, 0) == B.INT8W_OK
 
 
+def test_gemm_tiled_width_limit():
+    # a 256-row X tile of in_features = 2^23 would need 4 GiB of 32-bit offsets
+    rc, msg = err(B.int8_gemm(desc(N=64, K=1 << 23, gs=64), 4 * A16, 1 << 40, 17, 0))
+    assert rc == B.INT8W_ERR_SHAPE and "in_features" in msg
+
+
 def test_gemm_rows_times_width_limit():
     rc, msg = err(B.int8_gemm(desc(N=64, K=1 << 16, gs=64), 4 * A16, 1 << 40, 1 << 17, 0))
     assert rc == B.INT8W_ERR_SHAPE and "rows" in msg

@@ -338,6 +338,11 @@ int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m,
   const uint64_t K = w->in_features, N = w->out_features;
   if ((uint64_t)m * K > 0xFFFFFFFFull || (uint64_t)m * N > 0xFFFFFFFFull)
     return fail(INT8W_ERR_SHAPE, "m=%u rows too many for this weight", m);
+  // the tiled kernel addresses a 256-row X tile with 32-bit byte offsets
+  const bool tiled = m > 16u || (m > 1u && !smallm_supported(w->in_features, w->group_size));
+  if (tiled && K * 2u * 256u > 0xFFFFFFFFull)
+    return fail(INT8W_ERR_SHAPE, "in_features=%u above 2^23 - 1 needs m = 1 or a small-m shape (m=%u)",
+                w->in_features, m);
   Range ins[4];
   weight_ranges(w, ins);
   ins[3] = range("X", x, (uint64_t)m * K * 2);
