@@ -376,13 +376,15 @@ def test_every_entry_point_is_deterministic():
     r = bits_to_dev(synth.gen_act(rng, N))
     X4 = bits_to_dev(synth.gen_act(rng, (4, K)))
     X600 = bits_to_dev(synth.gen_act(rng, (600, K)))
+    X2048 = bits_to_dev(synth.gen_act(rng, (2048, K)))
     W = upload(w)
     calls = {
         "gemv": lambda: W.gemv(g),
         "silu_gate": lambda: W.gemv_silu_gate(g, u),
         "silu_gate_resid": lambda: W.gemv_silu_gate_resid(g, u, r),
         "gemm4": lambda: W.gemm(X4),
-        "gemm600": lambda: W.gemm(X600),
+        "gemm600": lambda: W.gemm(X600),    # 128 x 64 DMA-staged tiles
+        "gemm2048": lambda: W.gemm(X2048),  # 256 x 128 DMA-staged tiles
     }
     for name, f in calls.items():
         a = dev_to_bits(f())
