@@ -609,14 +609,20 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
       };
 #undef INT8W_VMCNT
 #undef INT8W_VMCNT_LGKM0
-      for (uint32_t k = 0;;) {
-        if (k + 1u >= ksteps) break;
+      // Steps 0 .. ksteps - 2, three to an iteration and the rest after the
+      // loop.  The loop has a single exit: with an exit after every step the
+      // compiler's wait counts at the loop head also cover the paths that
+      // leave, and it waited for every load in flight once per iteration.
+      const uint32_t nst = ksteps - 1u;
+      uint32_t k = 0;
+      for (; k + 3u <= nst; k += 3u) {
         step(R1, k, 2u, 1u);
-        if (++k + 1u >= ksteps) break;
-        step(R2, k, 0u, 2u);
-        if (++k + 1u >= ksteps) break;
-        step(R0, k, 1u, 0u);
-        ++k;
+        step(R2, k + 1u, 0u, 2u);
+        step(R0, k + 2u, 1u, 0u);
+      }
+      if (k < nst) {
+        step(R1, k, 2u, 1u);
+        if (k + 1u < nst) step(R2, k + 1u, 0u, 2u);
       }
 
     };
