@@ -120,15 +120,22 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(const uint8_t *__restric
   DqBlock<U> A, B;
   const uint32_t nblk = (nit + U - 1) / U;
   if (nblk) issue(A);
-  for (uint32_t b = 0; b < nblk;) {
-    if (b + 1 >= nblk) { consume(A); break; }
+  // two blocks per iteration and the rest after the loop: a single exit,
+  // so that the compiler's wait counts at the loop head do not also cover
+  // the paths that leave (with them it waited for the block just issued)
+  uint32_t b = 0;
+  for (; b + 2u < nblk; b += 2u) {
     issue(B);
     consume(A);
-    ++b;
-    if (b + 1 >= nblk) { consume(B); break; }
     issue(A);
     consume(B);
-    ++b;
+  }
+  if (b + 1u < nblk) {
+    issue(B);
+    consume(A);
+    consume(B);
+  } else if (b < nblk) {
+    consume(A);
   }
 }
 

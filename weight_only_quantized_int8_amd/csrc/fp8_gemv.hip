@@ -25,6 +25,8 @@
 //    (16 per 1 KiB segment) stay in its registers and a block scale is loaded
 //    with the codes, so a wave needs no LDS, no barrier and no staging before
 //    its first block (one block = one row, two rows in flight).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -275,16 +277,28 @@ __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__
       }
     }
     __syncthreads();
-    // 3. two-stage pipeline; the only branches are the loop exits
-    for (uint32_t b = 0; b < nblk;) {
-      if (b + 1 >= nblk) { consume(A); break; }
+    // 3. two-stage pipeline in a loop with a single exit, two blocks per
+    //    iteration and the rest after it (an exit after every block made the
+    //    compiler wait at the loop head for the block just issued); after
+    //    each consume only the other block's U RP loads may be in flight,
+    //    said explicitly because a consume past the wave's rows waits for
+    //    nothing
+    constexpr int kBlk = U * RP;
+    uint32_t b = 0;
+    for (; b + 2u < nblk; b += 2u) {
       issue(B);
       consume(A);
-      ++b;
-      if (b + 1 >= nblk) { consume(B); break; }
+      __builtin_amdgcn_s_waitcnt(((kBlk >> 4) << 14) | 0x0F70 | (kBlk & 15));
       issue(A);
       consume(B);
-      ++b;
+      __builtin_amdgcn_s_waitcnt(((kBlk >> 4) << 14) | 0x0F70 | (kBlk & 15));
+    }
+    if (b + 1u < nblk) {
+      issue(B);
+      consume(A);
+      consume(B);
+    } else if (b < nblk) {
+      consume(A);
     }
   }
 }
@@ -315,7 +329,9 @@ __global__ __launch_bounds__(512) void k_fp8_gemv_rx(const uint8_t *__restrict__
 
   struct RowBlock {
     u32x4 q[NS];
-    uint32_t s[kBlock ? NS : 1];  // block scale bits of each segment's run
+    // block scale bits of each segment's run; BF16 ones stay 16-bit values
+    // until they are used (no arithmetic on a block just requested)
+    std::conditional_t<SF == kSfBlockBf16, uint16_t, uint32_t> s[kBlock ? NS : 1];
   };
   u32x4 xw[NS][2];
 #pragma unroll
@@ -363,7 +379,11 @@ __global__ __launch_bounds__(512) void k_fp8_gemv_rx(const uint8_t *__restrict__
                                   make_float4(a[u][8], a[u][9], a[u][10], a[u][11]),
                                   make_float4(a[u][12], a[u][13], a[u][14], a[u][15]));
       if constexpr (kBlock) {
-        const float sc = SF == kSfBlockBf16 ? bf16_bits_to_f32((uint16_t)blk.s[u]) : __uint_as_float(blk.s[u]);
+        float sc;
+        if constexpr (SF == kSfBlockBf16)
+          sc = bf16_bits_to_f32(blk.s[u]);
+        else
+          sc = __uint_as_float(blk.s[u]);
         acc = __builtin_fmaf(sc, p, acc);
       } else {
         acc += p;
@@ -377,15 +397,20 @@ __global__ __launch_bounds__(512) void k_fp8_gemv_rx(const uint8_t *__restrict__
     }
     ++c_row;
   };
-  for (uint32_t b = 0; b < nr;) {
-    if (b + 1 >= nr) { consume(A); break; }
+  // two-stage pipeline in a loop with a single exit (as in k_fp8_gemv)
+  uint32_t b = 0;
+  for (; b + 2u < nr; b += 2u) {
     issue(B);
     consume(A);
-    ++b;
-    if (b + 1 >= nr) { consume(B); break; }
     issue(A);
     consume(B);
-    ++b;
+  }
+  if (b + 1u < nr) {
+    issue(B);
+    consume(A);
+    consume(B);
+  } else if (b < nr) {
+    consume(A);
   }
 }
 

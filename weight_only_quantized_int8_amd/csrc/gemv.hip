@@ -354,16 +354,31 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
         }
       }
     }
-    // 3. two-stage pipeline; the only branches are the loop exits
-    for (uint32_t b = 0; b < nblk;) {
-      if (b + 1 >= nblk) { consume(A); break; }
+    // 3. two-stage pipeline, two blocks per iteration and the rest after
+    //    the loop.  The loop has a single exit: with an exit after every
+    //    block, the compiler's wait counts at the loop head also covered the
+    //    paths that leave, and it waited there for the block just issued.
+    //    After each consume the other block's U RP loads may still be in
+    //    flight, and nothing older: said explicitly, because a consume whose
+    //    items are past the wave's rows reads nothing and so waits for
+    //    nothing, and the compiler would otherwise wait for every load
+    //    before reusing the consumed block's registers.
+    constexpr int kBlk = U * RP;
+    uint32_t b = 0;
+    for (; b + 2u < nblk; b += 2u) {
       issue(B);
       consume(A);
-      ++b;
-      if (b + 1 >= nblk) { consume(B); break; }
+      __builtin_amdgcn_s_waitcnt(((kBlk >> 4) << 14) | 0x0F70 | (kBlk & 15));
       issue(A);
       consume(B);
-      ++b;
+      __builtin_amdgcn_s_waitcnt(((kBlk >> 4) << 14) | 0x0F70 | (kBlk & 15));
+    }
+    if (b + 1u < nblk) {
+      issue(B);
+      consume(A);
+      consume(B);
+    } else if (b < nblk) {
+      consume(A);
     }
   }
 }
@@ -392,7 +407,7 @@ __device__ __forceinline__ void gemv_wave_rx(const uint8_t *__restrict__ codes, 
 
   struct RowBlock {
     u32x4 q[NS];
-    uint32_t s[NS], b[NS];  // BF16 bits of the lane's group scale and bias
+    uint16_t s[NS], b[NS];  // BF16 bits of the lane's group scale and bias
   };
   // the activation loads go out first: waiting for them never waits for codes
   u32x4 xw[NS][2];
@@ -437,8 +452,8 @@ __device__ __forceinline__ void gemv_wave_rx(const uint8_t *__restrict__ codes, 
     float acc = 0.f;
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-      const float sc = bf16_bits_to_f32((uint16_t)blk.s[u]);
-      const float bb = __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32((uint16_t)blk.b[u]));
+      const float sc = bf16_bits_to_f32(blk.s[u]);
+      const float bb = __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32(blk.b[u]));
       const float p = run_dot(blk.q[u], make_float4(a[u][0], a[u][1], a[u][2], a[u][3]),
                               make_float4(a[u][4], a[u][5], a[u][6], a[u][7]),
                               make_float4(a[u][8], a[u][9], a[u][10], a[u][11]),
@@ -449,16 +464,22 @@ __device__ __forceinline__ void gemv_wave_rx(const uint8_t *__restrict__ codes, 
     if (lane == 63u) y[rbeg + c_row] = to_bf16_bits(tot);
     ++c_row;
   };
-  // two-stage pipeline; the only branches are the loop exits
-  for (uint32_t b = 0; b < nr;) {
-    if (b + 1 >= nr) { consume(A); break; }
+  // two-stage pipeline in a loop with a single exit (see gemv_wave); the
+  // scale and bias stay 16-bit values until they are used, so that no
+  // arithmetic on a block just requested is placed at the loop's end
+  uint32_t b = 0;
+  for (; b + 2u < nr; b += 2u) {
     issue(B);
     consume(A);
-    ++b;
-    if (b + 1 >= nr) { consume(B); break; }
     issue(A);
     consume(B);
-    ++b;
+  }
+  if (b + 1u < nr) {
+    issue(B);
+    consume(A);
+    consume(B);
+  } else if (b < nr) {
+    consume(A);
   }
 }
 
@@ -670,7 +691,7 @@ __global__ __launch_bounds__(512) void k_moe_grouped(const uint8_t *__restrict__
 
       struct RowBlock {
         u32x4 q[NS];
-        uint32_t s[NS], b[NS];
+        uint16_t s[NS], b[NS];
       };
       uint32_t i_row = 0;
       auto issue = [&](RowBlock &blk) {
@@ -693,8 +714,8 @@ __global__ __launch_bounds__(512) void k_moe_grouped(const uint8_t *__restrict__
           float acc = 0.f;
 #pragma unroll
           for (int u = 0; u < NS; ++u) {
-            const float sc = bf16_bits_to_f32((uint16_t)blk.s[u]);
-            const float bb = __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32((uint16_t)blk.b[u]));
+            const float sc = bf16_bits_to_f32(blk.s[u]);
+            const float bb = __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32(blk.b[u]));
             const float4 *ap = grp_act + ((c * NS + u) * 4u) * 64u + lane;
             const float p = run_dot(blk.q[u], ap[0], ap[64], ap[128], ap[192]);
             const float S = grp_sum[(c * NS + u) * 64u + lane];
@@ -707,15 +728,19 @@ __global__ __launch_bounds__(512) void k_moe_grouped(const uint8_t *__restrict__
       };
       RowBlock A, B;
       issue(A);
-      for (uint32_t b = 0; b < nr;) {
-        if (b + 1 >= nr) { consume(A); break; }
+      uint32_t b = 0;
+      for (; b + 2u < nr; b += 2u) {
         issue(B);
         consume(A);
-        ++b;
-        if (b + 1 >= nr) { consume(B); break; }
         issue(A);
         consume(B);
-        ++b;
+      }
+      if (b + 1u < nr) {
+        issue(B);
+        consume(A);
+        consume(B);
+      } else if (b < nr) {
+        consume(A);
       }
     }
   }

@@ -173,15 +173,22 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(const uint16_t *__restri
   QBlock<U> A, B;
   const uint32_t nblk = (nit + U - 1) / U;
   if (nblk) issue(A);
-  for (uint32_t bl = 0; bl < nblk;) {
-    if (bl + 1 >= nblk) { consume(A); break; }
+  // two blocks per iteration and the rest after the loop: a single exit,
+  // so that the compiler's wait counts at the loop head do not also cover
+  // the paths that leave (with them it waited for the block just issued)
+  uint32_t bl = 0;
+  for (; bl + 2u < nblk; bl += 2u) {
     issue(B);
     consume(A);
-    ++bl;
-    if (bl + 1 >= nblk) { consume(B); break; }
     issue(A);
     consume(B);
-    ++bl;
+  }
+  if (bl + 1u < nblk) {
+    issue(B);
+    consume(A);
+    consume(B);
+  } else if (bl < nblk) {
+    consume(A);
   }
 }
 
