@@ -113,6 +113,19 @@ def test_gemv(N, K, gs):
     assert_close(dev_to_bits(y), y_ref, A, f"gemv {N}x{K} gs{gs}")
 
 
+# Rows per wave from 3 to 7 (about 2048 waves below 16384 rows): both
+# pipeline loops run whole iterations and then one or two leftover blocks.
+@pytest.mark.parametrize("N,K,gs", [(6149, 4096, 64), (10300, 4096, 32), (12389, 8192, 128), (8193, 5120, 64)])
+def test_gemv_several_rows_per_wave(N, K, gs):
+    log(f"gemv rows-per-wave N={N} K={K} gs={gs}")
+    w, rng = make_weight(21_000 + N + K + gs, N, K, gs)
+    x = synth.gen_act(rng, K)
+    y = upload(w).gemv(bits_to_dev(x))
+    _sync()
+    y_ref, A = oracle.gemv(w.packed, w.scales, w.biases, gs, x)
+    assert_close(dev_to_bits(y), y_ref, A, f"gemv {N}x{K} gs{gs}")
+
+
 @pytest.mark.parametrize("N,K,gs", [(1024, 4096, 64), (5, 4128, 32), (14336, 4096, 64), (33, 96, 32)])
 def test_gemv_writes_exactly_n_outputs(N, K, gs):
     log(f"gemv guard N={N} K={K} gs={gs}")
