@@ -16,8 +16,8 @@ lines: the same layer as seven single-weight launches, the quantizer on an
 8B gate/up weight, the expert-indexed gemv over 8 experts of that shape (top-2
 routing, 1 and 4 tokens), the FP8 E4M3 gemv (per-row and 128 x 128 block
 scales) on the 8B FFN shapes, dequantize_to and the gated GEMV of the 70B-shaped
-FFN, the small-batch gemm (m = 2..16) and the prefill gemm (m = 512, 2048) in
-TFLOP/s.
+FFN, the small-batch gemm (m = 2..16, and 32 and 64 at group size 64) and the
+prefill gemm (m = 512, 2048) in TFLOP/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
        python bench.py --profile-only     # dominant kernel + calibration copy, for rocprofv3
@@ -325,6 +325,14 @@ def secondary(dev, quick):
                 res[f"gemm_m{m}_{N}x{K}_gs{gs}"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
                                                     "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
             if gs == 64:
+                for m in (32, 64):  # batched decode: 16-row passes on the 4096-row weight
+                    X = bits_dev(synth.gen_act(rng, (m, K)), dev)
+                    Y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+                    t = time_batches(lambda i: ws[i % len(ws)].gemm(X, Y), 20)
+                    b = gemm_bytes(N, K, gs, m)
+                    res[f"gemm_m{m}_{N}x{K}_gs64"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
+                                                      "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
+                                                      "TFLOP/s": 2.0 * m * N * K / t / 1e12}
                 for m in (512, 2048):
                     X = bits_dev(synth.gen_act(rng, (m, K)), dev)
                     Y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)

@@ -193,12 +193,19 @@ int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const
 
 /* gemm: Y = X W^T.  X is BF16 [m, in_features] and Y BF16 [m, out_features],
  * both contiguous row-major.  Y[i,n] = RNE_bf16(sum_k w[n,k] * X[i,k]) with fp32
- * accumulation; for m > 16 the weight enters the matrix cores as
- * RNE_bf16(w[n,k]) (the dequantize_to value).  m == 0 enqueues nothing and
+ * accumulation.  m = 1 runs the gemv; 2 <= m <= 16 the small-m kernel, which
+ * multiplies the raw codes and applies each group's scale and bias to the
+ * group's partial sums; larger m the tiled kernel, where the weight enters the
+ * matrix cores as RNE_bf16(w[n,k]) (the dequantize_to value).  For
+ * 16 < m <= 64 on a weight that gives the tiled kernel few tiles per CU (so
+ * that its time is set by walking all of in_features, whatever m), the rows
+ * go through the small-m kernel in slices of 16 when ceil(m/16) passes over
+ * the weight are estimated faster: one launch per slice, all on `stream`, and
+ * row i's result is then the small-m kernel's.  m == 0 enqueues nothing and
  * returns INT8W_OK.  INT8W_ERR_SHAPE also when m * in_features or
  * m * out_features exceeds 2^32 - 1, or when in_features >= 2^23 for an m
- * that takes the tiled kernel (m > 16, or an m >= 2 whose scale/bias rows do
- * not fit the small-m kernel's LDS). */
+ * that takes the tiled kernel (m > 16 outside those slices, or an m >= 2
+ * whose scale/bias rows do not fit the small-m kernel's LDS). */
 int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, uint64_t stream);
 
 /* Human-readable description of the calling thread's most recent error

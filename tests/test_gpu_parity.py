@@ -297,6 +297,38 @@ def test_gemm_prefill_small(m, N, K, gs):
     assert_close(dev_to_bits(Y), Y_ref, A, f"gemm m={m} {N}x{K} gs{gs}")
 
 
+# 16 < m <= 64 on weights that give the tiled kernel few tiles per CU: the
+# rows go through the small-m kernel 16 at a time.  Every row is checked
+# against the oracle, and every slice of two or more rows bit for bit against
+# gemm on that slice alone (the small-m kernel itself; a one-row slice alone
+# would take the gemv).
+@pytest.mark.parametrize("m,N,K,gs", [
+    (17, 1024, 8192, 64),
+    (40, 1000, 8192, 32),
+    (33, 3000, 4096, 128),
+    (20, 500, 4160, 32),      # K not a multiple of 8 groups: the unstaged tiled shape would apply
+    (64, 4096, 14336, 64),    # 8B down projection
+])
+def test_gemm_in_slices_of_16_rows(m, N, K, gs):
+    log(f"gemm 16-row slices m={m} N={N} K={K} gs={gs}")
+    w, rng = make_weight(3500 + m + N + K, N, K, gs)
+    X = synth.gen_act(rng, (m, K))
+    W = upload(w)
+    Xd = bits_to_dev(X)
+    Y = W.gemm(Xd)
+    _sync()
+    got = dev_to_bits(Y)
+    Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
+    assert_close(got, Y_ref, A, f"gemm m={m} {N}x{K} gs{gs}")
+    for r0 in range(0, m, 16):
+        r1 = min(r0 + 16, m)
+        if r1 - r0 < 2:
+            continue
+        part = dev_to_bits(W.gemm(Xd[r0:r1].contiguous()))
+        _sync()
+        assert np.array_equal(got[r0:r1], part), f"rows {r0}..{r1 - 1} differ from gemm on the slice alone"
+
+
 @pytest.mark.parametrize("m,N,K,gs", [
     (513, 8200, 1024, 128),   # one scale/bias block (16 steps), ragged rows and columns
     (300, 24000, 1536, 64),   # three blocks of 8 steps, last column tile half full

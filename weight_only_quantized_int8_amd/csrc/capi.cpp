@@ -338,8 +338,11 @@ int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m,
   const uint64_t K = w->in_features, N = w->out_features;
   if ((uint64_t)m * K > 0xFFFFFFFFull || (uint64_t)m * N > 0xFFFFFFFFull)
     return fail(INT8W_ERR_SHAPE, "m=%u rows too many for this weight", m);
+  // 16 < m <= 64 on a small grid: 16-row passes of the small-m kernel
+  const bool sm_ok = smallm_supported(w->in_features, w->group_size);
+  const bool passes = m > 16u && sm_ok && gemm_prefer_smallm_passes(view(w), m);
   // the tiled kernel addresses a 256-row X tile with 32-bit byte offsets
-  const bool tiled = m > 16u || (m > 1u && !smallm_supported(w->in_features, w->group_size));
+  const bool tiled = !passes && (m > 16u || (m > 1u && !sm_ok));
   if (tiled && K * 2u * 256u > 0xFFFFFFFFull)
     return fail(INT8W_ERR_SHAPE, "in_features=%u above 2^23 - 1 needs m = 1 or a small-m shape (m=%u)",
                 w->in_features, m);
@@ -351,12 +354,17 @@ int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m,
   (void)hipGetLastError();
   hipStream_t s = as_stream(stream);
   hipError_t e;
-  if (m == 1)
+  if (m == 1) {
     e = launch_gemv(view(w), kEpiNone, x, nullptr, nullptr, y, s);
-  else if (m <= 16 && smallm_supported(w->in_features, w->group_size))
+  } else if (m <= 16 && sm_ok) {
     e = launch_gemm_smallm(view(w), x, y, m, s);
-  else
+  } else if (passes) {
+    e = hipSuccess;
+    for (uint32_t r0 = 0; r0 < m && e == hipSuccess; r0 += 16u)
+      e = launch_gemm_smallm(view(w), x + (size_t)r0 * K, y + (size_t)r0 * N, m - r0 < 16u ? m - r0 : 16u, s);
+  } else {
     e = launch_gemm_prefill(view(w), x, y, m, s);
+  }
   return finish_launch(e, s);
 }
 

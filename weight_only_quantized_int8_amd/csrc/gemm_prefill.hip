@@ -788,20 +788,44 @@ hipError_t launch_gemm_prefill_tile(int t, const WeightView &w, const uint16_t *
   }
 }
 
-hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
-                               hipStream_t stream) {
-  // Measured on MI355X: 256 x 128 tiles when they give at least ~3/4 of a
-  // tile per CU, else 128 x 128, else 128 x 64 (fewer idle CUs); staged by DMA
-  // where K allows (the 128 x 64 staged tiles: m = 512 on 4096 x 14336 in
-  // 107 us against 135 us unstaged).
-  const uint32_t cus = (uint32_t)device_cu_count();
+namespace {
+
+// Measured on MI355X: 256 x 128 tiles when they give at least ~3/4 of a tile
+// per CU, else 128 x 128, else 128 x 64 (fewer idle CUs); staged by DMA where
+// K allows (the 128 x 64 staged tiles: m = 512 on 4096 x 14336 in 107 us
+// against 135 us unstaged).
+int prefill_shape(const WeightView &w, uint32_t m, uint32_t cus) {
   const uint32_t t256 = ((m + 255u) / 256u) * ((w.N + 127u) / 128u);
   const uint32_t t128 = ((m + 127u) / 128u) * ((w.N + 127u) / 128u);
   const bool staged = w.K % (8u * w.gs) == 0u;
-  const int shape = 4u * t256 >= 3u * cus ? (staged ? 3 : 2)
-                    : 4u * t128 >= 3u * cus ? 0
-                    : staged ? 4 : 1;
-  return launch_gemm_prefill_tile(shape, w, X, Y, m, stream);
+  return 4u * t256 >= 3u * cus ? (staged ? 3 : 2) : 4u * t128 >= 3u * cus ? 0 : staged ? 4 : 1;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
+                               hipStream_t stream) {
+  return launch_gemm_prefill_tile(prefill_shape(w, m, (uint32_t)device_cu_count()), w, X, Y, m, stream);
+}
+
+// On the 128 x 64 grids (fewer than ~3/4 of a 128 x 128 tile per CU) the
+// tiled kernel's time hardly depends on m: one workgroup per CU walks all of
+// K, about 0.42 us per 64-deep step for each round of tiles over the CUs.  A
+// small-m pass streams the weight once, at about 4 TB/s plus ~3 us.  Measured
+// (graph-timed): 4096 x 14336 gs64, m = 17 / 32 / 64 / 96: passes 30 / 35 /
+// 68 / 105 us, tiled 90 / 90 / 91 / 91 us; 4096 x 4096, m = 48 / 64: 25 / 33
+// against 28 / 29 us; 14336 x 4096 (224 such tiles), m = 17: 30 against 31 us.
+bool gemm_prefer_smallm_passes(const WeightView &w, uint32_t m) {
+  if (m <= 16u || m > 64u) return false;
+  const uint32_t cus = (uint32_t)device_cu_count();
+  const int shape = prefill_shape(w, m, cus);
+  if (shape != 4 && shape != 1) return false;
+  const double tiles = (double)((m + 127u) / 128u) * (double)((w.N + 63u) / 64u);
+  const double rounds = (double)(uint32_t)((tiles + cus - 1.0) / cus);
+  const double t_tiled = rounds * (double)((w.K + 63u) / 64u) * 0.42;
+  const double bytes = (double)w.N * w.K + 4.0 * w.N * (w.K / w.gs);
+  const double t_pass = bytes / 4.0e6 + 3.0;  // us at 4 TB/s
+  return (double)((m + 15u) / 16u) * t_pass < t_tiled;
 }
 
 }  // namespace int8w

@@ -60,4 +60,9 @@ hipError_t launch_gemm_smallm(const WeightView &w, const uint16_t *X, uint16_t *
 hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                                hipStream_t stream);
 
+// For 16 < m <= 64: whether ceil(m / 16) passes of the small-m kernel over
+// 16-row slices of X are expected to beat the tiled kernel (a grid of few
+// tiles, each walking all of K).  The caller checks smallm_supported.
+bool gemm_prefer_smallm_passes(const WeightView &w, uint32_t m);
+
 }  // namespace int8w
