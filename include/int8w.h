@@ -199,9 +199,10 @@ int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const
  * matrix cores as RNE_bf16(w[n,k]) (the dequantize_to value).  For
  * 16 < m <= 64 on a weight that gives the tiled kernel few tiles per CU (so
  * that its time is set by walking all of in_features, whatever m), the rows
- * go through the small-m kernel in slices of 16 when ceil(m/16) passes over
- * the weight are estimated faster: one launch per slice, all on `stream`, and
- * row i's result is then the small-m kernel's.  m == 0 enqueues nothing and
+ * go through the small-m kernel in slices of 32 (16 where its two-tile form
+ * does not fit the LDS) when that many passes over the weight are estimated
+ * faster: one launch per slice, all on `stream`; each slice's rows are then
+ * what gemm gives for that slice alone.  m == 0 enqueues nothing and
  * returns INT8W_OK.  INT8W_ERR_SHAPE also when m * in_features or
  * m * out_features exceeds 2^32 - 1, or when in_features >= 2^23 for an m
  * that takes the tiled kernel (m > 16 outside those slices, or an m >= 2

@@ -298,19 +298,21 @@ def test_gemm_prefill_small(m, N, K, gs):
 
 
 # 16 < m <= 64 on weights that give the tiled kernel few tiles per CU: the
-# rows go through the small-m kernel 16 at a time.  Every row is checked
+# rows go through the small-m kernel 32 at a time (two X tiles per pass; a
+# slice of at most 16 rows takes the one-tile form).  Every row is checked
 # against the oracle, and every slice of two or more rows bit for bit against
-# gemm on that slice alone (the small-m kernel itself; a one-row slice alone
-# would take the gemv).
+# gemm on that slice alone (a one-row slice alone would take the gemv).
 @pytest.mark.parametrize("m,N,K,gs", [
     (17, 1024, 8192, 64),
     (40, 1000, 8192, 32),
     (33, 3000, 4096, 128),
     (20, 500, 4160, 32),      # K not a multiple of 8 groups: the unstaged tiled shape would apply
     (64, 4096, 14336, 64),    # 8B down projection
+    (50, 4096, 4096, 64),     # two passes, the second of 18 rows
+    (36, 300, 8192, 128),     # a 32-row pass and a 4-row one-tile pass
 ])
-def test_gemm_in_slices_of_16_rows(m, N, K, gs):
-    log(f"gemm 16-row slices m={m} N={N} K={K} gs={gs}")
+def test_gemm_in_slices_of_32_rows(m, N, K, gs):
+    log(f"gemm 32-row slices m={m} N={N} K={K} gs={gs}")
     w, rng = make_weight(3500 + m + N + K, N, K, gs)
     X = synth.gen_act(rng, (m, K))
     W = upload(w)
@@ -320,8 +322,8 @@ def test_gemm_in_slices_of_16_rows(m, N, K, gs):
     got = dev_to_bits(Y)
     Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
     assert_close(got, Y_ref, A, f"gemm m={m} {N}x{K} gs{gs}")
-    for r0 in range(0, m, 16):
-        r1 = min(r0 + 16, m)
+    for r0 in range(0, m, 32):
+        r1 = min(r0 + 32, m)
         if r1 - r0 < 2:
             continue
         part = dev_to_bits(W.gemm(Xd[r0:r1].contiguous()))

@@ -338,9 +338,11 @@ int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m,
   const uint64_t K = w->in_features, N = w->out_features;
   if ((uint64_t)m * K > 0xFFFFFFFFull || (uint64_t)m * N > 0xFFFFFFFFull)
     return fail(INT8W_ERR_SHAPE, "m=%u rows too many for this weight", m);
-  // 16 < m <= 64 on a small grid: 16-row passes of the small-m kernel
+  // 16 < m <= 64 on a small grid: passes of the small-m kernel over slices of
+  // 32 (or 16) rows
   const bool sm_ok = smallm_supported(w->in_features, w->group_size);
-  const bool passes = m > 16u && sm_ok && gemm_prefer_smallm_passes(view(w), m);
+  const uint32_t slice = m > 16u ? gemm_smallm_slice_rows(view(w), m) : 0u;
+  const bool passes = slice != 0u;
   // the tiled kernel addresses a 256-row X tile with 32-bit byte offsets
   const bool tiled = !passes && (m > 16u || (m > 1u && !sm_ok));
   if (tiled && K * 2u * 256u > 0xFFFFFFFFull)
@@ -359,9 +361,13 @@ int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m,
   } else if (m <= 16 && sm_ok) {
     e = launch_gemm_smallm(view(w), x, y, m, s);
   } else if (passes) {
+    // slices of `slice` rows; one of at most 16 rows takes the one-tile kernel
     e = hipSuccess;
-    for (uint32_t r0 = 0; r0 < m && e == hipSuccess; r0 += 16u)
-      e = launch_gemm_smallm(view(w), x + (size_t)r0 * K, y + (size_t)r0 * N, m - r0 < 16u ? m - r0 : 16u, s);
+    for (uint32_t r0 = 0; r0 < m && e == hipSuccess; r0 += slice) {
+      const uint32_t mi = m - r0 < slice ? m - r0 : slice;
+      e = mi > 16u ? launch_gemm_smallm32(view(w), x + (size_t)r0 * K, y + (size_t)r0 * N, mi, s)
+                   : launch_gemm_smallm(view(w), x + (size_t)r0 * K, y + (size_t)r0 * N, mi, s);
+    }
   } else {
     e = launch_gemm_prefill(view(w), x, y, m, s);
   }

@@ -1,6 +1,7 @@
-// gemm_smallm.hip -- Y = X W^T for 2 <= m <= 16 rows on gfx950 matrix cores
-// (rustdoc page "MlxInt8Weight", method gemm: X BF16 [m, in_features],
-// Y BF16 [m, out_features]).
+// gemm_smallm.hip -- Y = X W^T for 2 <= m <= 16 rows (one 16-row X tile), or
+// up to 32 (two tiles, MT = 2), on gfx950 matrix cores (rustdoc page
+// "MlxInt8Weight", method gemm: X BF16 [m, in_features], Y BF16
+// [m, out_features]).
 //
 // Still HBM-bound (each code byte is read once and used m times), but m fp32
 // FMAs per code would swamp the vector ALUs, so the products go to
@@ -20,14 +21,15 @@
 //    + 8..15 of each lane (one group); gs == 32: the two MFMAs take 8 codes of
 //    each 32-code half, one group each.
 //  * A workgroup of KS waves owns RT tiles of 16 weight rows and walks K in
-//    blocks of KB = 64*KS*SPW codes.  Each block (the tiles' codes and the 16
-//    X rows, rows past m zero) is copied by DMA (buffer_load_dwordx4 ... lds)
+//    blocks of KB = 64*KS*SPW codes.  Each block (the tiles' codes and the
+//    16 MT X rows, rows past m zero) is copied by DMA (buffer_load_dwordx4 ... lds)
 //    with every load reading whole 16-byte chunks of one row in contiguous
 //    runs (the weight stream stays sequential in HBM) and landing in LDS with
 //    the 16-byte chunks of row r XOR-swizzled by r mod 16 (so the 16 rows an
 //    MFMA operand read touches sit in distinct banks), then read back in MFMA
 //    operand layout.  Wave w takes the SPW steps [w*SPW, (w+1)*SPW) of every
-//    block for all RT tiles.
+//    block for all RT tiles; with MT = 2 each code fragment, converted once,
+//    feeds the MFMAs of both X tiles.
 //  * Pipeline: NS LDS block buffers; the DMA of NS - 1 blocks is in flight
 //    while one is consumed; one workgroup barrier per block.  Every global
 //    load goes through a bounded buffer resource: past the end it reads (or
@@ -56,14 +58,14 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int KS, int RT, int SPW, bool G32>
+template <int KS, int RT, int SPW, bool G32, int MT = 1>
 struct SmShape {
   static constexpr int kThreads = 64 * KS;
   static constexpr uint32_t KB = 64u * KS * SPW;         // codes per block
   static constexpr uint32_t CPR = KB / 16u;               // 16-byte code chunks per row per block
   static constexpr uint32_t XCPR = 2u * CPR;              // 16-byte X chunks per row per block
   static constexpr uint32_t CODE_BYTES = 16u * RT * KB;   // one block of codes in LDS
-  static constexpr uint32_t X_BYTES = 16u * 2u * KB;      // 16 X rows (rows past m are zero)
+  static constexpr uint32_t X_BYTES = 16u * MT * 2u * KB;  // 16 MT X rows (rows past m are zero)
   static constexpr uint32_t BUF_BYTES = CODE_BYTES + X_BYTES;
   static constexpr int NC = (int)(CODE_BYTES / 1024u / KS);  // code loads per wave per block
   static constexpr int NX = (int)(X_BYTES / 1024u / KS);     // X loads per wave per block
@@ -73,12 +75,12 @@ struct SmShape {
 
 // LDS (dynamic): NS block buffers [codes | X], then sb [16*RT][G+1] packed
 // (scale | bias << 16).  The partial-sum exchange reuses the block buffers.
-template <int KS, int RT, int SPW, int NS, bool G32>
+template <int KS, int RT, int SPW, int NS, bool G32, int MT>
 __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ X, uint16_t *__restrict__ Y,
     uint32_t N, uint32_t K, uint32_t m, uint32_t gs_log2) {
-  using S = SmShape<KS, RT, SPW, G32>;
+  using S = SmShape<KS, RT, SPW, G32, MT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_sm[];
   const uint32_t G = K >> gs_log2;
   const uint32_t SBP = G + 1u;  // odd pitch: the 16 rows of a read hit distinct banks
@@ -186,9 +188,11 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
 
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4 acc[RT];
+  f32x4 acc[MT][RT];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = zero;
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[mt][t] = zero;
 
   auto compute = [&](uint32_t blk, uint32_t buf) {
     const uint8_t *cb = lds_sm + buf * S::BUF_BYTES;
@@ -199,21 +203,32 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
       const uint32_t kg = blk * S::KB + kl;          // ... within the row
       uint32_t g = kg >> gs_log2;
       if (g >= G) g = G - 1u;  // a step past K holds zeros: any finite pair
-      // X fragments of the step's two MFMAs (row lr)
-      u32x4 xa, xb;
-      if constexpr (G32) {
-        const uint32_t ca = (kl + 8u * lg) >> 3, cbx = (kl + 32u + 8u * lg) >> 3;  // 16-byte X chunks
-        xa = *reinterpret_cast<const u32x4 *>(xbp + lr * (2u * S::KB) + 16u * (ca ^ lr));
-        xb = *reinterpret_cast<const u32x4 *>(xbp + lr * (2u * S::KB) + 16u * (cbx ^ lr));
-      } else {
-        const uint32_t ca = (kl + 16u * lg) >> 3;
-        xa = *reinterpret_cast<const u32x4 *>(xbp + lr * (2u * S::KB) + 16u * (ca ^ lr));
-        xb = *reinterpret_cast<const u32x4 *>(xbp + lr * (2u * S::KB) + 16u * ((ca + 1u) ^ lr));
+      // X fragments of the step's two MFMAs (row 16 mt + lr of each X tile;
+      // its chunks are swizzled by lr like every other row's)
+      bf16x8 xa8[MT], xb8[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint8_t *xr = xbp + (16u * mt + lr) * (2u * S::KB);
+        u32x4 xa, xb;
+        if constexpr (G32) {
+          const uint32_t ca = (kl + 8u * lg) >> 3, cbx = (kl + 32u + 8u * lg) >> 3;  // 16-byte X chunks
+          xa = *reinterpret_cast<const u32x4 *>(xr + 16u * (ca ^ lr));
+          xb = *reinterpret_cast<const u32x4 *>(xr + 16u * (cbx ^ lr));
+        } else {
+          const uint32_t ca = (kl + 16u * lg) >> 3;
+          xa = *reinterpret_cast<const u32x4 *>(xr + 16u * (ca ^ lr));
+          xb = *reinterpret_cast<const u32x4 *>(xr + 16u * ((ca + 1u) ^ lr));
+        }
+        xa8[mt] = __builtin_bit_cast(bf16x8, xa);
+        xb8[mt] = __builtin_bit_cast(bf16x8, xb);
       }
-      const bf16x8 xa8 = __builtin_bit_cast(bf16x8, xa), xb8 = __builtin_bit_cast(bf16x8, xb);
       if constexpr (G32) {
-        const f32x4 SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8, ones, zero, 0, 0, 0);
-        const f32x4 SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, ones, zero, 0, 0, 0);
+        f32x4 SA[MT], SB[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          SA[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8[mt], ones, zero, 0, 0, 0);
+          SB[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8[mt], ones, zero, 0, 0, 0);
+        }
         const uint32_t gb = g + 1u < G ? g + 1u : g;
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
@@ -225,17 +240,25 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
           const uint32_t pa = sb[row * SBP + g], pb = sb[row * SBP + gb];
           const float sa = __uint_as_float(pa << 16), ba = __uint_as_float(pa & 0xFFFF0000u);
           const float sbv = __uint_as_float(pb << 16), bbv = __uint_as_float(pb & 0xFFFF0000u);
-          const f32x4 PA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8, codes8_to_bf16x8(qa.x, qa.y), zero, 0, 0, 0);
-          const f32x4 PB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, codes8_to_bf16x8(qb.x, qb.y), zero, 0, 0, 0);
+          const bf16x8 qa8 = codes8_to_bf16x8(qa.x, qa.y), qb8 = codes8_to_bf16x8(qb.x, qb.y);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float v = __builtin_fmaf(sa, PA[r], __builtin_fmaf(ba, SA[r], acc[t][r]));
-            acc[t][r] = __builtin_fmaf(sbv, PB[r], __builtin_fmaf(bbv, SB[r], v));
+          for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 PA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8[mt], qa8, zero, 0, 0, 0);
+            const f32x4 PB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8[mt], qb8, zero, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float v = __builtin_fmaf(sa, PA[r], __builtin_fmaf(ba, SA[mt][r], acc[mt][t][r]));
+              acc[mt][t][r] = __builtin_fmaf(sbv, PB[r], __builtin_fmaf(bbv, SB[mt][r], v));
+            }
           }
         }
       } else {
-        f32x4 Sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8, ones, zero, 0, 0, 0);
-        Sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, ones, Sx, 0, 0, 0);
+        f32x4 Sx[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          Sx[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8[mt], ones, zero, 0, 0, 0);
+          Sx[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8[mt], ones, Sx[mt], 0, 0, 0);
+        }
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           const uint32_t row = 16u * t + lr;
@@ -243,10 +266,15 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
           const u32x4 q = *reinterpret_cast<const u32x4 *>(cb + row * S::KB + 16u * (c ^ lr));
           const uint32_t p = sb[row * SBP + g];
           const float s = __uint_as_float(p << 16), b = __uint_as_float(p & 0xFFFF0000u);
-          f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8, codes8_to_bf16x8(q.x, q.y), zero, 0, 0, 0);
-          P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8, codes8_to_bf16x8(q.z, q.w), P, 0, 0, 0);
+          const bf16x8 qa8 = codes8_to_bf16x8(q.x, q.y), qb8 = codes8_to_bf16x8(q.z, q.w);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[t][r] = __builtin_fmaf(s, P[r], __builtin_fmaf(b, Sx[r], acc[t][r]));
+          for (int mt = 0; mt < MT; ++mt) {
+            f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa8[mt], qa8, zero, 0, 0, 0);
+            P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb8[mt], qb8, P, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[mt][t][r] = __builtin_fmaf(s, P[r], __builtin_fmaf(b, Sx[mt][r], acc[mt][t][r]));
+          }
         }
       }
     }
@@ -259,9 +287,9 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
   // counts only this wave's DMA: the loop issues no other memory loads.
 #define INT8W_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
   static_assert((NS - 2) * (S::NC + S::NX) < 64, "vmcnt range");
-  static_assert(S::NX <= 4, "wait table");
+  static_assert(S::NX <= 8, "wait table");
   // X rows m .. 15 of every buffer: zeros (the MFMA A operand's unused rows)
-  for (uint32_t o = (kSkipX ? m : 16u) * 2u * S::KB + 16u * tid; o < S::X_BYTES; o += 16u * S::kThreads) {
+  for (uint32_t o = (kSkipX ? m : 16u * MT) * 2u * S::KB + 16u * tid; o < S::X_BYTES; o += 16u * S::kThreads) {
 #pragma unroll
     for (int u = 0; u < NS; ++u)
       *reinterpret_cast<u32x4 *>(lds_sm + u * S::BUF_BYTES + S::CODE_BYTES + o) = u32x4{0u, 0u, 0u, 0u};
@@ -274,7 +302,11 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_smallm(
       case 1: INT8W_VMCNT((NS - 2) * (S::NC + 1)); break;
       case 2: INT8W_VMCNT((NS - 2) * (S::NC + 2)); break;
       case 3: INT8W_VMCNT((NS - 2) * (S::NC + 3)); break;
-      default: INT8W_VMCNT((NS - 2) * (S::NC + 4)); break;
+      case 4: INT8W_VMCNT((NS - 2) * (S::NC + 4)); break;
+      case 5: INT8W_VMCNT((NS - 2) * (S::NC + 5)); break;
+      case 6: INT8W_VMCNT((NS - 2) * (S::NC + 6)); break;
+      case 7: INT8W_VMCNT((NS - 2) * (S::NC + 7)); break;
+      default: INT8W_VMCNT((NS - 2) * (S::NC + 8)); break;
     }
   };
   // Unrolled NS times so that every buffer index is a constant: the
@@ -302,41 +334,47 @@ pipeline_done:
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the look-ahead DMA (zeros past the end) has landed
   __syncthreads();  // every wave is done with the block buffers
   f32x4 *red = reinterpret_cast<f32x4 *>(lds_sm);
+  constexpr int kTiles = MT * RT;  // accumulator tiles per wave
 #pragma unroll
-  for (int t = 0; t < RT; ++t) red[(wave * RT + t) * 64u + lane] = acc[t];
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) red[(wave * kTiles + mt * RT + t) * 64u + lane] = acc[mt][t];
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    f32x4 v = red[t * 64u + lane];
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int w = 1; w < KS; ++w) {
-      const f32x4 o = red[(w * RT + t) * 64u + lane];
-      v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
-    }
-    const uint32_t n = n0 + 16u * t + lr;
-    if (n < N) {
+    for (int t = 0; t < RT; ++t) {
+      f32x4 v = red[(mt * RT + t) * 64u + lane];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t i = 4u * lg + r;
-        if (i < m) Y[(size_t)i * N + n] = to_bf16_bits(v[r]);
+      for (int w = 1; w < KS; ++w) {
+        const f32x4 o = red[(w * kTiles + mt * RT + t) * 64u + lane];
+        v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
+      }
+      const uint32_t n = n0 + 16u * t + lr;
+      if (n < N) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t i = 16u * mt + 4u * lg + r;
+          if (i < m) Y[(size_t)i * N + n] = to_bf16_bits(v[r]);
+        }
       }
     }
   }
 }
 
-template <int KS, int RT, int SPW, int NS>
+template <int KS, int RT, int SPW, int NS, int MT = 1>
 size_t smallm_lds_bytes(uint32_t K, uint32_t gs) {
-  using S = SmShape<KS, RT, SPW, false>;
+  using S = SmShape<KS, RT, SPW, false, MT>;
   const size_t G = K / gs;
   size_t bytes = NS * S::BUF_BYTES + (16u * RT * (G + 1u) + 1u) * 4u;  // + the spare slot
-  const size_t red = (size_t)KS * RT * 64u * 16u;
+  const size_t red = (size_t)KS * RT * MT * 64u * 16u;
   return bytes > red ? bytes : red;
 }
 
-template <int KS, int RT, int SPW, int NS, bool G32>
+template <int KS, int RT, int SPW, int NS, bool G32, int MT = 1>
 hipError_t launch_sm(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream) {
-  auto kern = k_gemm_smallm<KS, RT, SPW, NS, G32>;
+  auto kern = k_gemm_smallm<KS, RT, SPW, NS, G32, MT>;
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -345,7 +383,7 @@ hipError_t launch_sm(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32
     configured = true;
   }
   const uint32_t blocks = (w.N + 16u * RT - 1u) / (16u * RT);
-  const size_t lds = smallm_lds_bytes<KS, RT, SPW, NS>(w.K, w.gs);
+  const size_t lds = smallm_lds_bytes<KS, RT, SPW, NS, MT>(w.K, w.gs);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * KS), lds, stream,
                      reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m,
                      (uint32_t)__builtin_ctz(w.gs));
@@ -406,6 +444,33 @@ hipError_t launch_gemm_smallm_shape(int shape, const WeightView &w, const uint16
 hipError_t launch_gemm_smallm(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                               hipStream_t stream) {
   return launch_gemm_smallm_shape(smallm_choose(w.N, w.K, w.gs), w, X, Y, m, stream);
+}
+
+// Two X tiles (up to 32 rows) per pass: each code fragment converted once
+// feeds both tiles' MFMAs.  Shapes: 4/2/1/3 with many rows, 8/1/1/3 with few.
+#define INT8W_SM32_SHAPE0 4, 2, 1, 3
+#define INT8W_SM32_SHAPE1 8, 1, 1, 3
+int smallm32_choose(uint32_t N, uint32_t K, uint32_t gs) {
+  const uint32_t cus = (uint32_t)device_cu_count();
+  const int shape = (N + 15u) / 16u >= 2u * cus ? 0 : 1;
+  const size_t lds = shape == 0 ? smallm_lds_bytes<INT8W_SM32_SHAPE0, 2>(K, gs)
+                                : smallm_lds_bytes<INT8W_SM32_SHAPE1, 2>(K, gs);
+  if (lds <= 160u * 1024u) return shape;
+  return smallm_lds_bytes<INT8W_SM32_SHAPE1, 2>(K, gs) <= 160u * 1024u ? 1 : -1;
+}
+
+bool smallm32_supported(uint32_t N, uint32_t K, uint32_t gs) { return smallm32_choose(N, K, gs) >= 0; }
+
+hipError_t launch_gemm_smallm32(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
+                                hipStream_t stream) {
+  const int shape = smallm32_choose(w.N, w.K, w.gs);
+  if (shape < 0 || m > 32u) return hipErrorInvalidValue;
+  const bool g32 = w.gs == 32;
+  if (shape == 0)
+    return g32 ? launch_sm<INT8W_SM32_SHAPE0, true, 2>(w, X, Y, m, stream)
+               : launch_sm<INT8W_SM32_SHAPE0, false, 2>(w, X, Y, m, stream);
+  return g32 ? launch_sm<INT8W_SM32_SHAPE1, true, 2>(w, X, Y, m, stream)
+             : launch_sm<INT8W_SM32_SHAPE1, false, 2>(w, X, Y, m, stream);
 }
 
 }  // namespace int8w

@@ -60,9 +60,15 @@ hipError_t launch_gemm_smallm(const WeightView &w, const uint16_t *X, uint16_t *
 hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                                hipStream_t stream);
 
-// For 16 < m <= 64: whether ceil(m / 16) passes of the small-m kernel over
-// 16-row slices of X are expected to beat the tiled kernel (a grid of few
-// tiles, each walking all of K).  The caller checks smallm_supported.
-bool gemm_prefer_smallm_passes(const WeightView &w, uint32_t m);
+// The small-m kernel with two 16-row X tiles per pass (2 <= m <= 32), where
+// smallm32_supported(K, gs) (its buffers and scale/bias rows fit the LDS).
+bool smallm32_supported(uint32_t N, uint32_t K, uint32_t gs);
+hipError_t launch_gemm_smallm32(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
+                                hipStream_t stream);
+
+// For 16 < m <= 64: the rows per small-m pass (32, or 16 where only the
+// one-tile kernel fits) if passes over slices of X are expected to beat the
+// tiled kernel (a grid of few tiles, each walking all of K), else 0.
+uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m);
 
 }  // namespace int8w
