@@ -197,7 +197,7 @@ int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const
  * multiplies the raw codes and applies each group's scale and bias to the
  * group's partial sums; larger m the tiled kernel, where the weight enters the
  * matrix cores as RNE_bf16(w[n,k]) (the dequantize_to value).  For
- * 16 < m <= 64 on a weight that gives the tiled kernel few tiles per CU (so
+ * 16 < m <= 128 on a weight that gives the tiled kernel few tiles per CU (so
  * that its time is set by walking all of in_features, whatever m), the rows
  * go through the small-m kernel in slices of 32 (16 where its two-tile form
  * does not fit the LDS) when that many passes over the weight are estimated

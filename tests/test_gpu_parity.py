@@ -297,7 +297,7 @@ def test_gemm_prefill_small(m, N, K, gs):
     assert_close(dev_to_bits(Y), Y_ref, A, f"gemm m={m} {N}x{K} gs{gs}")
 
 
-# 16 < m <= 64 on weights that give the tiled kernel few tiles per CU: the
+# 16 < m <= 128 on weights that give the tiled kernel few tiles per CU: the
 # rows go through the small-m kernel 32 at a time (two X tiles per pass; a
 # slice of at most 16 rows takes the one-tile form).  Every row is checked
 # against the oracle, and every slice of two or more rows bit for bit against
@@ -310,6 +310,7 @@ def test_gemm_prefill_small(m, N, K, gs):
     (64, 4096, 14336, 64),    # 8B down projection
     (50, 4096, 4096, 64),     # two passes, the second of 18 rows
     (36, 300, 8192, 128),     # a 32-row pass and a 4-row one-tile pass
+    (96, 1024, 8192, 64),     # three passes
 ])
 def test_gemm_in_slices_of_32_rows(m, N, K, gs):
     log(f"gemm 32-row slices m={m} N={N} K={K} gs={gs}")

@@ -338,7 +338,7 @@ int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m,
   const uint64_t K = w->in_features, N = w->out_features;
   if ((uint64_t)m * K > 0xFFFFFFFFull || (uint64_t)m * N > 0xFFFFFFFFull)
     return fail(INT8W_ERR_SHAPE, "m=%u rows too many for this weight", m);
-  // 16 < m <= 64 on a small grid: passes of the small-m kernel over slices of
+  // 16 < m <= 128 on a small grid: passes of the small-m kernel over slices of
   // 32 (or 16) rows
   const bool sm_ok = smallm_supported(w->in_features, w->group_size);
   const uint32_t slice = m > 16u ? gemm_smallm_slice_rows(view(w), m) : 0u;

@@ -811,14 +811,15 @@ hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t 
 // On the 128 x 64 grids (fewer than ~3/4 of a 128 x 128 tile per CU) the
 // tiled kernel's time hardly depends on m: one workgroup per CU walks all of
 // K, about 0.42 us per 64-deep step for each round of tiles over the CUs.  A
-// small-m pass streams the weight once: about 3.5 TB/s plus ~3 us with two X
-// tiles (32 rows), 4 TB/s plus ~3 us with one.  Measured (graph-timed),
-// 32-row passes against the tiled kernel: 4096 x 14336 gs64, m = 32 / 64:
-// 24 / 46 against 90 / 91 us; 4096 x 4096, m = 32 / 64: 10 / 19 against 28 /
-// 29 us; 8192 x 28672 gs128, m = 64: 136 against 175 us; 14336 x 4096 (224
-// such tiles), m = 32 / 48: 25 / 48 against 30 / 30 us.
+// small-m pass streams the weight once: about 3 TB/s plus ~3 us with two X
+// tiles (32 rows), 4 TB/s plus ~3 us with one.  The passes are taken when
+// they are estimated at least 10 % faster.  Measured (graph-timed), 32-row
+// passes against the tiled kernel: 4096 x 14336 gs64, m = 32 / 64 / 96 / 128:
+// 24 / 46 / 72 / 96 against 90 / 91 / 91 / 92 us; 4096 x 4096, m = 32 / 64:
+// 10 / 19 against 28 / 29 us; 8192 x 28672 gs128, m = 64: 136 against 175
+// us; 14336 x 4096 (224 such tiles), m = 32 / 48: 25 / 48 against 30 / 30 us.
 uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m) {
-  if (m <= 16u || m > 64u) return 0;
+  if (m <= 16u || m > 128u) return 0;
   const uint32_t cus = (uint32_t)device_cu_count();
   const int shape = prefill_shape(w, m, cus);
   if (shape != 4 && shape != 1) return 0;
@@ -830,14 +831,14 @@ uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m) {
   double t_pass;
   if (smallm32_supported(w.N, w.K, w.gs)) {
     rows = 32u;
-    t_pass = bytes / 3.5e6 + 3.0;  // us at 3.5 TB/s
+    t_pass = bytes / 3.0e6 + 3.0;  // us at 3 TB/s
   } else if (smallm_supported(w.K, w.gs)) {
     rows = 16u;
     t_pass = bytes / 4.0e6 + 3.0;
   } else {
     return 0;
   }
-  return (double)((m + rows - 1u) / rows) * t_pass < t_tiled ? rows : 0u;
+  return (double)((m + rows - 1u) / rows) * t_pass < 0.9 * t_tiled ? rows : 0u;
 }
 
 }  // namespace int8w

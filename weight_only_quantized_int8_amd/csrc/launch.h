@@ -66,7 +66,7 @@ bool smallm32_supported(uint32_t N, uint32_t K, uint32_t gs);
 hipError_t launch_gemm_smallm32(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                                 hipStream_t stream);
 
-// For 16 < m <= 64: the rows per small-m pass (32, or 16 where only the
+// For 16 < m <= 128: the rows per small-m pass (32, or 16 where only the
 // one-tile kernel fits) if passes over slices of X are expected to beat the
 // tiled kernel (a grid of few tiles, each walking all of K), else 0.
 uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m);
