@@ -311,6 +311,7 @@ def test_gemm_prefill_small(m, N, K, gs):
     (50, 4096, 4096, 64),     # two passes, the second of 18 rows
     (36, 300, 8192, 128),     # a 32-row pass and a 4-row one-tile pass
     (96, 1024, 8192, 64),     # three passes
+    (30, 77, 2112, 64),       # ragged rows, K ends inside the fifth 512-code block
 ])
 def test_gemm_in_slices_of_32_rows(m, N, K, gs):
     log(f"gemm 32-row slices m={m} N={N} K={K} gs={gs}")
