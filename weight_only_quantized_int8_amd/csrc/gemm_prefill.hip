@@ -790,15 +790,27 @@ hipError_t launch_gemm_prefill_tile(int t, const WeightView &w, const uint16_t *
 
 namespace {
 
-// Measured on MI355X: 256 x 128 tiles when they give at least ~3/4 of a tile
-// per CU, else 128 x 128, else 128 x 64 (fewer idle CUs); staged by DMA where
-// K allows (the 128 x 64 staged tiles: m = 512 on 4096 x 14336 in 107 us
-// against 135 us unstaged).
+// Where K allows the DMA-staged kernel (K % (8 gs) == 0) it runs 256 x 128 or
+// 128 x 64 tiles, whichever an estimate puts first: a 64-deep K step takes
+// about 0.85 us per round of 256 x 128 tiles over the CUs (half a round for a
+// last round at most half full, done as half-height tiles) and 0.45 us per
+// round of 128 x 64 ones (whole rounds: their half-height tiles are slow).
+// Measured (graph-timed) against the 128 x 128 single-role kernel the rule
+// used before: 4096 x 14336, m = 768 / 1024: 178 / 179 us against 229 / 234;
+// 4096 x 4096, m = 768 / 1024: 57 / 57 against 64 / 66; 14336 x 4096,
+// m = 256: 59 against 70.  Other K: 256 x 128 tiles when they give at least
+// ~3/4 of a tile per CU, else 128 x 128, else 128 x 64.
 int prefill_shape(const WeightView &w, uint32_t m, uint32_t cus) {
   const uint32_t t256 = ((m + 255u) / 256u) * ((w.N + 127u) / 128u);
+  if (w.K % (8u * w.gs) == 0u) {
+    const uint32_t t12864 = ((m + 127u) / 128u) * ((w.N + 63u) / 64u);
+    const uint32_t rem = t256 % cus;
+    const double r256 = t256 <= cus ? 1.0 : (double)(t256 / cus) + (rem == 0u ? 0.0 : 2u * rem <= cus ? 0.5 : 1.0);
+    const double r12864 = (double)((t12864 + cus - 1u) / cus);
+    return r256 * 0.85 <= r12864 * 0.45 ? 3 : 4;
+  }
   const uint32_t t128 = ((m + 127u) / 128u) * ((w.N + 127u) / 128u);
-  const bool staged = w.K % (8u * w.gs) == 0u;
-  return 4u * t256 >= 3u * cus ? (staged ? 3 : 2) : 4u * t128 >= 3u * cus ? 0 : staged ? 4 : 1;
+  return 4u * t256 >= 3u * cus ? 2 : 4u * t128 >= 3u * cus ? 0 : 1;
 }
 
 }  // namespace
