@@ -208,9 +208,10 @@ void orc_gemv_silu_gate_resid(const uint32_t *packed, const uint16_t *scales,
  * the target layout.  The pages give no formula; this is the plain affine
  * min/max reading, evaluated in fp32 one operation at a time:
  *   per group of gs consecutive values v of a row (BF16, widened exactly):
- *     lo = min v, hi = max v
+ *     lo = min v, hi = max v               a zero extreme (-0 or +0) is taken as +0,
+ *                                          so neither depends on the order of -0/+0
  *     s  = RNE_bf16((hi - lo) / 255)       fp32 subtraction, fp32 division
- *     b  = lo                              already a BF16 value; -0 taken as +0
+ *     b  = lo                              already a BF16 value
  *     q  = clamp(rint((v - b) / s), 0, 255)  fp32 subtraction and division,
  *                                           round half to even
  *   and q = 0 for every value of a group whose s is zero.
@@ -241,7 +242,8 @@ void orc_quantize(const uint16_t *w, int64_t N, int64_t K, int64_t gs, uint32_t 
         if (v < lo) lo = v;
         if (v > hi) hi = v;
       }
-      if (lo == 0.0f) lo = 0.0f; /* a zero minimum is taken as +0 */
+      if (lo == 0.0f) lo = 0.0f; /* a zero extreme is +0: an all-zero group has scale +0 and */
+      if (hi == 0.0f) hi = 0.0f; /* bias +0 whichever signed zero comes first               */
       float span = hi - lo;
       float sf = span / 255.0f;
       uint16_t s_bits = orc_f32_to_bf16_rne(sf);

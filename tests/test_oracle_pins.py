@@ -467,6 +467,33 @@ def test_quantize_constant_group_has_zero_scale_and_bias_equal_to_the_value():
     assert (_codes_of(packed) == 0).all()
 
 
+def test_quantize_signed_zero_extremes_do_not_depend_on_order():
+    # Reading of the trait page's quantize (no formula given): a zero extreme,
+    # -0 or +0, is +0.  An all-zero group then has scale and bias with every
+    # bit clear (0x0000), whichever signed zero comes first; a group whose
+    # maximum is a zero has span 0 - lo exactly, as if that zero were +0.
+    gs = 32
+    pz, nz = 0x0000, 0x8000
+    rows = [
+        [nz] + [pz] * (gs - 1),            # -0 first
+        [pz] + [nz] * (gs - 1),            # +0 first
+        [nz] * gs,                         # all -0
+        [pz, nz] * (gs // 2),              # alternating
+        [nz] * (gs - 1) + [0xBF80],        # max -0, min -1: span 1
+        [0xBF80] + [nz] * (gs - 1),        # same values, -1 first
+    ]
+    w = np.array(rows, dtype=np.uint16)
+    packed, s, b = oracle.quantize(w, gs)
+    for r in range(4):
+        assert s[r, 0] == 0x0000 and b[r, 0] == 0x0000, (r, hex(s[r, 0]), hex(b[r, 0]))
+    # span 1 -> scale RNE_bf16(1/255), bias -1; the zeros sit at code RNE(1/s)
+    s_exp = rne_bf16_of_fraction(Fraction(1, 255))
+    for r in (4, 5):
+        assert s[r, 0] == s_exp and b[r, 0] == 0xBF80
+    assert np.array_equal(_codes_of(packed)[4], _codes_of(packed)[5][::-1])
+    assert (_codes_of(packed)[:4] == 0).all()
+
+
 @pytest.mark.parametrize("gs", [32, 64, 128])
 def test_quantize_round_trip_bound_exact_rationals(gs):
     # |q*s + b - v| <= s/2 for every value, except the top of a group whose s
