@@ -67,23 +67,30 @@ enum {
   INT8W_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
 };
 
-/* Check a weight view the way the page's load method checks its tensors: all
+/* Source: "MlxInt8Weight", method load (its list of failure cases).
+ * Check a weight view the way the page's load method checks its tensors: all
  * three buffers present, in_features divisible by group_size (hence by 4, the
  * codes per word), the per-group shape implied.  Also checks group_size is
  * supported and the pointers are aligned.  Touches no device memory. */
 int int8w_validate(const int8w_weight *w);
 
-/* Bytes of the quantized storage: N*K codes + 2*2*N*(K/group_size) for the
+/* Source: the DynQuantizedStorage trait page, method storage_size_in_bytes
+ * (the analogue for this layout).
+ * Bytes of the quantized storage: N*K codes + 2*2*N*(K/group_size) for the
  * BF16 scales and biases; 0 for an invalid shape. */
 uint64_t int8w_storage_bytes(uint32_t out_features, uint32_t in_features, uint32_t group_size);
 
-/* dequantize_to: write the full dequantised weight as BF16 to `out`, row-major
+/* Source: "MlxInt8Weight", method dequantize_to (kernel mlx_int8_dequant; the
+ * output holds at least out*in*2 bytes).
+ * dequantize_to: write the full dequantised weight as BF16 to `out`, row-major
  * [out_features, in_features]; out[n*K + k] = RNE_bf16(w[n,k]) (round to
  * nearest, ties to even).  `out` must hold out_features*in_features*2 bytes;
  * exactly that many are written. */
 int int8_dequantize_to(const int8w_weight *w, uint16_t *out, uint64_t stream);
 
-/* gemv: y = W x.  x is BF16 [in_features]; y is BF16 with at least
+/* Source: "MlxInt8Weight", method gemv (kernel mlx_int8_gemv: y = W x, x
+ * BF16 [in], y BF16 with at least out elements).
+ * gemv: y = W x.  x is BF16 [in_features]; y is BF16 with at least
  * out_features elements, of which exactly out_features are written:
  * y[n] = RNE_bf16(sum_k w[n,k] * x[k]), accumulated in fp32. */
 int int8_gemv(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint64_t stream);
@@ -93,7 +100,7 @@ int int8_gemv(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint64_t st
  * biases with the layout of int8w_weight (rustdoc page of the DynQuantizedStorage
  * trait, method quantize; the pages give no formula, this is the plain affine
  * min/max reading).  Per group of group_size values v of a row, in fp32:
- *   lo = min v (a zero minimum taken as +0), hi = max v,
+ *   lo = min v, hi = max v (a zero extreme, -0 or +0, taken as +0),
  *   scale = RNE_bf16((hi - lo) / 255), bias = lo,
  *   q = clamp(rint((v - bias) / scale), 0, 255), and q = 0 when scale == 0.
  * Then |q*scale + bias - v| <= scale/2 except at the top of a group whose
@@ -178,20 +185,26 @@ typedef struct {
  * x). */
 int int8w_fp8_gemv(const int8w_fp8_weight *w, const uint16_t *x, uint16_t *y, uint64_t stream);
 
-/* gemv_silu_gate: y = W (silu(gate) * up) in one launch, silu(g) = g/(1+e^-g).
+/* Source: "MlxInt8Weight", method gemv_silu_gate (kernel
+ * mlx_int8_gemv_silu_gate: one launch, the gated product kept off memory).
+ * gemv_silu_gate: y = W (silu(gate) * up) in one launch, silu(g) = g/(1+e^-g).
  * gate and up are BF16 [in_features]; the product silu(gate)*up is formed in
  * fp32 on chip and never written to memory.  y as for int8_gemv. */
 int int8_gemv_silu_gate(const int8w_weight *w, const uint16_t *gate, const uint16_t *up, uint16_t *y,
                         uint64_t stream);
 
-/* gemv_silu_gate_resid: the above plus a residual, in one launch:
+/* Source: "MlxInt8Weight", method gemv_silu_gate_resid (the residual form of
+ * the fused gated product, one launch).
+ * gemv_silu_gate_resid: the above plus a residual, in one launch:
  * y[n] = RNE_bf16(x_resid[n] + sum_k w[n,k] * silu(gate[k]) * up[k]), the
  * residual added in fp32 before the single rounding.  x_resid is BF16
  * [out_features]; y may be x_resid itself. */
 int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const uint16_t *up,
                               const uint16_t *x_resid, uint16_t *y, uint64_t stream);
 
-/* gemm: Y = X W^T.  X is BF16 [m, in_features] and Y BF16 [m, out_features],
+/* Source: "MlxInt8Weight", method gemm (kernel mlx_int8_gemm: Y = X W^T for m
+ * rows; its one-thread-per-output design is not followed here).
+ * gemm: Y = X W^T.  X is BF16 [m, in_features] and Y BF16 [m, out_features],
  * both contiguous row-major.  Y[i,n] = RNE_bf16(sum_k w[n,k] * X[i,k]) with fp32
  * accumulation.  m = 1 runs the gemv; 2 <= m <= 16 the small-m kernel, which
  * multiplies the raw codes and applies each group's scale and bias to the

@@ -67,6 +67,38 @@ def test_quantize_special_groups():
     assert (b_ref[0] == 0).all() and (b_ref[1, :2] == 0).all()  # zero minimum is +0
 
 
+@pytest.mark.parametrize("gs", [32, 64, 128])
+def test_quantize_signed_zero_groups(gs):
+    # all-zero groups in every order of -0 and +0, and groups whose maximum is
+    # a zero: scale and bias follow the oracle bit for bit (a zero extreme is
+    # +0 on both sides, so the lane order of the GPU min/max does not matter)
+    log(f"quantize signed-zero groups gs={gs}")
+    N, K = 12, 4 * gs
+    rng = np.random.Generator(np.random.PCG64(70_400 + gs))
+    w = synth.gen_dense_weight(rng, N, K)
+    pz, nz = np.uint16(0x0000), np.uint16(0x8000)
+    for n in range(N):
+        for g in range(K // gs):
+            sl = slice(g * gs, (g + 1) * gs)
+            kind = (n + g) % 6
+            if kind == 0:
+                w[n, sl] = nz; w[n, g * gs] = pz                    # one +0 first, then -0
+            elif kind == 1:
+                w[n, sl] = pz; w[n, g * gs] = nz                    # one -0 first, then +0
+            elif kind == 2:
+                w[n, sl] = np.where(rng.random(gs) < 0.5, nz, pz)   # random signs
+            elif kind == 3:
+                w[n, sl] = nz                                       # all -0
+            elif kind == 4:
+                w[n, sl] = np.where(rng.random(gs) < 0.5, nz, pz)   # maximum a zero,
+                w[n, g * gs + int(rng.integers(gs))] = 0xBF80       # minimum -1
+    p_ref, s_ref, b_ref = oracle.quantize(w, gs)
+    p, s, b, _ = gpu_quantize(w, gs)
+    assert np.array_equal(s, s_ref) and np.array_equal(b, b_ref) and np.array_equal(p, p_ref)
+    zero_groups = np.array([[(n + g) % 6 < 4 for g in range(K // gs)] for n in range(N)])
+    assert (s_ref[zero_groups] == 0).all() and (b_ref[zero_groups] == 0).all()
+
+
 def test_quantize_then_dequantize_round_trip_matches_oracle():
     log("quantize -> dequantize_to round trip")
     N, K, gs = 1024, 2048, 64

@@ -6,9 +6,9 @@
 // fp32, one operation at a time (the CPU oracle takes the same steps, so the
 // codes agree bit for bit):
 //   per group of gs consecutive values v of a row:
-//     lo = min v, hi = max v
+//     lo = min v, hi = max v                    (a zero extreme, -0 or +0, is +0)
 //     s  = RNE_bf16((hi - lo) / 255)            (fp32 subtraction, IEEE division)
-//     b  = lo                                   (a BF16 value already; -0 taken as +0)
+//     b  = lo                                   (a BF16 value already)
 //     q  = clamp(rint((v - b) / s), 0, 255)     (IEEE division, ties to even)
 //   and q = 0 for a group whose s is zero.  Inputs must be finite.
 //
@@ -129,7 +129,11 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(const uint16_t *__restri
           lo = fminf(lo, __shfl_xor(lo, off, 64));
           hi = fmaxf(hi, __shfl_xor(hi, off, 64));
         }
-        if (lo == 0.0f) lo = 0.0f;  // a zero minimum is +0 (the bias of an all-zero group is +0)
+        // A zero extreme is +0: the cross-lane min/max do not follow element
+        // order, so which signed zero survives is arbitrary; normalising both
+        // makes an all-zero group's scale and bias +0 whatever the order.
+        if (lo == 0.0f) lo = 0.0f;
+        if (hi == 0.0f) hi = 0.0f;
         const float sf = __fdiv_rn(hi - lo, 255.0f);
         const uint16_t s_bits = to_bf16_bits(sf);
         const uint16_t b_bits = to_bf16_bits(lo);  // exact
