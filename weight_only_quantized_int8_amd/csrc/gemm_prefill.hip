@@ -709,11 +709,13 @@ hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, 
   const uint32_t ntiles = (w.N + BN - 1) / BN;
   // When the full tiles leave a last round at most half full, the N tiles of
   // that round are done as half-height tiles (twice as many, about half the
-  // time each) in one last round.
+  // time each) in one last round.  Only for the 256-row tile: 64-row half
+  // tiles were slow, and the dispatcher picks 128 x 64 tiles only for grids
+  // of about one round anyway.
   const uint32_t cus = (uint32_t)device_cu_count();
   const uint32_t full = mtiles * ntiles, rem = full % cus;
   uint32_t nt_half = 0;
-  if (full > cus && rem != 0 && 2u * rem <= cus) {
+  if (BM == 256 && full > cus && rem != 0 && 2u * rem <= cus) {
     nt_half = (rem + mtiles - 1) / mtiles;
     if (nt_half >= ntiles) nt_half = 0;
   }
@@ -794,24 +796,35 @@ namespace {
 // 128 x 64 tiles, whichever an estimate puts first: a 64-deep K step takes
 // about 0.85 us per round of 256 x 128 tiles over the CUs (half a round for a
 // last round at most half full, done as half-height tiles) and 0.45 us per
-// round of 128 x 64 ones (whole rounds: their half-height tiles are slow).
-// Measured (graph-timed) against the 128 x 128 single-role kernel the rule
-// used before: 4096 x 14336, m = 768 / 1024: 178 / 179 us against 229 / 234;
-// 4096 x 4096, m = 768 / 1024: 57 / 57 against 64 / 66; 14336 x 4096,
-// m = 256: 59 against 70.  Other K: 256 x 128 tiles when they give at least
-// ~3/4 of a tile per CU, else 128 x 128, else 128 x 64.
-int prefill_shape(const WeightView &w, uint32_t m, uint32_t cus) {
+// round of 128 x 64 ones (whole rounds).  Measured (graph-timed) against the
+// 128 x 128 single-role kernel the rule used before: 4096 x 14336, m = 768 /
+// 1024: 178 / 179 us against 229 / 234; 4096 x 4096, m = 768 / 1024: 57 / 57
+// against 64 / 66; 14336 x 4096, m = 256: 59 against 70.  Other K: 256 x 128
+// tiles when they give at least ~3/4 of a tile per CU, else 128 x 128, else
+// 128 x 64 (about 0.42 us per step and round).
+struct PrefillPick {
+  int shape;        // launch_gemm_prefill_tile's shape number
+  double est_us;    // estimated kernel time, or a negative value when no estimate is calibrated
+};
+
+PrefillPick prefill_pick(const WeightView &w, uint32_t m, uint32_t cus) {
+  const double ksteps = (double)((w.K + 63u) / 64u);
   const uint32_t t256 = ((m + 255u) / 256u) * ((w.N + 127u) / 128u);
+  const uint32_t t12864 = ((m + 127u) / 128u) * ((w.N + 63u) / 64u);
+  const double r12864 = (double)((t12864 + cus - 1u) / cus);
   if (w.K % (8u * w.gs) == 0u) {
-    const uint32_t t12864 = ((m + 127u) / 128u) * ((w.N + 63u) / 64u);
     const uint32_t rem = t256 % cus;
     const double r256 = t256 <= cus ? 1.0 : (double)(t256 / cus) + (rem == 0u ? 0.0 : 2u * rem <= cus ? 0.5 : 1.0);
-    const double r12864 = (double)((t12864 + cus - 1u) / cus);
-    return r256 * 0.85 <= r12864 * 0.45 ? 3 : 4;
+    const double e256 = r256 * 0.85 * ksteps, e12864 = r12864 * 0.45 * ksteps;
+    return e256 <= e12864 ? PrefillPick{3, e256} : PrefillPick{4, e12864};
   }
   const uint32_t t128 = ((m + 127u) / 128u) * ((w.N + 127u) / 128u);
-  return 4u * t256 >= 3u * cus ? 2 : 4u * t128 >= 3u * cus ? 0 : 1;
+  if (4u * t256 >= 3u * cus) return {2, -1.0};
+  if (4u * t128 >= 3u * cus) return {0, -1.0};
+  return {1, r12864 * 0.42 * ksteps};
 }
+
+int prefill_shape(const WeightView &w, uint32_t m, uint32_t cus) { return prefill_pick(w, m, cus).shape; }
 
 }  // namespace
 
@@ -820,24 +833,21 @@ hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t 
   return launch_gemm_prefill_tile(prefill_shape(w, m, (uint32_t)device_cu_count()), w, X, Y, m, stream);
 }
 
-// On the 128 x 64 grids (fewer than ~3/4 of a 128 x 128 tile per CU) the
-// tiled kernel's time hardly depends on m: one workgroup per CU walks all of
-// K, about 0.42 us per 64-deep step for each round of tiles over the CUs.  A
+// For 16 < m <= 128 the tiled kernel often runs about one round of tiles, one
+// workgroup per CU walking all of K, so its time hardly depends on m.  A
 // small-m pass streams the weight once: about 3 TB/s plus ~3 us with two X
 // tiles (32 rows), 4 TB/s plus ~3 us with one.  The passes are taken when
-// they are estimated at least 10 % faster.  Measured (graph-timed), 32-row
-// passes against the tiled kernel: 4096 x 14336 gs64, m = 32 / 64 / 96 / 128:
-// 24 / 46 / 72 / 96 against 90 / 91 / 91 / 92 us; 4096 x 4096, m = 32 / 64:
-// 10 / 19 against 28 / 29 us; 8192 x 28672 gs128, m = 64: 136 against 175
-// us; 14336 x 4096 (224 such tiles), m = 32 / 48: 25 / 48 against 30 / 30 us.
+// they are estimated at least 10 % faster than the tile the dispatcher would
+// pick (its estimate from prefill_pick; tiles without a calibrated estimate
+// keep the tiled kernel).  Measured (graph-timed), 32-row passes against the
+// tiled kernel: 4096 x 14336 gs64, m = 32 / 64 / 96 / 128: 24 / 46 / 72 / 96
+// against 90 / 91 / 91 / 92 us; 4096 x 4096, m = 32 / 64: 10 / 19 against 28
+// / 29 us; 8192 x 28672 gs128, m = 64: 136 against 175 us; 14336 x 4096 (224
+// such tiles), m = 32 / 48: 25 / 48 against 30 / 30 us.
 uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m) {
   if (m <= 16u || m > 128u) return 0;
-  const uint32_t cus = (uint32_t)device_cu_count();
-  const int shape = prefill_shape(w, m, cus);
-  if (shape != 4 && shape != 1) return 0;
-  const double tiles = (double)((m + 127u) / 128u) * (double)((w.N + 63u) / 64u);
-  const double rounds = (double)(uint32_t)((tiles + cus - 1.0) / cus);
-  const double t_tiled = rounds * (double)((w.K + 63u) / 64u) * 0.42;
+  const PrefillPick pick = prefill_pick(w, m, (uint32_t)device_cu_count());
+  if (pick.est_us < 0.0) return 0;
   const double bytes = (double)w.N * w.K + 4.0 * w.N * (w.K / w.gs);
   uint32_t rows;
   double t_pass;
@@ -850,7 +860,7 @@ uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m) {
   } else {
     return 0;
   }
-  return (double)((m + rows - 1u) / rows) * t_pass < 0.9 * t_tiled ? rows : 0u;
+  return (double)((m + rows - 1u) / rows) * t_pass < 0.9 * pick.est_us ? rows : 0u;
 }
 
 }  // namespace int8w
