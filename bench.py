@@ -8,20 +8,22 @@ and up outputs.  Weights of several layers are cycled so that successive steps
 stream different bytes and the 256 MB last-level cache cannot serve them.
 
 value = algorithmic bytes per step (codes + scales + biases of every weight,
-plus the activations each launch reads and writes) / measured time per step,
-in GB/s, with each layer's launches replayed as a HIP graph.  The roofline
-object reports the dominant kernel (the gate+up gemv_multi launch) from HIP
-events around a batched, graph-replayed run of that launch alone.  Secondary
-lines: the same layer as seven single-weight launches, the quantizer on an
-8B gate/up weight, the expert-indexed gemv over 8 experts of that shape (top-2
-routing, 1 and 4 tokens), the FP8 E4M3 gemv (per-row and 128 x 128 block
-scales) on the 8B FFN shapes, dequantize_to and the gated GEMV of the 70B-shaped
-FFN, the small-batch gemm (m = 2..16, and 32 and 64 at group size 64) and the
-prefill gemm (m = 512, 2048) in TFLOP/s.
+plus the activations each launch reads and writes) / time per step, in GB/s:
+each layer's launches replayed as a HIP graph, a HIP event after every step,
+the median of 20 batches of consecutive steps.  The roofline object reports
+the dominant kernel (the gate+up gemv_multi launch), the median over graph
+replays of that launch alone.  Secondary lines, each the median of 20 graph
+replays over rotated weights: every single-launch call of the decode
+workloads (gemv on the gate, q/o and k/v shapes, gemv_silu_gate and
+gemv_silu_gate_resid on the 8B and 70B down shapes), dequantize_to of the
+70B-shaped weight, the own-built streaming read and copy (the achievable
+ceilings beside the nominal 8 TB/s), the quantizer, the expert-indexed gemv,
+the FP8 gemv, the small-batch gemm and the prefill gemm in TFLOP/s.
+cpu_baseline: the oracle on the host cores, at all cores and at one thread.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
-       python bench.py --profile-only     # dominant kernel + calibration copy, for rocprofv3
-       python bench.py --profile-prefill  # the m = 2048 prefill gemm alone, for rocprofv3 counters
+       python bench.py --profile NAME   # one launch alone + a calibration copy, for rocprofv3
+       python bench.py --traffic-from FETCH.csv WRITE.csv --target NAME   # write profiles/traffic_NAME.json
 """
 from __future__ import annotations
 
@@ -47,11 +49,6 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 LLC_BYTES = 256 << 20
 METRIC = "int8 GEMV achieved HBM GB/s (% of peak) at m=1; prefill GEMM TFLOP/s"
-# the device sources of the gate/up gemv kernel (its traffic record is void
-# once either changes)
-GEMV_SOURCES = [os.path.join(ROOT, "weight_only_quantized_int8_amd", "csrc", f)
-                for f in ("gemv.hip", "common.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_gate_up_traffic.json")
 
 
 def gemv_bytes(N, K, gs):
@@ -195,11 +192,12 @@ def time_graph_steps(graphs, steps):
     return start.elapsed_time(end) / 1e3 / steps
 
 
-def time_batches(fn, iters, reps=5):
+def time_batches(fn, iters, reps=20):
     """Seconds per call: `iters` calls (fn(0) .. fn(iters-1), which rotate
     their inputs) captured in one HIP graph after a warm-up, the graph replayed
-    `reps` times between two HIP events on the capturing stream; median over
-    the replays.  Graph replay keeps host launch cost out of the kernel time."""
+    `reps` times, a HIP event on the capturing stream after each replay; the
+    median over the replays (batches).  Graph replay keeps host launch cost out
+    of the kernel time."""
     for i in range(min(iters, 3)):
         fn(i)
     torch.cuda.synchronize()
@@ -209,32 +207,197 @@ def time_batches(fn, iters, reps=5):
             fn(i)
     g.replay()
     torch.cuda.synchronize()
-    times = []
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for r in range(reps):
         g.replay()
-        b.record()
-        b.synchronize()
-        times.append(a.elapsed_time(b) / 1e3 / iters)
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    times = [ev[r].elapsed_time(ev[r + 1]) / 1e3 / iters for r in range(reps)]
     del g
     return float(np.median(times))
+
+
+# ---------------------------------------------------------------- single launches (secondary lines and profiles)
+#
+# Each target is one call of the library, set up on rotated weights (enough
+# copies that the 256 MB last-level cache cannot serve repeats), with its
+# algorithmic bytes (or flops) per launch, the kernel that runs it and that
+# kernel's device sources (a traffic record is void once they change).
+
+CSRC = os.path.join(ROOT, "weight_only_quantized_int8_amd", "csrc")
+
+
+def _src(*names):
+    return [os.path.join(CSRC, n) for n in names] + [os.path.join(CSRC, "common.h")]
+
+
+class Target:
+    def __init__(self, name, kernel, sources, iters, bytes_=None, flops=None, note=""):
+        self.name, self.kernel, self.sources, self.iters = name, kernel, sources, iters
+        self.bytes, self.flops, self.note = bytes_, flops, note
+
+    def setup(self, dev):  # -> callable(i) launching call i
+        raise NotImplementedError
+
+
+class GemvTarget(Target):
+    def __init__(self, name, N, K, gs, kind, iters=30):
+        b = gated_resid_bytes(N, K, gs) if kind == "silu_gate_resid" else \
+            gemv_bytes(N, K, gs) + (2 * K if kind == "silu_gate" else 0)
+        super().__init__(name, "k_gemv<", _src("gemv.hip"), iters, bytes_=b,
+                         note=f"{kind} {N}x{K} gs{gs}")
+        self.N, self.K, self.gs, self.kind = N, K, gs, kind
+
+    def setup(self, dev):
+        N, K, gs = self.N, self.K, self.gs
+        ws = make_weights(5000 + N + K + gs, N, K, gs, copies_for(N * K), dev)
+        rng = np.random.default_rng(N + K)
+        g, u = bits_dev(synth.gen_act(rng, K), dev), bits_dev(synth.gen_act(rng, K), dev)
+        r = bits_dev(synth.gen_act(rng, N), dev)
+        y = torch.empty(N, dtype=torch.bfloat16, device=dev)
+        if self.kind == "gemv":
+            return lambda i: ws[i % len(ws)].gemv(g, y)
+        if self.kind == "silu_gate":
+            return lambda i: ws[i % len(ws)].gemv_silu_gate(g, u, y)
+        return lambda i: ws[i % len(ws)].gemv_silu_gate_resid(g, u, r, y)
+
+
+class GateUpTarget(Target):
+    """The decode step's dominant launch: gemv_multi over gate and up."""
+
+    def __init__(self):
+        super().__init__("gate_up", "k_gemv_multi", _src("gemv.hip"), 48,
+                         bytes_=launch_bytes("multi", ("gate", "up")), note="gemv_multi 2 x 14336x4096 gs64")
+
+    def setup(self, dev):
+        N, K = 14336, 4096
+        pairs = [make_weights(5100 + 2 * c, N, K, GS, 1, dev) + make_weights(5101 + 2 * c, N, K, GS, 1, dev)
+                 for c in range(copies_for(2 * N * K))]
+        x = bits_dev(synth.gen_act(np.random.default_rng(5), K), dev)
+        ys = [torch.empty(N, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        return lambda i: gemv_multi(pairs[i % len(pairs)], x, ys)
+
+
+class DequantTarget(Target):
+    def __init__(self, N=28672, K=8192, gs=128):
+        super().__init__("dequant", "k_dequant", _src("dequant.hip"), 10, bytes_=dequant_bytes(N, K, gs),
+                         note=f"dequantize_to {N}x{K} gs{gs}")
+        self.N, self.K, self.gs = N, K, gs
+
+    def setup(self, dev):
+        N, K, gs = self.N, self.K, self.gs
+        ws = make_weights(4000, N, K, gs, 2, dev)
+        outs = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        return lambda i: ws[i % 2].dequantize_to(outs[i % 2])
+
+
+class GemmTarget(Target):
+    def __init__(self, name, m, N, K, gs, kernel, iters):
+        fl = 2 * m * N * K
+        super().__init__(name, kernel, _src("gemm_prefill.hip" if m > 16 else "gemm_smallm.hip"), iters,
+                         bytes_=gemm_bytes(N, K, gs, m), flops=fl, note=f"gemm m={m} {N}x{K} gs{gs}")
+        self.m, self.N, self.K, self.gs = m, N, K, gs
+
+    def setup(self, dev):
+        m, N, K, gs = self.m, self.N, self.K, self.gs
+        ws = make_weights(2000 + N + gs, N, K, gs, copies_for(N * K) if m <= 128 else 2, dev)
+        X = bits_dev(synth.gen_act(np.random.default_rng(N + gs + m), (m, K)), dev)
+        Y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+        return lambda i: ws[i % len(ws)].gemm(X, Y)
+
+
+class StreamReadTarget(Target):
+    """The own-built streaming read over the bytes of one gate/up weight's codes."""
+
+    def __init__(self, nbytes=14336 * 4096):
+        super().__init__("stream_read", "k_stream_read", _src("measure.hip"), 30, bytes_=nbytes,
+                         note=f"plain streaming read of {nbytes} bytes")
+        self.n = nbytes
+
+    def setup(self, dev):
+        bufs = [torch.empty(self.n, dtype=torch.uint8, device=dev) for _ in range(copies_for(self.n))]
+        for b in bufs:
+            b.fill_(1)
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        return lambda i: binding.int8w_stream_read(bufs[i % len(bufs)].data_ptr(), self.n, sink.data_ptr(),
+                                                   torch.cuda.current_stream().cuda_stream)
+
+
+class StreamCopyTarget(Target):
+    def __init__(self, nbytes=256 << 20):
+        super().__init__("stream_copy", "k_stream_copy", _src("measure.hip"), 10, bytes_=2 * nbytes,
+                         note=f"plain streaming copy of {nbytes} bytes (read + write)")
+        self.n = nbytes
+
+    def setup(self, dev):
+        src = [torch.ones(self.n, dtype=torch.uint8, device=dev) for _ in range(2)]
+        dst = [torch.empty(self.n, dtype=torch.uint8, device=dev) for _ in range(2)]
+        return lambda i: binding.int8w_stream_copy(src[i % 2].data_ptr(), dst[i % 2].data_ptr(), self.n,
+                                                   torch.cuda.current_stream().cuda_stream)
+
+
+TARGETS = {t.name: t for t in [
+    GateUpTarget(),
+    GemvTarget("gate", 14336, 4096, 64, "gemv"),
+    GemvTarget("qo", 4096, 4096, 64, "gemv"),
+    GemvTarget("kv", 1024, 4096, 64, "gemv"),
+    GemvTarget("silu_gate", 4096, 14336, 64, "silu_gate"),
+    GemvTarget("down", 4096, 14336, 64, "silu_gate_resid"),
+    GemvTarget("down70b", 8192, 28672, 128, "silu_gate_resid"),
+    DequantTarget(),
+    GemmTarget("smallm16", 16, 4096, 14336, 64, "k_gemm_smallm", 30),
+    GemmTarget("prefill512", 512, 4096, 14336, 64, "k_gemm_prefill", 10),
+    GemmTarget("prefill2048", 2048, 14336, 4096, 64, "k_gemm_prefill", 10),
+    StreamReadTarget(),
+    StreamCopyTarget(),
+]}
+
+
+def traffic_file(name):
+    return os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+
+
+def traffic_record(name):
+    """HBM bytes per launch of a target from committed rocprofv3 counters, if still current."""
+    path = traffic_file(name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != source_sha(TARGETS[name].sources):
+        return None  # the kernel changed since the counters were taken
+    return rec
+
+
+def measure_target(t, dev):
+    fn = t.setup(dev)
+    s = time_batches(fn, t.iters)
+    out = {"us": s * 1e6, "call": t.note}
+    if t.bytes is not None:
+        out["GB/s"] = t.bytes / s / 1e9
+        out["frac_hbm"] = t.bytes / s / 1e9 / HBM_PEAK_GBS
+    if t.flops is not None:
+        out["TFLOP/s"] = t.flops / s / 1e12
+        out["frac_mfma_bf16"] = t.flops / s / 1e12 / BF16_MFMA_PEAK_TFLOPS
+    rec = traffic_record(t.name)
+    if rec:
+        out["hbm_traffic_ratio"] = rec["ratio_to_algorithmic"]
+    del fn
+    torch.cuda.empty_cache()
+    return out
 
 
 # ---------------------------------------------------------------- secondary measurements
 
 def secondary(dev, quick):
     res = {}
-    N, K, gs = 28672, 8192, 128  # 70B-shaped FFN: dequantize_to of the up/gate weight
-    ws = make_weights(4000, N, K, gs, 2, dev)
-    outs = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(2)]
-    for i in range(3):
-        ws[i % 2].dequantize_to(outs[i % 2])
-    t = time_batches(lambda i: ws[i % 2].dequantize_to(outs[i % 2]), 10)
-    b = dequant_bytes(N, K, gs)
-    res["dequantize_to_28672x8192_gs128"] = {"us": t * 1e6, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
-    del ws, outs
-    torch.cuda.empty_cache()
+    # the single-launch calls of the decode workloads, the calibration streams,
+    # dequantize_to of the 70B-shaped weight, and the profiled gemm shapes
+    for name in ("gate", "qo", "kv", "silu_gate", "down", "down70b", "dequant", "stream_read", "stream_copy"):
+        t = TARGETS[name]
+        res[name] = measure_target(t, dev)
+        print(f"# {name}: {res[name]['us']:.2f} us", file=sys.stderr, flush=True)
 
     N, K, gs = 14336, 4096, 64  # quantize an 8B gate/up weight (BF16 -> codes, scales, biases)
     rng = np.random.Generator(np.random.PCG64(4200))
@@ -301,18 +464,6 @@ def secondary(dev, quick):
             del ws, codes, sc
     torch.cuda.empty_cache()
 
-    N, K, gs = 8192, 28672, 128  # 70B-shaped down projection, gated + residual
-    ws = make_weights(4100, N, K, gs, copies_for(N * K), dev)
-    rng = np.random.default_rng(5)
-    g, u, r = (bits_dev(synth.gen_act(rng, n), dev) for n in (K, K, N))
-    y = torch.empty(N, dtype=torch.bfloat16, device=dev)
-    t = time_batches(lambda i: ws[i % len(ws)].gemv_silu_gate_resid(g, u, r, y), 30)
-    b = gated_resid_bytes(N, K, gs)
-    res["gemv_silu_gate_resid_8192x28672_gs128"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
-                                                   "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
-    del ws
-    torch.cuda.empty_cache()
-
     for N, K in ((14336, 4096), (4096, 14336)):  # small-batch decode and prefill gemm
         for gs in ((64,) if quick else (32, 64, 128)):
             ws = make_weights(2000 + N + gs, N, K, gs, copies_for(N * K), dev)
@@ -325,7 +476,7 @@ def secondary(dev, quick):
                 res[f"gemm_m{m}_{N}x{K}_gs{gs}"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
                                                     "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
             if gs == 64:
-                for m in (32, 64):  # batched decode: 16-row passes on the 4096-row weight
+                for m in (32, 64):  # batched decode: 32-row passes on the 4096-row weight
                     X = bits_dev(synth.gen_act(rng, (m, K)), dev)
                     Y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
                     t = time_batches(lambda i: ws[i % len(ws)].gemm(X, Y), 20)
@@ -342,23 +493,45 @@ def secondary(dev, quick):
                                                       "frac_mfma_bf16": fl / t / 1e12 / BF16_MFMA_PEAK_TFLOPS}
             del ws
             torch.cuda.empty_cache()
+    # a weight whose one round of 256 x 128 tiles walks all of K: m = 32 goes
+    # through one 32-row small-m pass
+    N, K, gs, m = 18944, 3584, 64, 32
+    ws = make_weights(2100, N, K, gs, copies_for(N * K), dev)
+    X = bits_dev(synth.gen_act(np.random.default_rng(2101), (m, K)), dev)
+    Y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+    t = time_batches(lambda i: ws[i % len(ws)].gemm(X, Y), 20)
+    b = gemm_bytes(N, K, gs, m)
+    res[f"gemm_m{m}_{N}x{K}_gs64"] = {"us": t * 1e6, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
+                                      "TFLOP/s": 2.0 * m * N * K / t / 1e12}
+    del ws
+    torch.cuda.empty_cache()
     return res
 
 
 # ---------------------------------------------------------------- CPU oracle baseline
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle computing the same step (each weight's product, the gated down projection)."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _decode_step_rate(budget_s, max_steps):
+    """The oracle computing the decode step (each weight's product, the gated
+    down projection) repeatedly for about budget_s seconds: (GB/s, steps, s)."""
     import oracle
     ws = {}
     for si, (name, N, K) in enumerate(WEIGHTS):
         rng = np.random.Generator(np.random.PCG64(synth.make_seed(1, si)))
         ws[name] = synth.gen_weight(rng, N, K, GS)
     rng = np.random.Generator(np.random.PCG64(synth.make_seed(1, 99)))
-    x = synth.gen_act(rng, 4096)
-    r = synth.gen_act(rng, 4096)
-    g = synth.gen_act(rng, 14336)
-    u = synth.gen_act(rng, 14336)
+    x, r = synth.gen_act(rng, 4096), synth.gen_act(rng, 4096)
+    g, u = synth.gen_act(rng, 14336), synth.gen_act(rng, 14336)
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -369,32 +542,59 @@ def cpu_baseline(budget_s=12.0):
         oracle.gemv_silu_gate_resid(w.packed, w.scales, w.biases, GS, g, u, r)
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 200:
+        if el >= budget_s or n >= max_steps:
             break
-    return {"value": plan_bytes(FUSED) * n / el / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"{n} decode-layer steps (the same products, shapes and byte count as the GPU step), "
-                      f"{el:.1f} s"}
+    return plan_bytes(FUSED) * n / el / 1e9, n, el
 
 
-def traffic_record():
-    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counters, if still current."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    with open(TRAFFIC_FILE) as f:
-        rec = json.load(f)
-    if rec.get("kernel_source_sha256") != source_sha(GEMV_SOURCES):
-        return None  # the kernel changed since the counters were taken
-    return rec
+def cpu_baseline():
+    """The oracle, as it is, on the host cores: the decode step at all cores
+    (the reported value) and at one thread, then bounded samples of the
+    prefill gemm and of the 70B-shaped dequantize_to at all cores."""
+    import oracle
+    cores = oracle.max_threads()
+    v, n, el = _decode_step_rate(8.0, 200)
+    out = {"value": v, "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": f"{n} decode-layer steps (the same products, shapes and byte count as the GPU step), "
+                     f"{el:.1f} s on {cores} threads",
+           "cpu_model": cpu_model()}
+    oracle.set_threads(1)
+    try:
+        v1, n1, el1 = _decode_step_rate(5.0, 50)
+    finally:
+        oracle.set_threads(cores)
+    out["one_thread"] = {"value": v1, "unit": "GB/s", "cores": 1,
+                         "sample": f"{n1} decode-layer steps, {el1:.1f} s"}
+    # prefill: 128 rows of the m = 512 workload on the 8B gate/up weight
+    rng = np.random.Generator(np.random.PCG64(7100))
+    w = synth.gen_weight(rng, 14336, 4096, GS)
+    X = synth.gen_act(rng, (128, 4096))
+    t0 = time.perf_counter()
+    oracle.gemm(w.packed, w.scales, w.biases, GS, X)
+    el = time.perf_counter() - t0
+    out["prefill_gemm"] = {"value": 2.0 * 128 * 14336 * 4096 / el / 1e9, "unit": "GFLOP/s", "cores": cores,
+                           "sample": f"gemm on 128 rows of X against the 14336x4096 gs64 weight, {el:.1f} s"}
+    # dequantize_to: 8192 rows of the 28672 x 8192 gs128 weight, three times
+    w = synth.gen_weight(rng, 8192, 8192, 128)
+    t0 = time.perf_counter()
+    for _ in range(3):
+        oracle.dequantize_to(w.packed, w.scales, w.biases, 128)
+    el = time.perf_counter() - t0
+    out["dequantize_to"] = {"value": 3 * dequant_bytes(8192, 8192, 128) / el / 1e9, "unit": "GB/s", "cores": cores,
+                            "sample": f"dequantize_to of 8192 rows of the 28672x8192 gs128 weight, 3 times, "
+                                      f"{el:.2f} s"}
+    return out
 
 
-def write_traffic_record(fetch_csv, write_csv):
+def write_traffic_record(name, fetch_csv, write_csv):
     """Turn two rocprofv3 --pmc counter_collection.csv files of `bench.py
-    --profile-only` (FETCH_SIZE, then WRITE_SIZE) into the traffic record:
-    median KiB per dispatch of the dominant kernel, scaled by what the same
+    --profile NAME` (FETCH_SIZE, then WRITE_SIZE) into the target's traffic
+    record: median KiB per dispatch of its kernel, scaled by what the same
     counter reads for the 256 MiB calibration copy."""
     import csv
     import statistics
+
+    t = TARGETS[name]
 
     def per_kernel(path):
         out = {}
@@ -404,29 +604,28 @@ def write_traffic_record(fetch_csv, write_csv):
         return out
 
     f, w = per_kernel(fetch_csv), per_kernel(write_csv)
-    dom = [k for k in f if "k_gemv_multi" in k[0]]
+    dom = [k for k in f if t.kernel in k[0]]
     cal = [k for k in f if "copyBuffer" in k[0] and max(f[k]) > 100000]
     if len(dom) != 1 or len(cal) != 1:
-        raise SystemExit(f"expected one dominant kernel and one calibration copy, got {dom} / {cal}")
+        raise SystemExit(f"expected one {t.kernel} kernel and one calibration copy, got {dom} / {cal}")
     dom, cal = dom[0], cal[0]
     copy_kib = (256 << 20) / 1024
     ff, wf = copy_kib / statistics.median(f[cal]), copy_kib / statistics.median(w[cal])
     fk, wk = statistics.median(f[dom]), statistics.median(w[dom])
     hbm = fk * 1024 * ff + wk * 1024 * wf
-    alg = launch_bytes("multi", ("gate", "up"))
-    short = re.search(r"(k_\w+<[^>]*>)", dom[0])
-    rec = {"kernel": (short.group(1) if short else dom[0]) + " (gemv_multi: gate+up, 2 x 14336x4096, group_size 64)",
-           "kernel_source_sha256": source_sha(GEMV_SOURCES),
-           "kernel_sources": [os.path.relpath(p, ROOT) for p in GEMV_SOURCES],
+    short = re.search(r"(k_\w+<[^>]*>|k_\w+)", dom[0])
+    rec = {"kernel": (short.group(1) if short else dom[0]) + f" ({t.note})",
+           "kernel_source_sha256": source_sha(t.sources),
+           "kernel_sources": [os.path.relpath(p, ROOT) for p in t.sources],
            "dispatches": len(f[dom]),
            "fetch_size_kib_median": fk, "write_size_kib_median": wk,
            "calibration_copy_bytes": 256 << 20,
            "calibration_fetch_size_kib": statistics.median(f[cal]),
            "calibration_write_size_kib": statistics.median(w[cal]),
            "fetch_factor": ff, "write_factor": wf,
-           "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": alg,
-           "ratio_to_algorithmic": hbm / alg}
-    with open(TRAFFIC_FILE, "w") as fo:
+           "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": t.bytes,
+           "ratio_to_algorithmic": hbm / t.bytes}
+    with open(traffic_file(name), "w") as fo:
         json.dump(rec, fo, indent=1)
     print(json.dumps(rec, indent=1))
 
@@ -456,40 +655,52 @@ def n_rotated_layers():
     return max(2, -(-2 * LLC_BYTES // per_layer))
 
 
-def profile_only(dev, replays=2):
-    """For rocprofv3: the dominant launch exactly as timed region 2 runs it
-    (graph replays), then a plain 256 MiB device copy that calibrates the
-    FETCH_SIZE / WRITE_SIZE counters."""
-    dl = DecodeLayers(dev, n_rotated_layers())
-    g, per_replay = dominant_graph(dl)
-    for _ in range(replays):
-        g.replay()
-    torch.cuda.synchronize()
+def calibration_copy(dev):
+    """Five plain 256 MiB device copies: what FETCH_SIZE / WRITE_SIZE read for
+    a known byte count scales the counters of the profiled kernel."""
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_only": True, "dominant_launches": per_replay * (replays + 1) + per_replay // 16,
-                      "calibration_copy_bytes": src.numel()}), flush=True)
+    return src.numel()
 
 
-def profile_prefill(dev, launches=12):
-    """For rocprofv3 counters of the prefill kernel: the m = 2048 gemm on the
-    8B gate/up weight [14336, 4096] gs64, launched `launches` times (after a
-    warm-up of the same launch) on two rotated weights."""
-    N, K, gs, m = 14336, 4096, 64, 2048
-    ws = make_weights(2000 + N + gs, N, K, gs, 2, dev)
-    rng = np.random.default_rng(N + gs)
-    X = bits_dev(synth.gen_act(rng, (m, K)), dev)
-    Y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
-    ws[0].gemm(X, Y)
+def profile_target(dev, name, replays=3):
+    """For rocprofv3: one target's launch alone, as bench.py times it (a HIP
+    graph of its rotated calls, replayed), then the calibration copy."""
+    t = TARGETS[name]
+    if name == "gate_up":  # exactly the roofline measurement's graph
+        dl = DecodeLayers(dev, n_rotated_layers())
+        g, per_replay = dominant_graph(dl)
+    else:
+        fn = t.setup(dev)
+        for i in range(min(t.iters, 3)):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(t.iters):
+                fn(i)
+        g.replay()
+        per_replay = t.iters
+    for _ in range(replays):
+        g.replay()
     torch.cuda.synchronize()
-    for i in range(launches):
-        ws[i % 2].gemm(X, Y)
-    torch.cuda.synchronize()
-    print(json.dumps({"profile_prefill": True, "m": m, "N": N, "K": K, "launches": launches + 1,
-                      "flops_per_launch": 2 * m * N * K}), flush=True)
+    nb = calibration_copy(dev)
+    print(json.dumps({"profile": name, "kernel": t.kernel, "call": t.note, "launches_timed": per_replay * replays,
+                      "algorithmic_bytes": t.bytes, "flops": t.flops, "calibration_copy_bytes": nb}), flush=True)
+
+
+def batch_medians(events, steps_per_event, n_batches):
+    """Seconds per step: the events bracket consecutive steps; they are split
+    into n_batches consecutive batches, and the median over the batches is
+    returned with the mean over all of them."""
+    per = [events[i].elapsed_time(events[i + 1]) / 1e3 for i in range(len(events) - 1)]
+    nb = max(1, min(n_batches, len(per)))
+    bounds = np.linspace(0, len(per), nb + 1).round().astype(int)
+    b = [sum(per[bounds[j]:bounds[j + 1]]) / ((bounds[j + 1] - bounds[j]) * steps_per_event) for j in range(nb)]
+    return float(np.median(b)), sum(per) / (len(per) * steps_per_event), nb
 
 
 def main():
@@ -500,14 +711,15 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--full-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-only", action="store_true")
-    ap.add_argument("--profile-prefill", action="store_true",
-                    help="only the m = 2048 prefill gemm, for rocprofv3 counters")
+    ap.add_argument("--profile", choices=sorted(TARGETS), help="one launch alone, for rocprofv3")
+    ap.add_argument("--profile-only", action="store_true", help="same as --profile gate_up")
+    ap.add_argument("--profile-prefill", action="store_true", help="same as --profile prefill2048")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the traffic record from two rocprofv3 --pmc runs of --profile-only, then exit")
+                    help="write profiles/traffic_<target>.json from two rocprofv3 --pmc runs of --profile, then exit")
+    ap.add_argument("--target", default="gate_up", choices=sorted(TARGETS), help="the target of --traffic-from")
     args = ap.parse_args()
     if args.traffic_from:
-        write_traffic_record(*args.traffic_from)
+        write_traffic_record(args.target, *args.traffic_from)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -515,11 +727,9 @@ def main():
     load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.profile_prefill:
-        profile_prefill(dev)
-        return
-    if args.profile_only:
-        profile_only(dev)
+    prof = args.profile or ("gate_up" if args.profile_only else "prefill2048" if args.profile_prefill else None)
+    if prof:
+        profile_target(dev, prof)
         return
 
     n_layers = n_rotated_layers()
@@ -531,31 +741,43 @@ def main():
         dl.step(i, FUSED)
     torch.cuda.synchronize()
 
-    # ---- timed region 1: K steps, each layer's launches replayed as one HIP graph
+    # ---- timed region 1: exactly K steps, each layer's launches replayed as
+    # one HIP graph; a HIP event after every step, the steps split into 20
+    # consecutive batches, value from the median batch
     graphs = dl.graphs(FUSED)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_s = time_graph_steps(graphs, args.steps)
+    ev[0].record()
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_s, step_mean_s, n_batches = batch_medians(ev, 1, 20)
     value = step_bytes / step_s / 1e9
 
     # ---- timed region 2: the dominant launch alone, back to back (see
-    # dominant_graph); HIP events on the launch stream around the replays.
+    # dominant_graph); a HIP event on the launch stream after every replay,
+    # median over at least 20 replays
     g_dom, dom_per_replay = dominant_graph(dl)
-    reps = max(2, -(-2 * args.steps // dom_per_replay))
-    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s2.record()
-    for _ in range(reps):
+    reps = max(20, -(-2 * args.steps // dom_per_replay))
+    ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev2[0].record()
+    for r in range(reps):
         g_dom.replay()
-    e2.record()
+        ev2[r + 1].record()
     torch.cuda.synchronize()
-    avg_dom = s2.elapsed_time(e2) / 1e3 / (reps * dom_per_replay)
+    avg_dom, mean_dom, _ = batch_medians(ev2, dom_per_replay, reps)
     b_dom = launch_bytes("multi", ("gate", "up"))
-    traffic = traffic_record()
+    traffic = traffic_record("gate_up")
     roofline = {"bound": "hbm", "achieved": b_dom / avg_dom / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": b_dom / avg_dom / 1e9 / HBM_PEAK_GBS,
                 "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
-                "kernel": "k_gemv_multi: gate+up, 2 x 14336x4096 gs64", "bytes_per_launch": b_dom,
-                "avg_launch_us": avg_dom * 1e6, "launches": reps * dom_per_replay}
+                "kernel": "k_gemv_multi: the step's gate+up launch (int8_gemv_multi), 2 x 14336x4096 gs64",
+                "bytes_per_launch": b_dom, "avg_launch_us": avg_dom * 1e6, "mean_launch_us": mean_dom * 1e6,
+                "launches": reps * dom_per_replay, "batches": reps,
+                "timing": "median over graph replays of 48 launches, HIP events on the launch stream"}
 
     # ---- per-launch view (eager launches, HIP events around each; includes
     # host launch latency, reported for reference only)
@@ -570,7 +792,7 @@ def main():
     for name, kind, names in FUSED:
         avg = float(np.mean(per_call[name]))
         b = launch_bytes(kind, names)
-        calls[name] = {"weights": list(names), "kind": kind, "bytes": b, "avg_event_us": avg * 1e6,
+        calls[name] = {"weights": list(names), "kind": kind, "bytes": b, "avg_eager_event_us": avg * 1e6,
                        "GB/s": b / avg / 1e9}
 
     # ---- the same layer as seven single-weight launches (one graph per layer)
@@ -585,7 +807,8 @@ def main():
         "config": {"workload": "llama3-8b-shaped decode layer at m=1, group_size=64: gemv_multi(q,k,v), gemv(o), "
                                "gemv_multi(gate,up), gemv_silu_gate_resid(down)",
                    "bytes_per_step": step_bytes, "layers_rotated": n_layers, "frac_hbm_peak": value / HBM_PEAK_GBS,
-                   "timing": "HIP graph per layer", "wall_s": wall},
+                   "timing": f"HIP graph per layer, HIP event after every step, median of {n_batches} batches",
+                   "mean_ms_per_step": step_mean_s * 1e3, "wall_s": wall},
         "roofline": roofline,
         "calls": calls,
         "unfused_step": unfused,

@@ -79,6 +79,8 @@ def _load():
         lib.orc_fp8_gemv.argtypes = [p, p, i64, i64, ctypes.c_int, i64, ctypes.c_double, p, p, p]
         lib.orc_moe_gemv.argtypes = [p, p, p, i64, i64, i64, i64, p, i64, p, i64, i64, p, p]
         lib.orc_max_threads.restype = ctypes.c_int
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -110,6 +112,11 @@ def _weight(packed, scales, biases, group_size):
 
 def max_threads() -> int:
     return int(_load().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for the oracle's row loops (results are the same for any count)."""
+    _load().orc_set_threads(int(n))
 
 
 def bf16_to_f32(bits) -> np.ndarray:

@@ -367,3 +367,13 @@ int orc_max_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads for the row loops from now on (timing the oracle at 1 thread and at
+ * all cores); results do not depend on it. */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

@@ -17,23 +17,46 @@ from weight_only_quantized_int8_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def header_functions():
-    text = open(os.path.join(ROOT, "include", "int8w.h")).read()
+def header_functions(header="int8w.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(int8w?_\w+)\s*\(", text, flags=re.M)))
 
 
+def all_header_functions():
+    return sorted(set().union(*(header_functions(h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+                                if h.endswith(".h"))))
+
+
 def test_header_declares_the_entry_points():
     assert header_functions() == sorted(B.EXPORTED)
+    assert header_functions("int8w_measure.h") == sorted(B.EXPORTED_MEASURE)
 
 
 def test_library_exports_every_declared_symbol():
     lib = B.load_library()
-    for name in header_functions():
+    names = all_header_functions()
+    assert len(names) == len(B.EXPORTED) + len(B.EXPORTED_MEASURE)
+    for name in names:
         assert hasattr(lib, name), name
     nm = os.popen(f"nm -D --defined-only {B.library_path()}").read()
-    for name in header_functions():
+    for name in names:
         assert re.search(rf"\bT {name}$", nm, flags=re.M), f"{name} is not an exported text symbol"
+
+
+@pytest.mark.parametrize("call,code,text", [
+    (lambda: B.int8w_stream_read(0, 1024, A16, 0), B.INT8W_ERR_NULL, "src is NULL"),
+    (lambda: B.int8w_stream_read(A16, 1000, A16, 0), B.INT8W_ERR_SHAPE, "multiple of 1024"),
+    (lambda: B.int8w_stream_read(A16, 0, A16, 0), B.INT8W_ERR_SHAPE, "multiple of 1024"),
+    (lambda: B.int8w_stream_read(A16 + 8, 1024, A16, 0), B.INT8W_ERR_ALIGN, "src is not 16-byte"),
+    (lambda: B.int8w_stream_read(A16, 1024, 0, 0), B.INT8W_ERR_NULL, "sink is NULL"),
+    (lambda: B.int8w_stream_copy(A16, 0, 1024, 0), B.INT8W_ERR_NULL, "dst is NULL"),
+    (lambda: B.int8w_stream_copy(A16, A16 + 512, 1024, 0), B.INT8W_ERR_ALIAS, "overlaps"),
+    (lambda: B.int8w_stream_copy(A16, 2 * A16 + 4, 1024, 0), B.INT8W_ERR_ALIGN, "dst is not 16-byte"),
+])
+def test_calibration_streams_reject_invalid_calls(call, code, text):
+    rc, msg = err(call())
+    assert rc == code and text in msg, (rc, msg)
 
 
 def test_storage_bytes():

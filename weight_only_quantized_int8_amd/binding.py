@@ -40,6 +40,8 @@ EXPORTED = (
     "int8_gemv_silu_gate_resid", "int8_gemm", "int8_gemv_multi", "int8_quantize", "int8_moe_gemv",
     "int8w_fp8_gemv", "int8w_last_error",
 )
+# calibration streams declared in include/int8w_measure.h
+EXPORTED_MEASURE = ("int8w_stream_read", "int8w_stream_copy")
 FP8_PER_ROW, FP8_BLOCK_BF16, FP8_BLOCK_F32, FP8_SINGLE = 0, 1, 2, 3  # INT8W_FP8_*
 MAX_MULTI = 4  # INT8W_MAX_MULTI
 MAX_MOE_SLOTS = 65536  # INT8W_MAX_MOE_SLOTS
@@ -119,6 +121,10 @@ def load_library() -> ctypes.CDLL:
     lib.int8_moe_gemv.restype = ctypes.c_int
     lib.int8w_fp8_gemv.argtypes = [ctypes.POINTER(Fp8WeightDesc), P, P, u64]
     lib.int8w_fp8_gemv.restype = ctypes.c_int
+    lib.int8w_stream_read.argtypes = [P, u64, P, u64]
+    lib.int8w_stream_read.restype = ctypes.c_int
+    lib.int8w_stream_copy.argtypes = [P, P, u64, u64]
+    lib.int8w_stream_copy.restype = ctypes.c_int
     lib.int8w_last_error.argtypes = []
     lib.int8w_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -173,6 +179,14 @@ def int8_moe_gemv(desc: WeightDesc, num_experts: int, x: int, x_rows: int, ids: 
 
 def int8w_fp8_gemv(desc: Fp8WeightDesc, x: int, y: int, stream: int) -> int:
     return load_library().int8w_fp8_gemv(ctypes.byref(desc), x, y, stream)
+
+
+def int8w_stream_read(src: int, nbytes: int, sink: int, stream: int) -> int:
+    return load_library().int8w_stream_read(src, nbytes, sink, stream)
+
+
+def int8w_stream_copy(src: int, dst: int, nbytes: int, stream: int) -> int:
+    return load_library().int8w_stream_copy(src, dst, nbytes, stream)
 
 
 def int8_gemv_multi(descs, x: int, ys, stream: int) -> int:

@@ -12,6 +12,7 @@
 #include <cstring>
 
 #include "int8w.h"
+#include "int8w_measure.h"
 #include "launch.h"
 
 namespace int8w {
@@ -375,5 +376,38 @@ int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m,
 }
 
 const char *int8w_last_error(void) { return g_last_error; }
+
+// ---- calibration kernels (int8w_measure.h)
+
+static int check_stream_args(const void *src, uint64_t bytes) {
+  if (!src) return fail(INT8W_ERR_NULL, "src is NULL");
+  if (bytes == 0 || bytes % 1024u != 0 || bytes > (1ull << 40))
+    return fail(INT8W_ERR_SHAPE, "bytes %llu is not a positive multiple of 1024 up to 2^40",
+                (unsigned long long)bytes);
+  if (!aligned(src, 16)) return fail(INT8W_ERR_ALIGN, "src is not 16-byte aligned");
+  return INT8W_OK;
+}
+
+int int8w_stream_read(const void *src, uint64_t bytes, uint32_t *sink, uint64_t stream) {
+  int rc = check_stream_args(src, bytes);
+  if (rc) return rc;
+  if (!sink) return fail(INT8W_ERR_NULL, "sink is NULL");
+  if (!aligned(sink, 4)) return fail(INT8W_ERR_ALIGN, "sink is not 4-byte aligned");
+  (void)hipGetLastError();
+  hipStream_t s = as_stream(stream);
+  return finish_launch(launch_stream_read(src, bytes, sink, s), s);
+}
+
+int int8w_stream_copy(const void *src, void *dst, uint64_t bytes, uint64_t stream) {
+  int rc = check_stream_args(src, bytes);
+  if (rc) return rc;
+  if (!dst) return fail(INT8W_ERR_NULL, "dst is NULL");
+  if (!aligned(dst, 16)) return fail(INT8W_ERR_ALIGN, "dst is not 16-byte aligned");
+  if (overlaps(range("dst", dst, bytes), range("src", src, bytes)))
+    return fail(INT8W_ERR_ALIAS, "dst overlaps src");
+  (void)hipGetLastError();
+  hipStream_t s = as_stream(stream);
+  return finish_launch(launch_stream_copy(src, dst, bytes, s), s);
+}
 
 }  // extern "C"

@@ -71,4 +71,9 @@ hipError_t launch_gemm_smallm32(const WeightView &w, const uint16_t *X, uint16_t
 // tiled kernel (a grid of few tiles, each walking all of K), else 0.
 uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m);
 
+// Calibration streams (not part of the layer path): read `bytes` once, or
+// copy them; bytes a multiple of 1024.
+hipError_t launch_stream_read(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t stream);
+hipError_t launch_stream_copy(const void *src, void *dst, uint64_t bytes, hipStream_t stream);
+
 }  // namespace int8w

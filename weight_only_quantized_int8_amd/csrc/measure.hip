@@ -1,0 +1,139 @@
+// measure.hip -- calibration kernels for the bandwidth figures: a plain
+// streaming read and a plain streaming copy, built the way the layer kernels
+// stream their weights (contiguous 1 KiB items per wave, 16 bytes per lane,
+// bounded buffer loads, two blocks of loads in flight).  They give the
+// achievable HBM rate on this chip for a read-only and for a read-plus-write
+// stream, the ceilings that the gemv and the dequantize_to / quantize
+// figures are compared with.  Not part of the layer path.
+#include "common.h"
+
+namespace int8w {
+
+namespace {
+
+constexpr int kMThreads = 512;  // 8 waves
+constexpr int kMU = 4;          // 1 KiB items per pipeline block
+
+// wave gw of `waves` owns items [beg, beg + n) of `items`
+struct WaveRange {
+  uint64_t beg;
+  uint32_t n;
+};
+__device__ __forceinline__ WaveRange wave_range(uint64_t items, uint32_t waves, uint32_t gw) {
+  const uint64_t q = items / waves, r = items % waves;
+  return {gw * q + (gw < r ? gw : r), (uint32_t)(q + (gw < r ? 1u : 0u))};
+}
+
+// vmcnt(n) with expcnt and lgkmcnt left open
+#define INT8W_M_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
+
+__global__ __launch_bounds__(kMThreads) void k_stream_read(const uint8_t *__restrict__ src, uint64_t items,
+                                                           uint32_t *sink) {
+  const uint32_t gw = blockIdx.x * (kMThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const WaveRange wr = wave_range(items, gridDim.x * (kMThreads / 64), gw);
+  const auto rs = make_rsrc(src + wr.beg * 1024u, wr.n * 1024u);
+  const uint32_t vo = (threadIdx.x & 63u) << 4;
+  u32x4 A[kMU], B[kMU];
+  uint32_t acc = 0, i_item = 0;
+  // items past the wave's range read out of bounds (zeros, no memory access)
+  auto issue = [&](u32x4 *blk) {
+#pragma unroll
+    for (int u = 0; u < kMU; ++u) {
+      const uint32_t so = __builtin_amdgcn_readfirstlane(i_item << 10);
+      blk[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(i_item < wr.n ? vo : kOutOfRange), (int)so,
+                                                     kAuxNontemporal);
+      ++i_item;
+    }
+  };
+  auto consume = [&](const u32x4 *blk) {
+#pragma unroll
+    for (int u = 0; u < kMU; ++u) acc ^= blk[u].x ^ blk[u].y ^ blk[u].z ^ blk[u].w;
+  };
+  const uint32_t nblk = (wr.n + kMU - 1) / kMU;
+  issue(A);
+  uint32_t b = 0;
+  for (; b + 2u < nblk; b += 2u) {
+    issue(B);
+    consume(A);
+    INT8W_M_VMCNT(kMU);
+    issue(A);
+    consume(B);
+    INT8W_M_VMCNT(kMU);
+  }
+  if (b + 1u < nblk) {
+    issue(B);
+    consume(A);
+    consume(B);
+  } else if (b < nblk) {
+    consume(A);
+  }
+  // keeps the loads alive; the value is never this in practice
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+__global__ __launch_bounds__(kMThreads) void k_stream_copy(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
+                                                           uint64_t items) {
+  const uint32_t gw = blockIdx.x * (kMThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const WaveRange wr = wave_range(items, gridDim.x * (kMThreads / 64), gw);
+  const auto rs = make_rsrc(src + wr.beg * 1024u, wr.n * 1024u);
+  uint8_t *out = dst + wr.beg * 1024u + ((threadIdx.x & 63u) << 4);
+  const uint32_t vo = (threadIdx.x & 63u) << 4;
+  u32x4 A[kMU], B[kMU];
+  uint32_t i_item = 0, c_item = 0;
+  auto issue = [&](u32x4 *blk) {
+#pragma unroll
+    for (int u = 0; u < kMU; ++u) {
+      const uint32_t so = __builtin_amdgcn_readfirstlane(i_item << 10);
+      blk[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(i_item < wr.n ? vo : kOutOfRange), (int)so,
+                                                     kAuxNontemporal);
+      ++i_item;
+    }
+  };
+  auto consume = [&](const u32x4 *blk) {
+#pragma unroll
+    for (int u = 0; u < kMU; ++u) {
+      if (c_item < wr.n) *reinterpret_cast<u32x4 *>(out + ((size_t)c_item << 10)) = blk[u];
+      ++c_item;
+    }
+  };
+  const uint32_t nblk = (wr.n + kMU - 1) / kMU;
+  issue(A);
+  uint32_t b = 0;
+  for (; b + 2u < nblk; b += 2u) {
+    issue(B);
+    consume(A);
+    INT8W_M_VMCNT(kMU);
+    issue(A);
+    consume(B);
+    INT8W_M_VMCNT(kMU);
+  }
+  if (b + 1u < nblk) {
+    issue(B);
+    consume(A);
+    consume(B);
+  } else if (b < nblk) {
+    consume(A);
+  }
+}
+#undef INT8W_M_VMCNT
+
+}  // namespace
+
+int device_cu_count();
+
+// two 8-wave workgroups per CU, as the large gemv launches
+hipError_t launch_stream_read(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t stream) {
+  const uint32_t blocks = 2u * (uint32_t)device_cu_count();
+  hipLaunchKernelGGL(k_stream_read, dim3(blocks), dim3(kMThreads), 0, stream, reinterpret_cast<const uint8_t *>(src),
+                     bytes >> 10, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(const void *src, void *dst, uint64_t bytes, hipStream_t stream) {
+  const uint32_t blocks = 2u * (uint32_t)device_cu_count();
+  hipLaunchKernelGGL(k_stream_copy, dim3(blocks), dim3(kMThreads), 0, stream, reinterpret_cast<const uint8_t *>(src),
+                     reinterpret_cast<uint8_t *>(dst), bytes >> 10);
+  return hipGetLastError();
+}
+
+}  // namespace int8w
