@@ -3,10 +3,17 @@
 // Y BF16 [m, out_features]).
 //
 // A dense contraction, bound by v_mfma_f32_16x16x32_bf16 throughput:
-//  * Block tile BM x BN = 256 x 128 outputs over 8 waves (4 x 2, each wave
-//    64 x 64), or 128 x 128 / 128 x 64 over 4 waves when there are too few
+//  * Block tile BM x BN = 256 x 128 outputs; with K staged by DMA (the usual
+//    case) over 4 MFMA waves of 64 x 128 each, otherwise over 8 waves of
+//    64 x 64; 128 x 128 / 128 x 64 over 4 waves when there are too few
 //    large tiles to occupy the CUs; K step 64; MFMA tiles of 16 x 16 with
-//    fp32 accumulators.
+//    fp32 accumulators.  A 64 x 128 wave reads 24 KiB of operands from LDS
+//    per step for 64 products (43 flops per LDS byte; a 64 x 64 wave, 32):
+//    measured, LDS reads at 32 flops per byte cap the matrix cores near
+//    70 % even without other LDS traffic, and the 256 x 128 DMA-staged
+//    kernel went 9-12 % faster with 4 such waves than with 8 of 64 x 64
+//    (same result bits: each output sums the same products in the same
+//    order).
 //  * Per K step the block stages a 128 x 64 BF16 tile of X and a 128 x 64
 //    tile of the weight into LDS.  The weight arrives as codes (16 per lane,
 //    one 16-byte load) and is dequantized on the way in: w = q*s + b in fp32
@@ -25,7 +32,7 @@
 //  * Work order: the M tiles of one N tile are consecutive, and consecutive
 //    work items are kept on one XCD (workgroups are dealt round-robin over
 //    the 8 XCDs), so the blocks sharing a weight tile share an L2.
-//  * The large shape (256 x 128) specialises waves: 8 MFMA waves consume step
+//  * The large shape (256 x 128) specialises waves: MFMA waves consume step
 //    k while producer waves load, dequantize and store a later step, with one
 //    barrier per step.  With one workgroup per CU the waves of the
 //    single-role design moved in lockstep between an MFMA phase and a
@@ -657,10 +664,6 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
 #pragma unroll
       for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
-  // one half step's operands at a time: the other MFMA wave on the SIMD
-  // covers the LDS latency (measured equal to or faster than reading both
-  // halves ahead, with fewer registers)
-  bf16x8 a[TI], b[TJ];
   __syncthreads();  // the producers' scale/bias staging
   __syncthreads();  // step 0 is in LDS
   // on a half tile the waves of the lower rows have nothing to multiply (but
@@ -670,15 +673,35 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
     return;
   }
   uint32_t s = 0;
-  for (uint32_t k = 0;;) {
-    load_frags(a, b, stage(s), 0u);
-    mma(a, b);
-    load_frags(a, b, stage(s), 1u);
-    mma(a, b);
-    if (k + 1u >= ksteps) break;
-    __syncthreads();  // step k + 1 is in LDS; everyone is done with step k
-    s = next3(s);
-    ++k;
+  if constexpr (kMma >= 8) {
+    // one half step's operands at a time: the other MFMA wave on the SIMD
+    // covers the LDS latency (measured equal to or faster than reading both
+    // halves ahead, with fewer registers)
+    bf16x8 a[TI], b[TJ];
+    for (uint32_t k = 0;;) {
+      load_frags(a, b, stage(s), 0u);
+      mma(a, b);
+      load_frags(a, b, stage(s), 1u);
+      mma(a, b);
+      if (k + 1u >= ksteps) break;
+      __syncthreads();  // step k + 1 is in LDS; everyone is done with step k
+      s = next3(s);
+      ++k;
+    }
+  } else {
+    // one MFMA wave per SIMD: both half steps' operands are requested before
+    // the first product, so the second half's LDS latency hides under it
+    bf16x8 a0[TI], b0[TJ], a1[TI], b1[TJ];
+    for (uint32_t k = 0;;) {
+      load_frags(a0, b0, stage(s), 0u);
+      load_frags(a1, b1, stage(s), 1u);
+      mma(a0, b0);
+      mma(a1, b1);
+      if (k + 1u >= ksteps) break;
+      __syncthreads();  // step k + 1 is in LDS; everyone is done with step k
+      s = next3(s);
+      ++k;
+    }
   }
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
@@ -773,8 +796,9 @@ hipError_t launch_tile(const WeightView &w, const uint16_t *X, uint16_t *Y, uint
 
 // Tile shapes (BM x BN, waves): 0 = 128 x 128 (2 x 2), 1 = 128 x 64 (2 x 2),
 // 2 = 256 x 128 (4 x 2 MFMA waves + 8 producer waves), 3 = 256 x 128 staged
-// by DMA (4 x 2 MFMA waves + 4 producer waves; K % (8 gs) == 0), 4 = 128 x 64
-// staged by DMA (2 x 2 MFMA waves + 4 producer waves; K % (8 gs) == 0).
+// by DMA (4 x 1 MFMA waves of 64 x 128 + 4 producer waves; K % (8 gs) == 0),
+// 4 = 128 x 64 staged by DMA (2 x 2 MFMA waves + 4 producer waves;
+// K % (8 gs) == 0).
 hipError_t launch_gemm_prefill_tile(int t, const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                                     hipStream_t stream) {
   switch (t) {
@@ -782,7 +806,7 @@ hipError_t launch_gemm_prefill_tile(int t, const WeightView &w, const uint16_t *
     case 2: return launch_tile_ws<256, 128, 4, 2, 8>(w, X, Y, m, stream);
     case 3:
       if (w.K % (8u * w.gs) != 0u) return hipErrorInvalidValue;
-      return launch_tile_dma<256, 128, 4, 2, 4>(w, X, Y, m, stream);
+      return launch_tile_dma<256, 128, 4, 1, 4>(w, X, Y, m, stream);
     case 4:
       if (w.K % (8u * w.gs) != 0u) return hipErrorInvalidValue;
       return launch_tile_dma<128, 64, 2, 2, 4>(w, X, Y, m, stream);
