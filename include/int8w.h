@@ -222,6 +222,27 @@ int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const
  * whose scale/bias rows do not fit the small-m kernel's LDS). */
 int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, uint64_t stream);
 
+/* Source: "MlxInt8Weight", method gemm, as int8_gemm; this form takes a
+ * workspace so that a grid with too few tiles to occupy the GPU (e.g. m = 512
+ * on a 4096-row weight) can split in_features over several work items per
+ * tile.  Each item stores its fp32 partial in the workspace and a second
+ * launch on the same stream adds the parts in a fixed order, so results are
+ * deterministic (they may differ from int8_gemm's in the last bits, within the
+ * same bound).
+ *   int8_gemm_workspace_bytes(w, m): the bytes int8_gemm_ws needs for m rows
+ *     of this weight; 0 when it would not split (or for an invalid weight).
+ *   int8_gemm_ws(w, x, y, m, workspace, workspace_bytes, stream): as
+ *     int8_gemm.  workspace is a DEVICE buffer, 256-byte aligned, of at least
+ *     int8_gemm_workspace_bytes(w, m) bytes; its contents are scratch (no
+ *     initial value needed, none kept).  The library does not allocate it.
+ *     Calls that share a workspace must not run concurrently.  INT8W_ERR_NULL
+ *     for a NULL workspace, INT8W_ERR_ALIGN, INT8W_ERR_SHAPE if it is too
+ *     small, INT8W_ERR_ALIAS if it overlaps X, Y or the weight; otherwise as
+ *     int8_gemm. */
+uint64_t int8_gemm_workspace_bytes(const int8w_weight *w, uint32_t m);
+int int8_gemm_ws(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, void *workspace,
+                 uint64_t workspace_bytes, uint64_t stream);
+
 /* Human-readable description of the calling thread's most recent error
  * ("" if none).  The pointer stays valid until the thread's next call. */
 const char *int8w_last_error(void);

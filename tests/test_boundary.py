@@ -296,3 +296,19 @@ def test_fp8_gemv_rejects():
     assert rc == B.INT8W_ERR_ALIAS and "scale" in msg
     rc, msg = err(B.int8w_fp8_gemv(fp8desc(), x, x + 2 * 255, 0))
     assert rc == B.INT8W_ERR_ALIAS and "input x" in msg
+
+
+def test_gemm_workspace_rules():
+    d = desc(N=4096, K=14336, gs=64)
+    need = B.int8_gemm_workspace_bytes(d, 512)
+    assert need >= 4 * 64 * 4 * 32768  # m = 512 on a 4096-row weight: 4 parts of 64 tiles
+    assert B.int8_gemm_workspace_bytes(d, 16) == 0 and B.int8_gemm_workspace_bytes(d, 2048) == 0
+    X, Y, WS = 8 * A16, 64 * A16, 512 * A16
+    rc, msg = err(B.int8_gemm_ws(d, X, Y, 512, 0, 0, 0))
+    assert rc == B.INT8W_ERR_NULL and "workspace" in msg
+    rc, msg = err(B.int8_gemm_ws(d, X, Y, 512, WS + 16, need, 0))
+    assert rc == B.INT8W_ERR_ALIGN and "workspace" in msg
+    rc, msg = err(B.int8_gemm_ws(d, X, Y, 512, WS, need - 1, 0))
+    assert rc == B.INT8W_ERR_SHAPE and "needs" in msg
+    rc, msg = err(B.int8_gemm_ws(d, X, Y, 512, X, need, 0))
+    assert rc == B.INT8W_ERR_ALIAS and "workspace" in msg

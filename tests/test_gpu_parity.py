@@ -349,12 +349,13 @@ def test_gemm_prefill_small(m, N, K, gs):
     (32, 18944, 3584, 64),    # the tiled kernel would take one round of 256 x 128 tiles
 ])
 def test_gemm_in_slices_of_32_rows(m, N, K, gs):
+    # int8_gemm (no workspace): with one, some of these grids split K instead
     log(f"gemm 32-row slices m={m} N={N} K={K} gs={gs}")
     w, rng = make_weight(3500 + m + N + K, N, K, gs)
     X = synth.gen_act(rng, (m, K))
     W = upload(w)
     Xd = bits_to_dev(X)
-    Y = W.gemm(Xd)
+    Y = W.gemm(Xd, split_k=False)
     _sync()
     got = dev_to_bits(Y)
     Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
@@ -363,7 +364,7 @@ def test_gemm_in_slices_of_32_rows(m, N, K, gs):
         r1 = min(r0 + 32, m)
         if r1 - r0 < 2:
             continue
-        part = dev_to_bits(W.gemm(Xd[r0:r1].contiguous()))
+        part = dev_to_bits(W.gemm(Xd[r0:r1].contiguous(), split_k=False))
         _sync()
         assert np.array_equal(got[r0:r1], part), f"rows {r0}..{r1 - 1} differ from gemm on the slice alone"
 
@@ -414,6 +415,42 @@ def test_gemm_prefill_full_size_all_rows(m, N, K):
     Yb = dev_to_bits(Y)
     Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
     assert_close(Yb, Y_ref, A, f"gemm m={m} {N}x{K}")
+
+
+# A grid with too few tiles splits K over several work items per tile (the
+# workspace form, int8_gemm_ws, which Int8Weight.gemm uses when the call
+# needs one): every output against the oracle, a repeat call bit-identical,
+# and int8_gemm without a workspace (no split) within the same bound.  The
+# cases run back to back on one workspace, so stale partials of an earlier
+# shape would show.
+@pytest.mark.parametrize("m,N,K,gs", [
+    (90, 1500, 16384, 64),    # 8 parts of 4 scale/bias blocks, ragged rows and columns
+    (300, 2000, 8192, 32),    # 8 parts of 4 blocks
+    (600, 3000, 16384, 64),   # 7 parts of 4 or 5 blocks
+    (257, 1024, 12288, 64),   # 8 parts; the second row tile holds one row
+    (128, 4096, 14336, 64),   # the 8B down projection at m = 128: 7 parts
+    (1000, 2048, 4096, 64),   # 4 parts
+])
+def test_gemm_split_k(m, N, K, gs):
+    from weight_only_quantized_int8_amd import binding as B
+    log(f"gemm split K m={m} N={N} K={K} gs={gs}")
+    w, rng = make_weight(3_800 + m + N + K, N, K, gs)
+    X = synth.gen_act(rng, (m, K))
+    W = upload(w)
+    assert B.int8_gemm_workspace_bytes(W.desc, m) > 0, "the shape is expected to split"
+    Xd = bits_to_dev(X)
+    Y = W.gemm(Xd)
+    _sync()
+    got = dev_to_bits(Y)
+    Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
+    assert_close(got, Y_ref, A, f"split gemm m={m} {N}x{K} gs{gs}")
+    Y2 = W.gemm(Xd)
+    _sync()
+    assert np.array_equal(dev_to_bits(Y2), got)
+    Y3 = torch.empty_like(Y)
+    assert B.int8_gemm(W.desc, Xd.data_ptr(), Y3.data_ptr(), m, torch.cuda.current_stream().cuda_stream) == 0
+    _sync()
+    assert_close(dev_to_bits(Y3), Y_ref, A, f"unsplit gemm m={m} {N}x{K} gs{gs}")
 
 
 def test_gemm_m1_is_gemv_bit_exact():

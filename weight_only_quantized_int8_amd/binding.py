@@ -38,7 +38,7 @@ ERROR_NAMES = {
 EXPORTED = (
     "int8w_validate", "int8w_storage_bytes", "int8_dequantize_to", "int8_gemv", "int8_gemv_silu_gate",
     "int8_gemv_silu_gate_resid", "int8_gemm", "int8_gemv_multi", "int8_quantize", "int8_moe_gemv",
-    "int8w_fp8_gemv", "int8w_last_error",
+    "int8w_fp8_gemv", "int8w_last_error", "int8_gemm_workspace_bytes", "int8_gemm_ws",
 )
 # calibration streams declared in include/int8w_measure.h
 EXPORTED_MEASURE = ("int8w_stream_read", "int8w_stream_copy")
@@ -121,6 +121,10 @@ def load_library() -> ctypes.CDLL:
     lib.int8_moe_gemv.restype = ctypes.c_int
     lib.int8w_fp8_gemv.argtypes = [ctypes.POINTER(Fp8WeightDesc), P, P, u64]
     lib.int8w_fp8_gemv.restype = ctypes.c_int
+    lib.int8_gemm_workspace_bytes.argtypes = [W, ctypes.c_uint32]
+    lib.int8_gemm_workspace_bytes.restype = ctypes.c_uint64
+    lib.int8_gemm_ws.argtypes = [W, P, P, ctypes.c_uint32, P, u64, u64]
+    lib.int8_gemm_ws.restype = ctypes.c_int
     lib.int8w_stream_read.argtypes = [P, u64, P, u64]
     lib.int8w_stream_read.restype = ctypes.c_int
     lib.int8w_stream_copy.argtypes = [P, P, u64, u64]
@@ -179,6 +183,14 @@ def int8_moe_gemv(desc: WeightDesc, num_experts: int, x: int, x_rows: int, ids: 
 
 def int8w_fp8_gemv(desc: Fp8WeightDesc, x: int, y: int, stream: int) -> int:
     return load_library().int8w_fp8_gemv(ctypes.byref(desc), x, y, stream)
+
+
+def int8_gemm_workspace_bytes(desc: WeightDesc, m: int) -> int:
+    return int(load_library().int8_gemm_workspace_bytes(ctypes.byref(desc), m))
+
+
+def int8_gemm_ws(desc: WeightDesc, x: int, y: int, m: int, ws: int, ws_bytes: int, stream: int) -> int:
+    return load_library().int8_gemm_ws(ctypes.byref(desc), x, y, m, ws, ws_bytes, stream)
 
 
 def int8w_stream_read(src: int, nbytes: int, sink: int, stream: int) -> int:
@@ -312,7 +324,9 @@ class Int8Weight:
                                          y.data_ptr(), _stream_of(self.device)))
         return y
 
-    def gemm(self, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    def gemm(self, x: torch.Tensor, y: torch.Tensor | None = None, split_k: bool = True) -> torch.Tensor:
+        """Y = X W^T.  With split_k (the default) a call whose grid has too few
+        tiles runs int8_gemm_ws on a cached per-device workspace; otherwise int8_gemm."""
         if x.dim() != 2 or x.shape[1] != self.in_features:
             raise ValueError(f"X must be [m, {self.in_features}]")
         m = x.shape[0]
@@ -320,8 +334,29 @@ class Int8Weight:
         if y is None:
             y = torch.empty((m, self.out_features), dtype=torch.bfloat16, device=self.device)
         _need_bf16(y, "Y", m * self.out_features, self.device)
-        _check(int8_gemm(self.desc, x.data_ptr(), y.data_ptr(), m, _stream_of(self.device)))
+        need = int8_gemm_workspace_bytes(self.desc, m) if split_k and m > 16 else 0
+        if need:
+            ws = _workspace(self.device, need)
+            _check(int8_gemm_ws(self.desc, x.data_ptr(), y.data_ptr(), m, ws.data_ptr(), ws.numel(),
+                                _stream_of(self.device)))
+        else:
+            _check(int8_gemm(self.desc, x.data_ptr(), y.data_ptr(), m, _stream_of(self.device)))
         return y
+
+
+# One gemm workspace per device (scratch for split-K partials), grown on
+# demand.  Calls that use it are ordered on the caller's stream; overlapping
+# calls on several streams of one device would share it and race.
+_workspaces: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 64 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
 
 
 def gemv_multi(weights, x: torch.Tensor, ys=None):

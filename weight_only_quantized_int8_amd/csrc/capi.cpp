@@ -329,7 +329,15 @@ int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const
   return gemv_gated(w, gate, up, x_resid, y, stream, true);
 }
 
-int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, uint64_t stream) {
+}  // extern "C"
+
+namespace int8w {
+namespace {
+
+// gemm with an optional workspace (ws == nullptr: the tiled kernel never
+// splits K).  ws_bytes is checked against what the chosen launch needs.
+int gemm_common(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, void *ws, uint64_t ws_bytes,
+                uint64_t stream) {
   int rc = validate(w);
   if (rc) return rc;
   if (m == 0) return ok();
@@ -342,18 +350,32 @@ int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m,
   // 16 < m <= 128 on a small grid: passes of the small-m kernel over slices of
   // 32 (or 16) rows
   const bool sm_ok = smallm_supported(w->in_features, w->group_size);
-  const uint32_t slice = m > 16u ? gemm_smallm_slice_rows(view(w), m) : 0u;
+  const uint32_t slice = m > 16u ? gemm_smallm_slice_rows(view(w), m, ws != nullptr) : 0u;
   const bool passes = slice != 0u;
   // the tiled kernel addresses a 256-row X tile with 32-bit byte offsets
   const bool tiled = !passes && (m > 16u || (m > 1u && !sm_ok));
   if (tiled && K * 2u * 256u > 0xFFFFFFFFull)
     return fail(INT8W_ERR_SHAPE, "in_features=%u above 2^23 - 1 needs m = 1 or a small-m shape (m=%u)",
                 w->in_features, m);
+  const uint64_t need = tiled && ws ? gemm_prefill_workspace_bytes(view(w), m) : 0u;
+  if (ws) {
+    if (!aligned(ws, 256)) return fail(INT8W_ERR_ALIGN, "workspace is not 256-byte aligned");
+    if (ws_bytes < need)
+      return fail(INT8W_ERR_SHAPE, "workspace of %llu bytes, this call needs %llu", (unsigned long long)ws_bytes,
+                  (unsigned long long)need);
+  }
   Range ins[4];
   weight_ranges(w, ins);
   ins[3] = range("X", x, (uint64_t)m * K * 2);
   rc = check_alias(range("Y", y, (uint64_t)m * N * 2), ins, 4);
   if (rc) return rc;
+  if (need) {
+    const Range outs[2] = {range("Y", y, (uint64_t)m * N * 2), range("X", x, (uint64_t)m * K * 2)};
+    rc = check_alias(range("workspace", ws, need), ins, 3);
+    if (rc) return rc;
+    rc = check_alias(range("workspace", ws, need), outs, 2);
+    if (rc) return rc;
+  }
   (void)hipGetLastError();
   hipStream_t s = as_stream(stream);
   hipError_t e;
@@ -370,9 +392,32 @@ int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m,
                    : launch_gemm_smallm(view(w), x + (size_t)r0 * K, y + (size_t)r0 * N, mi, s);
     }
   } else {
-    e = launch_gemm_prefill(view(w), x, y, m, s);
+    e = launch_gemm_prefill(view(w), x, y, m, need ? ws : nullptr, s);
   }
   return finish_launch(e, s);
+}
+
+}  // namespace
+}  // namespace int8w
+
+extern "C" {
+
+int int8_gemm(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, uint64_t stream) {
+  return gemm_common(w, x, y, m, nullptr, 0, stream);
+}
+
+uint64_t int8_gemm_workspace_bytes(const int8w_weight *w, uint32_t m) {
+  if (validate(w) != INT8W_OK || m <= 16u) return 0;
+  const uint64_t K = w->in_features, N = w->out_features;
+  if ((uint64_t)m * K > 0xFFFFFFFFull || (uint64_t)m * N > 0xFFFFFFFFull || K * 2u * 256u > 0xFFFFFFFFull) return 0;
+  if (gemm_smallm_slice_rows(view(w), m, true) != 0u) return 0;
+  return gemm_prefill_workspace_bytes(view(w), m);
+}
+
+int int8_gemm_ws(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, void *workspace,
+                 uint64_t workspace_bytes, uint64_t stream) {
+  if (!workspace) return fail(INT8W_ERR_NULL, "workspace is NULL (int8_gemm takes no workspace)");
+  return gemm_common(w, x, y, m, workspace, workspace_bytes, stream);
 }
 
 const char *int8w_last_error(void) { return g_last_error; }

@@ -397,6 +397,21 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_ws(
   }
 }
 
+// Split of K over several work items per tile (grids with too few tiles to
+// occupy the CUs).  Part p of a tile covers scale/bias blocks (8 groups each)
+// p * nblk / parts .. (p + 1) * nblk / parts - 1.  Each MFMA wave stores its
+// fp32 partial of the tile to part[p][tile][wave] (lane-major float4s, 1 KiB
+// per store instruction); k_splitk_sum, launched next on the same stream,
+// adds the parts in the order 0 .. parts - 1 and writes the BF16 outputs.  The
+// kernel boundary orders the two: no atomics, no flags, deterministic sums.
+// parts == 1: no split, no workspace.
+struct SplitK {
+  uint32_t parts;
+  uint32_t nblk;
+  uint32_t ntiles;
+  float *part;
+};
+
 // The main prefill kernel: wave-specialised like k_gemm_prefill_ws, with the
 // operands staged by DMA (buffer_load_dwordx4 ... lds: memory straight into
 // LDS, no registers, no LDS stores).
@@ -419,7 +434,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ X, uint16_t *__restrict__ Y,
     uint32_t N, uint32_t K, uint32_t m, uint32_t gs_log2, uint32_t mtiles, uint32_t nbig, uint32_t mt_half,
-    uint32_t nt_big, uint32_t nwork) {
+    uint32_t nt_big, uint32_t nwork, SplitK sk) {
   constexpr int kMma = WGM * WGN;          // MFMA waves
   constexpr int kPT = 64 * NP;             // producer threads
   constexpr int XR = kPT / 8;              // X rows per producer pass
@@ -442,10 +457,23 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
   // so that a grid of 3.5 rounds of full tiles ends in one round of half tiles
   // instead of half a round of full ones.  Within each kind, consecutive
   // items (the M tiles of one N tile) stay on one XCD.
+  // With a split of K (sk.parts > 1) the items are (tile, part) pairs, the
+  // parts of a tile consecutive, and there are no half tiles; the item's K
+  // range is kb .. kb + kl - 1, a whole number of scale/bias blocks.
   uint32_t bid = blockIdx.x;
   bool half;
-  uint32_t m0, n0;
-  if (bid < nbig) {
+  uint32_t m0, n0, part = 0, tile = 0, kb = 0, kl = K;
+  if (sk.parts > 1u) {
+    if (nwork % kXcds == 0) bid = (bid % kXcds) * (nwork / kXcds) + bid / kXcds;
+    part = bid % sk.parts;
+    tile = bid / sk.parts;
+    half = false;
+    m0 = (tile % mtiles) * BM;
+    n0 = (tile / mtiles) * BN;
+    const uint32_t blo = part * sk.nblk / sk.parts, bhi = (part + 1u) * sk.nblk / sk.parts;
+    kb = blo << (gs_log2 + 3u);
+    kl = (bhi - blo) << (gs_log2 + 3u);
+  } else if (bid < nbig) {
     if (nbig % kXcds == 0) bid = (bid % kXcds) * (nbig / kXcds) + bid / kXcds;
     half = false;
     m0 = (bid % mtiles) * BM;
@@ -461,7 +489,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
   const uint32_t tile_rows = half ? (uint32_t)BM / 2u : (uint32_t)BM;
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u, wave = uniform_pf(tid >> 6);
-  const uint32_t ksteps = (K + BK - 1) / BK;
+  const uint32_t ksteps = (kl + BK - 1) / BK;
 
   if (wave >= (uint32_t)kMma) {
     // ---------------- producer waves
@@ -469,10 +497,12 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
     const uint32_t G = K >> gs_log2;
     const uint32_t mrows = m - m0 < tile_rows ? m - m0 : tile_rows;
     const uint32_t nrows = N - n0 < (uint32_t)BN ? N - n0 : (uint32_t)BN;
-    const auto rx = make_rsrc(X + (size_t)m0 * K, mrows * K * 2u);
-    const auto rw = make_rsrc(codes + (size_t)n0 * K, nrows * K);
-    const auto rs = make_rsrc(scales + (size_t)n0 * G, nrows * G * 2u);
-    const auto rb = make_rsrc(biases + (size_t)n0 * G, nrows * G * 2u);
+    // views start at the item's first K position; rows keep their full stride
+    const uint32_t gb = kb >> gs_log2;
+    const auto rx = make_rsrc(X + (size_t)m0 * K + kb, mrows * K * 2u - 2u * kb);
+    const auto rw = make_rsrc(codes + (size_t)n0 * K + kb, nrows * K - kb);
+    const auto rs = make_rsrc(scales + (size_t)n0 * G + gb, nrows * G * 2u - 2u * gb);
+    const auto rb = make_rsrc(biases + (size_t)n0 * G + gb, nrows * G * 2u - 2u * gb);
     const uint32_t wr = ptid >> 2, wp = ptid & 3u;
     // The producer schedule, for XJN X loads per wave and step (the wait
     // counts below are compile-time immediates, hence a template).
@@ -493,7 +523,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
       auto xdma = [&](uint32_t ks, uint32_t st) {
         const bool live = ks < ksteps;
         const uint32_t k0 = live ? ks * BK : 0u;
-        const bool xin = live && k0 + xchunk * 8u < K;
+        const bool xin = live && k0 + xchunk * 8u < kl;
 #pragma unroll
         for (int j = 0; j < XJ; ++j)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -505,7 +535,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
       // rows 64 (pw % kSbW) .. + 63 of the scales (pw < kSbW) or biases.
       // Needs K % (8 gs) == 0, so that every row's block is 16 whole bytes.
       const uint32_t sbs_log2 = gs_log2 - 3u;  // steps per block, log2
-      const uint32_t nblk = K >> (gs_log2 + 3u);
+      const uint32_t nblk = kl >> (gs_log2 + 3u);
       auto sbuf = [&](uint32_t i) { return lds_pf + 3u * kStage + i * kSbBytes; };
       const uint32_t sbrow = (pw % kSbW) * 64u + plane;
       const uint32_t vsbd = sbrow < nrows ? sbrow * G * 2u : kOutOfRange;
@@ -529,7 +559,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
       auto issue = [&](Regs &r, uint32_t ks) {
         const bool live = ks < ksteps;
         const uint32_t k0 = live ? ks * BK : 0u;
-        const bool win = live && k0 + wp * 16u < K;
+        const bool win = live && k0 + wp * 16u < kl;
 #pragma unroll
         for (int p = 0; p < WP; ++p)
           r.w[p] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(win ? vw[p] : kOutOfRange), (int)uniform_pf(k0),
@@ -573,15 +603,13 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
       };
       // vmcnt(n) with expcnt and lgkmcnt left open
 #define INT8W_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
-      // vmcnt(n) and lgkmcnt(0)
-#define INT8W_VMCNT_LGKM0(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0070 | ((n) & 15))
       Regs R0, R1, R2;
       // Iteration k (between barriers k - 1 and k): the X DMA of step k + 2
       // goes to stage (k + 2) % 3 (it held step k - 1, read before barrier
       // k - 1); step k + 1's weights are dequantized into stage (k + 1) % 3;
-      // step k + 4's codes are requested; and the X DMA of step k + 1, issued
-      // one iteration earlier, is awaited.  Barrier k thus publishes step k + 1
-      // and every X DMA has two iterations to land.
+      // step k + 4's codes are requested; and every load of the wave is
+      // awaited.  Barrier k thus publishes step k + 1 (whose X arrived during
+      // iteration k - 1) and k + 2's.
       sbdma(0u);
       if (1u < nblk) sbdma(1u);
       issue(R0, 0);
@@ -604,18 +632,20 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
         // at the first step of scale/bias block b, block b + 1 goes into the
         // buffer that held block b - 1
         if (s != 0u && (s & ((1u << sbs_log2) - 1u)) == 0u && (s >> sbs_log2) + 1u < nblk) sbdma((s >> sbs_log2) + 1u);
-        // The X DMA of step k + 1 has landed and this wave's LDS stores are
-        // done; then a bare barrier.  A fenced barrier would also wait for
-        // every load still in flight -- step k + 2's X and the codes of step
-        // k + 4 -- and so expose their latency on every step.  (A scale/bias
-        // block requested here is older than step k + 3's X, so the wait two
-        // iterations on covers it, before its first reader, gs / 8 >= 4
-        // steps on.)
-        INT8W_VMCNT_LGKM0(XJ + 2 * WP);
+        // Everything this wave requested has landed (vmcnt(0)) and its LDS
+        // stores are done; then the barrier that publishes step k + 1.  A
+        // partial count -- all but the XJ + 2 WP youngest loads, leaving
+        // step k + 2's X and the codes of step k + 4 in flight -- is not
+        // enough: an LDS-DMA load was seen still writing its rows after
+        // younger register loads had been counted off (nondeterministic
+        // rows in a probe of short K ranges; gone with vmcnt(0), which
+        // costs 10-17 %).  So the X of step k + 2, requested at the start of
+        // this step, has this step's length to land, and the scale/bias
+        // blocks are covered the same way.
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
         asm volatile("s_barrier" ::: "memory");
       };
 #undef INT8W_VMCNT
-#undef INT8W_VMCNT_LGKM0
       // Steps 0 .. ksteps - 2, three to an iteration and the rest after the
       // loop.  The loop has a single exit: with an exit after every step the
       // compiler's wait counts at the loop head also cover the paths that
@@ -631,7 +661,13 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
         step(R1, k, 2u, 1u);
         if (k + 1u < nst) step(R2, k + 1u, 0u, 2u);
       }
-
+      // The last steps requested X past the end (zeros into LDS) and codes
+      // that nobody reads.  Wait for all of it before the wave ends: an
+      // LDS-DMA write still in flight when the workgroup finishes lands in
+      // the LDS of the next workgroup on the CU.  (Seen as nondeterministic
+      // tiles on grids of more than one round whose K-step count is a
+      // multiple of 3: the stray zeros hit stage 0 of the next tile.)
+      __builtin_amdgcn_s_waitcnt(0);
     };
     if (half)
       run(std::integral_constant<int, BM / (16 * NP)>{});
@@ -703,6 +739,16 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
       ++k;
     }
   }
+  if (sk.parts > 1u) {
+    // this wave's fp32 partial of its sub-tile, lane-major float4s
+    constexpr uint32_t kVals = TI * TJ;  // float4s per lane
+    float *mine = sk.part + (((size_t)part * sk.ntiles + tile) * kMma + wave) * kVals * 256u + lane * 4u;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) *reinterpret_cast<f32x4 *>(mine + (i * TJ + j) * 256u) = acc[i][j];
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
 #pragma unroll
@@ -718,8 +764,43 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
   }
 }
 
+// The sum of a split launch's parts: thread t adds float4 t of every part
+// (part[0] + part[1] + ... in that order), rounds to BF16 and writes the
+// four outputs it holds (rows 4 lg .. 4 lg + 3 of a 16 x 16 MFMA tile, one
+// column), with the MFMA waves' layout: wave w of a WGM x WGN grid, TI x TJ
+// tiles of 16 x 16 per wave.
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(256) void k_splitk_sum(const float *__restrict__ part, uint32_t parts, uint32_t ntiles,
+                                                    uint32_t mtiles, uint16_t *__restrict__ Y, uint32_t m, uint32_t N) {
+  constexpr uint32_t WTM = BM / WGM, WTN = BN / WGN, TI = WTM / 16, TJ = WTN / 16, kMma = WGM * WGN;
+  constexpr uint32_t kVals = TI * TJ;
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t lane = t & 63u, e = (t >> 6) % kVals, wave = (t >> 6) / kVals % kMma, tile = (t >> 6) / kVals / kMma;
+  if (tile >= ntiles) return;
+  const size_t stride = (size_t)ntiles * kMma * kVals * 256u;  // floats per part
+  const float *p0 = part + ((size_t)tile * kMma + wave) * kVals * 256u + (size_t)e * 256u + lane * 4u;
+  f32x4 sum = *reinterpret_cast<const f32x4 *>(p0);
+  for (uint32_t q = 1; q < parts; ++q) sum += *reinterpret_cast<const f32x4 *>(p0 + q * stride);
+  const uint32_t wm = wave / WGN, wn = wave % WGN, i = e / TJ, j = e % TJ;
+  const uint32_t m0 = (tile % mtiles) * BM, n0 = (tile / mtiles) * BN;
+  const uint32_t n = n0 + wn * WTN + 16u * j + (lane & 15u);
+  if (n >= N) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t row = m0 + wm * WTM + 16u * i + 4u * (lane >> 4) + r;
+    if (row < m) Y[(size_t)row * N + n] = to_bf16_bits(sum[r]);
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, int NP>
-hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream) {
+uint64_t split_bytes(uint32_t tiles, uint32_t parts) {
+  constexpr uint64_t kSub = (uint64_t)BM / WGM * (BN / WGN) * 4u;  // fp32 partial of one wave
+  return (uint64_t)parts * tiles * (WGM * WGN) * kSub;
+}
+
+template <int BM, int BN, int WGM, int WGN, int NP>
+hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream,
+                           uint32_t parts = 1, void *ws = nullptr) {
   auto kern = k_gemm_prefill_dma<BM, BN, WGM, WGN, NP>;
   static bool configured = false;
   if (!configured) {
@@ -730,6 +811,24 @@ hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, 
   }
   const uint32_t mtiles = (m + BM - 1) / BM;
   const uint32_t ntiles = (w.N + BN - 1) / BN;
+  const size_t lds = 3u * (BM + BN) * BK * 2u + BN * 16u * 2u * 2u;
+  const uint32_t gs_log2 = (uint32_t)__builtin_ctz(w.gs);
+  if (parts > 1u) {
+    const uint32_t tiles = mtiles * ntiles;
+    if (ws == nullptr) return hipErrorInvalidValue;
+    SplitK sk{parts, w.K >> (gs_log2 + 3u), tiles, static_cast<float *>(ws)};
+    const uint32_t nwork = tiles * parts;
+    hipLaunchKernelGGL(kern, dim3(nwork), dim3(64 * (WGM * WGN + NP)), lds, stream,
+                       reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m, gs_log2,
+                       mtiles, 0u, 0u, 0u, nwork, sk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr uint32_t kThreadsPerTile = (uint32_t)(BM * BN) / 4u;  // one float4 of outputs each
+    const uint32_t blocks = (uint32_t)(((uint64_t)tiles * kThreadsPerTile + 255u) / 256u);
+    hipLaunchKernelGGL((k_splitk_sum<BM, BN, WGM, WGN>), dim3(blocks), dim3(256), 0, stream,
+                       static_cast<const float *>(ws), parts, tiles, mtiles, Y, m, w.N);
+    return hipGetLastError();
+  }
   // When the full tiles leave a last round at most half full, the N tiles of
   // that round are done as half-height tiles (twice as many, about half the
   // time each) in one last round.  Only for the 256-row tile: 64-row half
@@ -746,10 +845,10 @@ hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, 
   const uint32_t mt_half = (m + BM / 2 - 1) / (BM / 2);
   const uint32_t nbig = mtiles * nt_big;
   const uint32_t nwork = nbig + mt_half * nt_half;
-  const size_t lds = 3u * (BM + BN) * BK * 2u + BN * 16u * 2u * 2u;
+  const SplitK none{1u, 0u, 0u, nullptr};
   hipLaunchKernelGGL(kern, dim3(nwork), dim3(64 * (WGM * WGN + NP)), lds, stream,
-                     reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m,
-                     (uint32_t)__builtin_ctz(w.gs), mtiles, nbig, mt_half, nt_big, nwork);
+                     reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m, gs_log2,
+                     mtiles, nbig, mt_half, nt_big, nwork, none);
   return hipGetLastError();
 }
 
@@ -828,10 +927,14 @@ namespace {
 // 128 x 64 (about 0.42 us per step and round).
 struct PrefillPick {
   int shape;        // launch_gemm_prefill_tile's shape number
+  uint32_t parts;   // K parts per tile (shape 3 only; 1 = no split)
   double est_us;    // estimated kernel time, or a negative value when no estimate is calibrated
 };
 
-PrefillPick prefill_pick(const WeightView &w, uint32_t m, uint32_t cus) {
+// A split of K into `parts` (shape 3, a workspace given): (tile, part) items,
+// one round per ceil(items / CUs), each walking about 1 / parts of K, plus
+// ~5 us for storing the fp32 partials and the launch that sums them.
+PrefillPick prefill_pick(const WeightView &w, uint32_t m, uint32_t cus, bool can_split) {
   const double ksteps = (double)((w.K + 63u) / 64u);
   const uint32_t t256 = ((m + 255u) / 256u) * ((w.N + 127u) / 128u);
   const uint32_t t12864 = ((m + 127u) / 128u) * ((w.N + 63u) / 64u);
@@ -839,22 +942,38 @@ PrefillPick prefill_pick(const WeightView &w, uint32_t m, uint32_t cus) {
   if (w.K % (8u * w.gs) == 0u) {
     const uint32_t rem = t256 % cus;
     const double r256 = t256 <= cus ? 1.0 : (double)(t256 / cus) + (rem == 0u ? 0.0 : 2u * rem <= cus ? 0.5 : 1.0);
-    const double e256 = r256 * 0.85 * ksteps, e12864 = r12864 * 0.45 * ksteps;
-    return e256 <= e12864 ? PrefillPick{3, e256} : PrefillPick{4, e12864};
+    PrefillPick best{3, 1u, r256 * 0.85 * ksteps};
+    const uint32_t nblk = w.K / (8u * w.gs);
+    const double steps_per_blk = (double)(8u * w.gs) / 64.0;
+    if (can_split) {
+      for (uint32_t parts = 2; parts <= 8u && 2u * parts <= nblk; ++parts) {
+        const double rounds = (double)((t256 * parts + cus - 1u) / cus);
+        const double est = rounds * 0.85 * steps_per_blk * (double)((nblk + parts - 1u) / parts) + 5.0;
+        if (est < best.est_us) best = PrefillPick{3, parts, est};
+      }
+    }
+    const double e12864 = r12864 * 0.45 * ksteps;
+    return best.est_us <= e12864 ? best : PrefillPick{4, 1u, e12864};
   }
   const uint32_t t128 = ((m + 127u) / 128u) * ((w.N + 127u) / 128u);
-  if (4u * t256 >= 3u * cus) return {2, -1.0};
-  if (4u * t128 >= 3u * cus) return {0, -1.0};
-  return {1, r12864 * 0.42 * ksteps};
+  if (4u * t256 >= 3u * cus) return {2, 1u, -1.0};
+  if (4u * t128 >= 3u * cus) return {0, 1u, -1.0};
+  return {1, 1u, r12864 * 0.42 * ksteps};
 }
-
-int prefill_shape(const WeightView &w, uint32_t m, uint32_t cus) { return prefill_pick(w, m, cus).shape; }
 
 }  // namespace
 
-hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
+uint64_t gemm_prefill_workspace_bytes(const WeightView &w, uint32_t m) {
+  const PrefillPick pick = prefill_pick(w, m, (uint32_t)device_cu_count(), true);
+  if (pick.parts <= 1u) return 0;
+  return split_bytes<256, 128, 4, 1, 4>(((m + 255u) / 256u) * ((w.N + 127u) / 128u), pick.parts);
+}
+
+hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, void *ws,
                                hipStream_t stream) {
-  return launch_gemm_prefill_tile(prefill_shape(w, m, (uint32_t)device_cu_count()), w, X, Y, m, stream);
+  const PrefillPick pick = prefill_pick(w, m, (uint32_t)device_cu_count(), ws != nullptr);
+  if (pick.parts > 1u) return launch_tile_dma<256, 128, 4, 1, 4>(w, X, Y, m, stream, pick.parts, ws);
+  return launch_gemm_prefill_tile(pick.shape, w, X, Y, m, stream);
 }
 
 // For 16 < m <= 128 the tiled kernel often runs about one round of tiles, one
@@ -868,9 +987,9 @@ hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t 
 // against 90 / 91 / 91 / 92 us; 4096 x 4096, m = 32 / 64: 10 / 19 against 28
 // / 29 us; 8192 x 28672 gs128, m = 64: 136 against 175 us; 14336 x 4096 (224
 // such tiles), m = 32 / 48: 25 / 48 against 30 / 30 us.
-uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m) {
+uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m, bool can_split) {
   if (m <= 16u || m > 128u) return 0;
-  const PrefillPick pick = prefill_pick(w, m, (uint32_t)device_cu_count());
+  const PrefillPick pick = prefill_pick(w, m, (uint32_t)device_cu_count(), can_split);
   if (pick.est_us < 0.0) return 0;
   const double bytes = (double)w.N * w.K + 4.0 * w.N * (w.K / w.gs);
   uint32_t rows;

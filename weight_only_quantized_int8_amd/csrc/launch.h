@@ -57,7 +57,12 @@ hipError_t launch_gemm_smallm(const WeightView &w, const uint16_t *X, uint16_t *
                               hipStream_t stream);
 
 // Y[m, N] = X[m, K] W^T for large m (weight tiles dequantized to BF16 in LDS).
-hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
+// With a workspace (ws != nullptr, at least gemm_prefill_workspace_bytes; no
+// initial value) a grid with too few tiles splits K over several work items
+// per tile, whose fp32 partials a second launch adds in a fixed order;
+// ws == nullptr never splits.
+uint64_t gemm_prefill_workspace_bytes(const WeightView &w, uint32_t m);
+hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, void *ws,
                                hipStream_t stream);
 
 // The small-m kernel with two 16-row X tiles per pass (2 <= m <= 32), where
@@ -68,8 +73,9 @@ hipError_t launch_gemm_smallm32(const WeightView &w, const uint16_t *X, uint16_t
 
 // For 16 < m <= 128: the rows per small-m pass (32, or 16 where only the
 // one-tile kernel fits) if passes over slices of X are expected to beat the
-// tiled kernel (a grid of few tiles, each walking all of K), else 0.
-uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m);
+// tiled kernel (a grid of few tiles, each walking all of K; split over K
+// when can_split), else 0.
+uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m, bool can_split);
 
 // Calibration streams (not part of the layer path): read `bytes` once, or
 // copy them; bytes a multiple of 1024.
