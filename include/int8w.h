@@ -243,6 +243,22 @@ uint64_t int8_gemm_workspace_bytes(const int8w_weight *w, uint32_t m);
 int int8_gemm_ws(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, void *workspace,
                  uint64_t workspace_bytes, uint64_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): int8_gemm_ws
+ * with the workspace taken from a static device array that the library holds
+ * on every GPU it runs on, INT8W_NOALLOC_SCRATCH_BYTES (64 MiB) each, until
+ * the process ends.  Same arguments, kernels and result bits as int8_gemm_ws
+ * with a workspace of at least int8_gemm_workspace_bytes(w, m); nothing is
+ * allocated or freed (no hipMalloc / hipFree, no allocating library call).
+ * The array needs no initial value and keeps the last call's partials.  All
+ * calls on one GPU share it: calls that can overlap on that GPU (several
+ * streams or host threads) race.  Errors: INT8W_ERR_SHAPE when
+ * int8_gemm_workspace_bytes(w, m) exceeds INT8W_NOALLOC_SCRATCH_BYTES
+ * (nothing is enqueued; int8_gemm_ws takes any size), INT8W_ERR_HIP when the
+ * array's device address cannot be looked up; otherwise as int8_gemm. */
+#define INT8W_NOALLOC_SCRATCH_BYTES (64u << 20)
+int int8_gemm_noalloc(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, uint64_t stream);
+
 /* Human-readable description of the calling thread's most recent error
  * ("" if none).  The pointer stays valid until the thread's next call. */
 const char *int8w_last_error(void);

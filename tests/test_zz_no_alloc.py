@@ -1,0 +1,99 @@
+"""int8_gemm_noalloc (the gemm whose split-K workspace is the library's static
+device scratch) against int8_gemm_ws (the same gemm with a caller-allocated
+workspace): bit-identical outputs on consecutive calls, the second one
+smaller, so the scratch holds the first call's partials when the second
+starts; shapes that do not split, the same bits as int8_gemm; a call whose
+split needs more than the scratch holds is rejected before anything runs.
+A few rows of the split result are also checked against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_close, bits_to_dev, dev_to_bits, make_weight, upload
+from weight_only_quantized_int8_amd import binding as B
+from weight_only_quantized_int8_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _poisoned(m, n):
+    return torch.full((m, n), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+def _run_ws(W, Xd, m):
+    need = B.int8_gemm_workspace_bytes(W.desc, m)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    Y = _poisoned(m, W.out_features)
+    rc = B.int8_gemm_ws(W.desc, Xd.data_ptr(), Y.data_ptr(), m, ws.data_ptr(), ws.numel(), _stream())
+    assert rc == 0, B.load_library().int8w_last_error()
+    return Y
+
+
+def _run_noalloc(W, Xd, m):
+    Y = _poisoned(m, W.out_features)
+    rc = B.int8_gemm_noalloc(W.desc, Xd.data_ptr(), Y.data_ptr(), m, _stream())
+    assert rc == 0, B.load_library().int8w_last_error()
+    return Y
+
+
+def test_noalloc_split_two_calls_then_smaller():
+    N, K, gs = 4096, 14336, 64
+    w, rng = make_weight(7_100, N, K, gs)
+    W = upload(w)
+    for m in (600, 200):  # 60 MiB of partials, then 28 MiB over the first call's
+        need = B.int8_gemm_workspace_bytes(W.desc, m)
+        log(f"noalloc split m={m} {N}x{K} gs{gs} need={need}")
+        assert 0 < need <= B.NOALLOC_SCRATCH_BYTES, "the shape is expected to split within the scratch"
+        X = synth.gen_act(rng, (m, K))
+        Xd = bits_to_dev(X)
+        Y_na = _run_noalloc(W, Xd, m)
+        Y_ws = _run_ws(W, Xd, m)
+        torch.cuda.synchronize()
+        got, exp = dev_to_bits(Y_na), dev_to_bits(Y_ws)
+        assert np.array_equal(got, exp), f"m={m}: {np.count_nonzero(got != exp)} outputs differ from int8_gemm_ws"
+        rows = np.array([0, 1, m // 2, m - 1])
+        Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X[rows])
+        assert_close(got[rows], Y_ref, A, f"noalloc m={m} sampled rows")
+
+
+@pytest.mark.parametrize("m,N,K,gs", [(2048, 4096, 4096, 64), (8, 512, 1024, 32), (1, 256, 512, 128)])
+def test_noalloc_unsplit_matches_int8_gemm(m, N, K, gs):
+    log(f"noalloc unsplit m={m} {N}x{K} gs{gs}")
+    w, rng = make_weight(7_200 + m, N, K, gs)
+    W = upload(w)
+    assert B.int8_gemm_workspace_bytes(W.desc, m) == 0
+    Xd = bits_to_dev(synth.gen_act(rng, (m, K)))
+    Y_na = _run_noalloc(W, Xd, m)
+    Y = _poisoned(m, N)
+    assert B.int8_gemm(W.desc, Xd.data_ptr(), Y.data_ptr(), m, _stream()) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_bits(Y_na), dev_to_bits(Y))
+
+
+def test_noalloc_rejects_split_beyond_scratch():
+    # 28672 x 28672 at m = 256 splits over 224 MiB of partials
+    N, K, gs, m = 28672, 28672, 64, 256
+    packed = torch.empty(N * K // 4, dtype=torch.int32, device="cuda")
+    scales = torch.empty(N * (K // gs), dtype=torch.int16, device="cuda")
+    biases = torch.empty(N * (K // gs), dtype=torch.int16, device="cuda")
+    desc = B.WeightDesc(packed.data_ptr(), scales.data_ptr(), biases.data_ptr(), N, K, gs)
+    need = B.int8_gemm_workspace_bytes(desc, m)
+    log(f"noalloc reject m={m} {N}x{K} need={need}")
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    X = torch.zeros((m, K), dtype=torch.bfloat16, device="cuda")
+    Y = _poisoned(m, N)
+    rc = B.int8_gemm_noalloc(desc, X.data_ptr(), Y.data_ptr(), m, _stream())
+    torch.cuda.synchronize()
+    assert rc == B.INT8W_ERR_SHAPE
+    assert b"scratch" in B.load_library().int8w_last_error()
+    assert bool((Y.view(torch.int16) == -1).all()), "a rejected call must enqueue nothing"

@@ -38,7 +38,7 @@ ERROR_NAMES = {
 EXPORTED = (
     "int8w_validate", "int8w_storage_bytes", "int8_dequantize_to", "int8_gemv", "int8_gemv_silu_gate",
     "int8_gemv_silu_gate_resid", "int8_gemm", "int8_gemv_multi", "int8_quantize", "int8_moe_gemv",
-    "int8w_fp8_gemv", "int8w_last_error", "int8_gemm_workspace_bytes", "int8_gemm_ws",
+    "int8w_fp8_gemv", "int8w_last_error", "int8_gemm_workspace_bytes", "int8_gemm_ws", "int8_gemm_noalloc",
 )
 # calibration streams declared in include/int8w_measure.h
 EXPORTED_MEASURE = ("int8w_stream_read", "int8w_stream_copy")
@@ -125,6 +125,8 @@ def load_library() -> ctypes.CDLL:
     lib.int8_gemm_workspace_bytes.restype = ctypes.c_uint64
     lib.int8_gemm_ws.argtypes = [W, P, P, ctypes.c_uint32, P, u64, u64]
     lib.int8_gemm_ws.restype = ctypes.c_int
+    lib.int8_gemm_noalloc.argtypes = [W, P, P, ctypes.c_uint32, u64]
+    lib.int8_gemm_noalloc.restype = ctypes.c_int
     lib.int8w_stream_read.argtypes = [P, u64, P, u64]
     lib.int8w_stream_read.restype = ctypes.c_int
     lib.int8w_stream_copy.argtypes = [P, P, u64, u64]
@@ -191,6 +193,13 @@ def int8_gemm_workspace_bytes(desc: WeightDesc, m: int) -> int:
 
 def int8_gemm_ws(desc: WeightDesc, x: int, y: int, m: int, ws: int, ws_bytes: int, stream: int) -> int:
     return load_library().int8_gemm_ws(ctypes.byref(desc), x, y, m, ws, ws_bytes, stream)
+
+
+def int8_gemm_noalloc(desc: WeightDesc, x: int, y: int, m: int, stream: int) -> int:
+    return load_library().int8_gemm_noalloc(ctypes.byref(desc), x, y, m, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # INT8W_NOALLOC_SCRATCH_BYTES
 
 
 def int8w_stream_read(src: int, nbytes: int, sink: int, stream: int) -> int:

@@ -27,7 +27,7 @@ COMMON = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 SOURCES = ["dequant.hip", "quantize.hip", "gemv.hip", "fp8_gemv.hip", "gemm_smallm.hip", "gemm_prefill.hip",
-           "measure.hip", "capi.cpp"]
+           "measure.hip", "noalloc.hip", "capi.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -332,7 +332,14 @@ int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const
 }  // extern "C"
 
 namespace int8w {
-namespace {
+
+int report_error(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
 
 // gemm with an optional workspace (ws == nullptr: the tiled kernel never
 // splits K).  ws_bytes is checked against what the chosen launch needs.
@@ -397,7 +404,6 @@ int gemm_common(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t 
   return finish_launch(e, s);
 }
 
-}  // namespace
 }  // namespace int8w
 
 extern "C" {

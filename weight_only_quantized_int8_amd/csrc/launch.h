@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "int8w.h"
+
 namespace int8w {
 
 struct WeightView {
@@ -81,5 +83,12 @@ uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m, bool can_split)
 // copy them; bytes a multiple of 1024.
 hipError_t launch_stream_read(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t stream);
 hipError_t launch_stream_copy(const void *src, void *dst, uint64_t bytes, hipStream_t stream);
+
+// ---- C-ABI internals shared by capi.cpp and noalloc.hip
+// Records the calling thread's last error message and returns code.
+int report_error(int code, const char *fmt, ...);
+// int8_gemm / int8_gemm_ws: ws == nullptr never splits K.
+int gemm_common(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t m, void *ws,
+                uint64_t ws_bytes, uint64_t stream);
 
 }  // namespace int8w
