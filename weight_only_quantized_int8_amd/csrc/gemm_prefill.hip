@@ -422,13 +422,22 @@ struct SplitK {
 //    registers, and wait for step k + 1's X DMA, issued one iteration
 //    earlier; barrier k then publishes step k + 1 while the MFMA waves
 //    consume step k.
+//  * The producers split by the kind of load they issue: two waves issue
+//    only DMA (X and the scale/bias blocks), the others only register loads
+//    of codes.  A wave's partial vmcnt wait is then a count of loads of one
+//    kind, which land in issue order.  When one wave mixed the kinds, waiting
+//    for all but its younger register loads was seen to let an LDS-DMA load
+//    still be writing its rows after the barrier (nondeterministic rows with
+//    K split into short ranges); waiting for every load instead exposed the
+//    codes' look-ahead at each barrier and cost 10-17 %.
 //  * Scales and biases arrive by DMA in blocks of 8 groups per row (16
 //    bytes; gs / 8 steps), double-buffered in LDS: per step a producer reads
 //    one scale and one bias per row it dequantizes from LDS instead of
 //    issuing two 2-byte global loads.  Needs K % (8 gs) == 0.
-//  * Measured on MI355X (m = 2048, 14336 x 4096): per-instruction costs of
-//    the producers' global loads set the pace, not the MFMAs; staging X and
-//    the scales/biases by DMA took 292 us to about 268 us.
+//  * Measured on MI355X (graph-timed): m = 2048 on 14336 x 4096 in 249 us
+//    and on 4096 x 14336 in 200 us (1.2 PFLOP/s); one producer role per
+//    wave took them from 267 / 230 us (every producer issuing both kinds and
+//    waiting for all of its loads at each barrier).
 template <int BM, int BN, int WGM, int WGN, int NP>
 __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
@@ -436,16 +445,10 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
     uint32_t N, uint32_t K, uint32_t m, uint32_t gs_log2, uint32_t mtiles, uint32_t nbig, uint32_t mt_half,
     uint32_t nt_big, uint32_t nwork, SplitK sk) {
   constexpr int kMma = WGM * WGN;          // MFMA waves
-  constexpr int kPT = 64 * NP;             // producer threads
-  constexpr int XR = kPT / 8;              // X rows per producer pass
-  constexpr int WR = kPT / 4;              // weight rows per producer pass
-  constexpr int XP = BM / XR;
-  constexpr int WP = BN / WR;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TI = WTM / 16, TJ = WTN / 16;
-  static_assert(XP >= 1 && WP >= 1 && BM % XR == 0 && BN % WR == 0, "whole load passes");
-  constexpr uint32_t kSbW = BN / 64;  // waves per array in the scale/bias DMA (64 rows each)
-  static_assert(BN % 64 == 0 && 2 * (BN / 64) <= NP, "scale/bias staging: 64 rows of scales or biases per wave");
+  constexpr uint32_t kSbW = BN / 64;  // loads per array in the scale/bias DMA (64 rows each)
+  static_assert(BN % 64 == 0, "scale/bias staging: 64 rows of scales or biases per load");
   constexpr uint32_t kStage = (BM + BN) * BK * 2;
   constexpr uint32_t kSbBytes = BN * 16u * 2u;  // one block: 8 groups of scales and of biases per row
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_pf[];
@@ -492,187 +495,213 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
   const uint32_t ksteps = (kl + BK - 1) / BK;
 
   if (wave >= (uint32_t)kMma) {
-    // ---------------- producer waves
-    const uint32_t ptid = tid - 64u * kMma;
+    // ---------------- producer waves: ND DMA waves (X and the scale/bias
+    // blocks, memory straight into LDS) and NP - ND dequantizing waves (codes
+    // into registers, BF16 weights stored to LDS).  A wave issues loads of
+    // one kind only: a partial vmcnt is then a count of its own DMA loads,
+    // or of its own register loads, and each kind lands in issue order.
+    constexpr int ND = 2, NQ = NP - ND;
+    constexpr int kQT = 64 * NQ;     // dequantizing threads
+    constexpr int QWR = kQT / 4;     // weight rows per pass (4 chunks of 16 codes per row)
+    constexpr int QWP = BN / QWR;    // passes per step
+    static_assert(NQ >= 1 && QWP >= 1 && BN % QWR == 0, "whole weight passes");
+    static_assert((2 * kSbW) % ND == 0 && BM % (16 * ND) == 0, "whole DMA shares");
+    constexpr int kSbPer = (int)(2 * kSbW) / ND;  // scale/bias loads per DMA wave and block
     const uint32_t G = K >> gs_log2;
     const uint32_t mrows = m - m0 < tile_rows ? m - m0 : tile_rows;
     const uint32_t nrows = N - n0 < (uint32_t)BN ? N - n0 : (uint32_t)BN;
-    // views start at the item's first K position; rows keep their full stride
     const uint32_t gb = kb >> gs_log2;
-    const auto rx = make_rsrc(X + (size_t)m0 * K + kb, mrows * K * 2u - 2u * kb);
-    const auto rw = make_rsrc(codes + (size_t)n0 * K + kb, nrows * K - kb);
-    const auto rs = make_rsrc(scales + (size_t)n0 * G + gb, nrows * G * 2u - 2u * gb);
-    const auto rb = make_rsrc(biases + (size_t)n0 * G + gb, nrows * G * 2u - 2u * gb);
-    const uint32_t wr = ptid >> 2, wp = ptid & 3u;
-    // The producer schedule, for XJN X loads per wave and step (the wait
-    // counts below are compile-time immediates, hence a template).
-    auto run = [&](auto xjn) {
-      constexpr int XJN = decltype(xjn)::value;
-      // X by DMA: one instruction fills 8 LDS rows (1 KiB, lane i -> byte 16 i);
-      // lane i carries row r0 + i / 8 and, through the swizzle, logical chunk
-      // (i % 8) ^ (i / 8).  Producer wave pw fills rows 8 (j NP + pw) .. + 7.
-      constexpr int XJ = XJN;  // X loads per wave and step (half for a half tile)
-      const uint32_t pw = wave - (uint32_t)kMma, plane = lane;
-      const uint32_t xchunk = (plane & 7u) ^ (plane >> 3);
-      uint32_t vxd[XJ];
+    const uint32_t sbs_log2 = gs_log2 - 3u;  // steps per scale/bias block, log2
+    const uint32_t nblk = kl >> (gs_log2 + 3u);
+    auto sbuf = [&](uint32_t i) { return lds_pf + 3u * kStage + i * kSbBytes; };
+    const uint32_t pw = wave - (uint32_t)kMma;
+    // Steps 0 .. ksteps - 2 are the loop's, three to an iteration, one barrier
+    // each; the loop has a single exit (with an exit after every step the
+    // compiler's wait counts at the loop head also cover the paths that leave).
+    const uint32_t nst = ksteps - 1u;
+    if (pw < (uint32_t)ND) {
+      // ---- DMA wave d: X rows 8 (j ND + d) .. + 7 of every step, and the
+      // scale/bias loads d, d + ND, ... of every block
+      const uint32_t d = pw;
+      const auto rx = make_rsrc(X + (size_t)m0 * K + kb, mrows * K * 2u - 2u * kb);
+      const auto rs = make_rsrc(scales + (size_t)n0 * G + gb, nrows * G * 2u - 2u * gb);
+      const auto rb = make_rsrc(biases + (size_t)n0 * G + gb, nrows * G * 2u - 2u * gb);
+      auto run = [&](auto xjn) {
+        constexpr int XJ = decltype(xjn)::value;  // X loads per DMA wave and step
+        const uint32_t xchunk = (lane & 7u) ^ (lane >> 3);
+        uint32_t vxd[XJ];
 #pragma unroll
-      for (int j = 0; j < XJ; ++j) {
-        const uint32_t row = (j * NP + pw) * 8u + (plane >> 3);
-        vxd[j] = row < mrows ? row * K * 2u + xchunk * 16u : kOutOfRange;
-      }
-      auto xdma = [&](uint32_t ks, uint32_t st) {
-        const bool live = ks < ksteps;
-        const uint32_t k0 = live ? ks * BK : 0u;
-        const bool xin = live && k0 + xchunk * 8u < kl;
-#pragma unroll
-        for (int j = 0; j < XJ; ++j)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rx, (__attribute__((address_space(3))) void *)(stage(st) + (j * NP + pw) * 8u * (BK * 2)), 16,
-              (int)(xin ? vxd[j] : kOutOfRange), (int)uniform_pf(2u * k0), 0, 0);
-      };
-      // Scales and biases by DMA, a block of 8 groups (8 gs codes, gs / 8
-      // steps) at a time, double-buffered: wave pw copies 16 bytes per row for
-      // rows 64 (pw % kSbW) .. + 63 of the scales (pw < kSbW) or biases.
-      // Needs K % (8 gs) == 0, so that every row's block is 16 whole bytes.
-      const uint32_t sbs_log2 = gs_log2 - 3u;  // steps per block, log2
-      const uint32_t nblk = kl >> (gs_log2 + 3u);
-      auto sbuf = [&](uint32_t i) { return lds_pf + 3u * kStage + i * kSbBytes; };
-      const uint32_t sbrow = (pw % kSbW) * 64u + plane;
-      const uint32_t vsbd = sbrow < nrows ? sbrow * G * 2u : kOutOfRange;
-      auto sbdma = [&](uint32_t blk) {
-        if (pw < 2u * kSbW)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              pw >= kSbW ? rb : rs,
-              (__attribute__((address_space(3))) void *)(sbuf(blk & 1u) + (pw / kSbW) * (BN * 16u) +
-                                                         (pw % kSbW) * 1024u),
-              16, (int)vsbd, (int)uniform_pf(blk * 16u), 0, 0);
-      };
-      uint32_t vw[WP];
-#pragma unroll
-      for (int p = 0; p < WP; ++p) {
-        const uint32_t row = p * WR + wr;
-        vw[p] = row < nrows ? row * K + wp * 16u : kOutOfRange;
-      }
-      struct Regs {
-        u32x4 w[WP];
-      };
-      auto issue = [&](Regs &r, uint32_t ks) {
-        const bool live = ks < ksteps;
-        const uint32_t k0 = live ? ks * BK : 0u;
-        const bool win = live && k0 + wp * 16u < kl;
-#pragma unroll
-        for (int p = 0; p < WP; ++p)
-          r.w[p] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(win ? vw[p] : kOutOfRange), (int)uniform_pf(k0),
-                                                         kAuxNontemporal);
-      };
-      // Every pass's scale and bias of step ks, read from LDS in one round
-      // trip before the step's DMA and stores are issued (the compiler keeps
-      // LDS reads behind LDS writes that might alias them).
-      struct SbVals {
-        float sc[WP], bi[WP];
-      };
-      auto read_sb = [&](uint32_t ks) {
-        SbVals v;
-        const uint8_t *sb = sbuf((ks >> sbs_log2) & 1u);
-        const uint32_t g = ((ks * BK + wp * 16u) >> gs_log2) & 7u;
-#pragma unroll
-        for (int p = 0; p < WP; ++p) {
-          const uint32_t srow = p * WR + wr;
-          v.sc[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + srow * 16u + 2u * g));
-          v.bi[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + BN * 16u + srow * 16u + 2u * g));
+        for (int j = 0; j < XJ; ++j) {
+          const uint32_t row = (j * ND + d) * 8u + (lane >> 3);
+          vxd[j] = row < mrows ? row * K * 2u + xchunk * 16u : kOutOfRange;
         }
-        return v;
-      };
-      auto store = [&](const Regs &r, uint8_t *buf, const SbVals &v) {
-        uint8_t *ws = buf + BM * BK * 2;
+        auto xdma = [&](uint32_t ks, uint32_t st) {
+          const bool live = ks < ksteps;
+          const uint32_t k0 = live ? ks * BK : 0u;
+          const bool xin = live && k0 + xchunk * 8u < kl;
 #pragma unroll
-        for (int p = 0; p < WP; ++p) {
-          const float sc = v.sc[p], bi = v.bi[p];
-          const uint32_t word[4] = {r.w[p].x, r.w[p].y, r.w[p].z, r.w[p].w};
-          uint32_t o[8];
+          for (int j = 0; j < XJ; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void *)(stage(st) + (j * ND + d) * 8u * (BK * 2)), 16,
+                (int)(xin ? vxd[j] : kOutOfRange), (int)uniform_pf(2u * k0), 0, 0);
+        };
+        // load i of a block: 16 bytes per row for rows 64 (i % kSbW) .. + 63
+        // of the scales (i < kSbW) or the biases
+        auto sbdma = [&](uint32_t blk) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            o[2 * i] = pack_bf16x2(__builtin_fmaf(code_f32(word[i], 0), sc, bi), __builtin_fmaf(code_f32(word[i], 1), sc, bi));
-            o[2 * i + 1] =
-                pack_bf16x2(__builtin_fmaf(code_f32(word[i], 2), sc, bi), __builtin_fmaf(code_f32(word[i], 3), sc, bi));
+          for (int c = 0; c < kSbPer; ++c) {
+            const uint32_t i = d + (uint32_t)c * ND;
+            const uint32_t sbrow = (i % kSbW) * 64u + lane;
+            const uint32_t vsbd = sbrow < nrows ? sbrow * G * 2u : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                i >= kSbW ? rb : rs,
+                (__attribute__((address_space(3))) void *)(sbuf(blk & 1u) + (i / kSbW) * (BN * 16u) +
+                                                           (i % kSbW) * 1024u),
+                16, (int)vsbd, (int)uniform_pf(blk * 16u), 0, 0);
           }
-          const uint32_t row = p * WR + wr;
-          *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp)) = u32x4{o[0], o[1], o[2], o[3]};
-          *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp + 1u)) = u32x4{o[4], o[5], o[6], o[7]};
-        }
-      };
-      // vmcnt(n) with expcnt and lgkmcnt left open
+        };
 #define INT8W_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
-      Regs R0, R1, R2;
-      // Iteration k (between barriers k - 1 and k): the X DMA of step k + 2
-      // goes to stage (k + 2) % 3 (it held step k - 1, read before barrier
-      // k - 1); step k + 1's weights are dequantized into stage (k + 1) % 3;
-      // step k + 4's codes are requested; and every load of the wave is
-      // awaited.  Barrier k thus publishes step k + 1 (whose X arrived during
-      // iteration k - 1) and k + 2's.
-      sbdma(0u);
-      if (1u < nblk) sbdma(1u);
-      issue(R0, 0);
-      issue(R1, 1);
-      issue(R2, 2);
-      xdma(0u, 0u);
-      xdma(1u, 1u);
-      INT8W_VMCNT(3 * WP + 2 * XJ);  // scale/bias blocks 0 and 1 have landed
-      __syncthreads();  // ... for every producer wave
-      store(R0, stage(0u), read_sb(0u));
-      issue(R0, 3);
-      INT8W_VMCNT(XJ + WP);  // the X DMA of step 0 has landed
-      __syncthreads();  // step 0 is in LDS
-      auto step = [&](Regs &r, uint32_t k, uint32_t sx, uint32_t sw) {
-        const uint32_t s = k + 1u;
-        const SbVals v = read_sb(s);
-        xdma(k + 2u, sx);
-        store(r, stage(sw), v);
-        issue(r, k + 4u);
-        // at the first step of scale/bias block b, block b + 1 goes into the
-        // buffer that held block b - 1
-        if (s != 0u && (s & ((1u << sbs_log2) - 1u)) == 0u && (s >> sbs_log2) + 1u < nblk) sbdma((s >> sbs_log2) + 1u);
-        // Everything this wave requested has landed (vmcnt(0)) and its LDS
-        // stores are done; then the barrier that publishes step k + 1.  A
-        // partial count -- all but the XJ + 2 WP youngest loads, leaving
-        // step k + 2's X and the codes of step k + 4 in flight -- is not
-        // enough: an LDS-DMA load was seen still writing its rows after
-        // younger register loads had been counted off (nondeterministic
-        // rows in a probe of short K ranges; gone with vmcnt(0), which
-        // costs 10-17 %).  So the X of step k + 2, requested at the start of
-        // this step, has this step's length to land, and the scale/bias
-        // blocks are covered the same way.
-        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
-        asm volatile("s_barrier" ::: "memory");
-      };
+        static_assert(2 * XJ + kSbPer < 64, "vmcnt range");
+        sbdma(0u);
+        if (1u < nblk) sbdma(1u);
+        xdma(0u, 0u);
+        xdma(1u, 1u);
+        INT8W_VMCNT(2 * XJ);  // scale/bias blocks 0 and 1 have landed
+        __syncthreads();      // ... published for the dequantizing waves
+        INT8W_VMCNT(XJ);      // the X of step 0 has landed
+        __syncthreads();      // step 0 is in LDS
+        // Iteration k (between barriers k - 1 and k): step k + 2's X goes to
+        // stage (k + 2) % 3 (it held step k - 1, read before barrier k - 1);
+        // at the first step of scale/bias block b, block b + 1 goes to the
+        // buffer that held block b - 1; then step k + 1's X, requested one
+        // iteration earlier, is awaited (everything older than this
+        // iteration's loads) and barrier k publishes it.  A scale/bias block
+        // requested here is older than the next iteration's X, so it has
+        // landed by the next barrier, before its first reader (gs / 8 >= 4
+        // steps on).
+        auto step = [&](uint32_t k, uint32_t sx) {
+          const uint32_t s = k + 1u;
+          xdma(k + 2u, sx);
+          if (s != 0u && (s & ((1u << sbs_log2) - 1u)) == 0u && (s >> sbs_log2) + 1u < nblk) {
+            sbdma((s >> sbs_log2) + 1u);
+            INT8W_VMCNT(XJ + kSbPer);
+          } else {
+            INT8W_VMCNT(XJ);
+          }
+          asm volatile("s_barrier" ::: "memory");
+        };
 #undef INT8W_VMCNT
-      // Steps 0 .. ksteps - 2, three to an iteration and the rest after the
-      // loop.  The loop has a single exit: with an exit after every step the
-      // compiler's wait counts at the loop head also cover the paths that
-      // leave, and it waited for every load in flight once per iteration.
-      const uint32_t nst = ksteps - 1u;
-      uint32_t k = 0;
-      for (; k + 3u <= nst; k += 3u) {
-        step(R1, k, 2u, 1u);
-        step(R2, k + 1u, 0u, 2u);
-        step(R0, k + 2u, 1u, 0u);
-      }
-      if (k < nst) {
-        step(R1, k, 2u, 1u);
-        if (k + 1u < nst) step(R2, k + 1u, 0u, 2u);
-      }
-      // The last steps requested X past the end (zeros into LDS) and codes
-      // that nobody reads.  Wait for all of it before the wave ends: an
-      // LDS-DMA write still in flight when the workgroup finishes lands in
-      // the LDS of the next workgroup on the CU.  (Seen as nondeterministic
-      // tiles on grids of more than one round whose K-step count is a
-      // multiple of 3: the stray zeros hit stage 0 of the next tile.)
-      __builtin_amdgcn_s_waitcnt(0);
+        uint32_t k = 0;
+        for (; k + 3u <= nst; k += 3u) {
+          step(k, 2u);
+          step(k + 1u, 0u);
+          step(k + 2u, 1u);
+        }
+        if (k < nst) {
+          step(k, 2u);
+          if (k + 1u < nst) step(k + 1u, 0u);
+        }
+        // the last steps requested X past the end (zeros into LDS): an
+        // LDS-DMA write still in flight when the workgroup ends would land in
+        // the LDS of the next workgroup on the CU
+        __builtin_amdgcn_s_waitcnt(0);
+      };
+      if (half)
+        run(std::integral_constant<int, BM / (16 * ND)>{});
+      else
+        run(std::integral_constant<int, BM / (8 * ND)>{});
+      return;
+    }
+    // ---- dequantizing wave: 16 codes per lane and pass, QWP passes of QWR
+    // rows per step; codes requested three steps ahead into registers
+    const uint32_t qtid = tid - 64u * (uint32_t)(kMma + ND);
+    const auto rw = make_rsrc(codes + (size_t)n0 * K + kb, nrows * K - kb);
+    const uint32_t wr = qtid >> 2, wp = qtid & 3u;
+    uint32_t vw[QWP];
+#pragma unroll
+    for (int p = 0; p < QWP; ++p) {
+      const uint32_t row = p * QWR + wr;
+      vw[p] = row < nrows ? row * K + wp * 16u : kOutOfRange;
+    }
+    struct Regs {
+      u32x4 w[QWP];
     };
-    if (half)
-      run(std::integral_constant<int, BM / (16 * NP)>{});
-    else
-      run(std::integral_constant<int, BM / (8 * NP)>{});
+    auto issue = [&](Regs &r, uint32_t ks) {
+      const bool live = ks < ksteps;
+      const uint32_t k0 = live ? ks * BK : 0u;
+      const bool win = live && k0 + wp * 16u < kl;
+#pragma unroll
+      for (int p = 0; p < QWP; ++p)
+        r.w[p] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(win ? vw[p] : kOutOfRange), (int)uniform_pf(k0),
+                                                       kAuxNontemporal);
+    };
+    // every pass's scale and bias of step ks, read from LDS in one round trip
+    // before the step's stores (the compiler keeps LDS reads behind LDS
+    // writes that might alias them)
+    struct SbVals {
+      float sc[QWP], bi[QWP];
+    };
+    auto read_sb = [&](uint32_t ks) {
+      SbVals v;
+      const uint8_t *sb = sbuf((ks >> sbs_log2) & 1u);
+      const uint32_t g = ((ks * BK + wp * 16u) >> gs_log2) & 7u;
+#pragma unroll
+      for (int p = 0; p < QWP; ++p) {
+        const uint32_t srow = p * QWR + wr;
+        v.sc[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + srow * 16u + 2u * g));
+        v.bi[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + BN * 16u + srow * 16u + 2u * g));
+      }
+      return v;
+    };
+    auto store = [&](const Regs &r, uint8_t *buf, const SbVals &v) {
+      uint8_t *ws = buf + BM * BK * 2;
+#pragma unroll
+      for (int p = 0; p < QWP; ++p) {
+        const float sc = v.sc[p], bi = v.bi[p];
+        const uint32_t word[4] = {r.w[p].x, r.w[p].y, r.w[p].z, r.w[p].w};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = pack_bf16x2(__builtin_fmaf(code_f32(word[i], 0), sc, bi), __builtin_fmaf(code_f32(word[i], 1), sc, bi));
+          o[2 * i + 1] =
+              pack_bf16x2(__builtin_fmaf(code_f32(word[i], 2), sc, bi), __builtin_fmaf(code_f32(word[i], 3), sc, bi));
+        }
+        const uint32_t row = p * QWR + wr;
+        *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp)) = u32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp + 1u)) = u32x4{o[4], o[5], o[6], o[7]};
+      }
+    };
+    Regs R0, R1, R2;
+    issue(R0, 0);
+    issue(R1, 1);
+    issue(R2, 2);
+    __syncthreads();  // the scale/bias blocks 0 and 1 are in LDS
+    store(R0, stage(0u), read_sb(0u));
+    issue(R0, 3);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): step 0's weights are stored
+    __syncthreads();  // step 0 is in LDS
+    // Iteration k: step k + 1's weights are dequantized into stage (k + 1) % 3
+    // from codes requested three iterations earlier, step k + 4's codes are
+    // requested, and barrier k publishes the stores.  The code loads stay in
+    // flight across the barrier.
+    auto step = [&](Regs &r, uint32_t k, uint32_t sw) {
+      const SbVals v = read_sb(k + 1u);
+      store(r, stage(sw), v);
+      issue(r, k + 4u);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+    };
+    uint32_t k = 0;
+    for (; k + 3u <= nst; k += 3u) {
+      step(R1, k, 1u);
+      step(R2, k + 1u, 2u);
+      step(R0, k + 2u, 0u);
+    }
+    if (k < nst) {
+      step(R1, k, 1u);
+      if (k + 1u < nst) step(R2, k + 1u, 2u);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     return;
   }
 
