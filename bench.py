@@ -9,16 +9,20 @@ stream different bytes and the 256 MB last-level cache cannot serve them.
 
 value = algorithmic bytes per step (codes + scales + biases of every weight,
 plus the activations each launch reads and writes) / time per step, in GB/s:
-each layer's launches replayed as a HIP graph, a HIP event after every step,
-the median of 20 batches of consecutive steps.  The roofline object reports
+the steps replayed as HIP graphs of up to 12 consecutive steps (so that the
+host's cost of launching a graph does not sit between steps; the launches keep
+their stream order), a HIP event after every graph, the median of 20 batches
+of consecutive graphs.  The roofline object reports
 the dominant kernel (the gate+up gemv_multi launch), the median over graph
 replays of that launch alone.  Secondary lines, each the median of 20 graph
 replays over rotated weights: every single-launch call of the decode
 workloads (gemv on the gate, q/o and k/v shapes, gemv_silu_gate and
 gemv_silu_gate_resid on the 8B and 70B down shapes), dequantize_to of the
-70B-shaped weight, the own-built streaming read and copy (the achievable
-ceilings beside the nominal 8 TB/s), the quantizer, the expert-indexed gemv,
-the FP8 gemv, the small-batch gemm and the prefill gemm in TFLOP/s.
+70B-shaped weight, the own-built streaming read (at the byte counts of the
+q/o, gate/up and 70B down weights), copy and expand (the achievable ceilings
+beside the nominal 8 TB/s; each streaming line carries its fraction of the
+matching ceiling), the quantizer, the expert-indexed gemv, the FP8 gemv, the
+small-batch gemm and the prefill gemm in TFLOP/s.
 cpu_baseline: the oracle on the host cores, at all cores and at one thread.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
@@ -166,13 +170,18 @@ class DecodeLayers:
                 b.record()
                 timings.append((name, a, b))
 
-    def graphs(self, plan):
-        """One HIP graph per rotated layer holding that layer's launches."""
+    def graphs(self, plan, per=1):
+        """HIP graphs of `per` consecutive steps each (the layers in rotation),
+        one per starting layer: graph j runs steps j, j + 1, ..., j + per - 1
+        (mod the layer count).  Several steps per graph keep the host's graph
+        launch cost off the GPU's critical path; the launches inside keep
+        their stream order, so every step still runs after the one before."""
         out = []
         for li in range(len(self.layers)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                self.step(li, plan)
+                for s in range(per):
+                    self.step(li + s, plan)
             out.append(g)
         for g in out:
             g.replay()
@@ -180,13 +189,26 @@ class DecodeLayers:
         return out
 
 
-def time_graph_steps(graphs, steps):
-    """Seconds per step over `steps` replays (cycling the layers), HIP events on the replay stream."""
+def steps_per_graph(steps, most=12):
+    """The largest count of steps per graph, at most `most`, that divides `steps`."""
+    return max(d for d in range(1, most + 1) if steps % d == 0)
+
+
+def replay_steps(graphs, per, steps, events=None):
+    """Exactly `steps` steps as steps / per graph replays, continuing the layer
+    rotation from one replay to the next; a HIP event after each replay."""
+    for r in range(steps // per):
+        graphs[(r * per) % len(graphs)].replay()
+        if events is not None:
+            events[r + 1].record()
+
+
+def time_graph_steps(graphs, per, steps):
+    """Seconds per step over `steps` steps replayed as graphs of `per` steps, HIP events on the replay stream."""
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(steps):
-        graphs[i % len(graphs)].replay()
+    replay_steps(graphs, per, steps)
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / 1e3 / steps
@@ -308,10 +330,11 @@ class GemmTarget(Target):
 
 
 class StreamReadTarget(Target):
-    """The own-built streaming read over the bytes of one gate/up weight's codes."""
+    """The own-built streaming read over as many bytes as one weight's codes
+    (by default the 8B gate/up weight's)."""
 
-    def __init__(self, nbytes=14336 * 4096):
-        super().__init__("stream_read", "k_stream_read", _src("measure.hip"), 30, bytes_=nbytes,
+    def __init__(self, name="stream_read", nbytes=14336 * 4096):
+        super().__init__(name, "k_stream_read", _src("measure.hip"), 30, bytes_=nbytes,
                          note=f"plain streaming read of {nbytes} bytes")
         self.n = nbytes
 
@@ -337,6 +360,22 @@ class StreamCopyTarget(Target):
                                                    torch.cuda.current_stream().cuda_stream)
 
 
+class StreamExpandTarget(Target):
+    """The own-built streaming expand: every byte widened to 16 bits (one byte
+    read, two written: dequantize_to's mix)."""
+
+    def __init__(self, nbytes=128 << 20):
+        super().__init__("stream_expand", "k_stream_expand", _src("measure.hip"), 10, bytes_=3 * nbytes,
+                         note=f"plain streaming expand of {nbytes} bytes to {2 * nbytes} (read + 2 x write)")
+        self.n = nbytes
+
+    def setup(self, dev):
+        src = [torch.ones(self.n, dtype=torch.uint8, device=dev) for _ in range(copies_for(self.n))]
+        dst = [torch.empty(2 * self.n, dtype=torch.uint8, device=dev) for _ in range(2)]
+        return lambda i: binding.int8w_stream_expand(src[i % len(src)].data_ptr(), dst[i % 2].data_ptr(), self.n,
+                                                     torch.cuda.current_stream().cuda_stream)
+
+
 TARGETS = {t.name: t for t in [
     GateUpTarget(),
     GemvTarget("gate", 14336, 4096, 64, "gemv"),
@@ -350,8 +389,16 @@ TARGETS = {t.name: t for t in [
     GemmTarget("prefill512", 512, 4096, 14336, 64, "k_gemm_prefill", 10),
     GemmTarget("prefill2048", 2048, 14336, 4096, 64, "k_gemm_prefill", 10),
     StreamReadTarget(),
+    StreamReadTarget("stream_read_q", 4096 * 4096),
+    StreamReadTarget("stream_read_70b", 8192 * 28672),
     StreamCopyTarget(),
+    StreamExpandTarget(),
 ]}
+
+# the own-built ceiling each streaming line is compared with: a plain read of
+# about the same byte count for the gemv lines, the expand for dequantize_to
+CEILING_OF = {"gate": "stream_read", "silu_gate": "stream_read", "down": "stream_read", "qo": "stream_read_q",
+              "kv": "stream_read_q", "down70b": "stream_read_70b", "dequant": "stream_expand"}
 
 
 def traffic_file(name):
@@ -394,10 +441,14 @@ def secondary(dev, quick):
     res = {}
     # the single-launch calls of the decode workloads, the calibration streams,
     # dequantize_to of the 70B-shaped weight, and the profiled gemm shapes
-    for name in ("gate", "qo", "kv", "silu_gate", "down", "down70b", "dequant", "stream_read", "stream_copy"):
+    for name in ("gate", "qo", "kv", "silu_gate", "down", "down70b", "dequant", "stream_read", "stream_read_q",
+                 "stream_read_70b", "stream_copy", "stream_expand"):
         t = TARGETS[name]
         res[name] = measure_target(t, dev)
         print(f"# {name}: {res[name]['us']:.2f} us", file=sys.stderr, flush=True)
+    for name, ceil in CEILING_OF.items():
+        res[name]["ceiling"] = ceil
+        res[name]["frac_of_ceiling"] = res[name]["GB/s"] / res[ceil]["GB/s"]
 
     N, K, gs = 14336, 4096, 64  # quantize an 8B gate/up weight (BF16 -> codes, scales, biases)
     rng = np.random.Generator(np.random.PCG64(4200))
@@ -412,7 +463,9 @@ def secondary(dev, quick):
 
     t = time_batches(quant, 10)
     b = 2 * N * K + N * K + 4 * N * K // gs
-    res["quantize_14336x4096_gs64"] = {"us": t * 1e6, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
+    res["quantize_14336x4096_gs64"] = {"us": t * 1e6, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
+                                       "ceiling": "stream_copy",
+                                       "frac_of_ceiling": b / t / 1e9 / res["stream_copy"]["GB/s"]}
     del wd, packed, sc, bi
     torch.cuda.empty_cache()
 
@@ -741,21 +794,25 @@ def main():
         dl.step(i, FUSED)
     torch.cuda.synchronize()
 
-    # ---- timed region 1: exactly K steps, each layer's launches replayed as
-    # one HIP graph; a HIP event after every step, the steps split into 20
-    # consecutive batches, value from the median batch
-    graphs = dl.graphs(FUSED)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # ---- timed region 1: exactly K steps, replayed as HIP graphs of `per`
+    # consecutive steps (per divides K); a HIP event after every replay, the
+    # replays split into (up to) 20 consecutive batches, value from the median
+    # batch
+    per = steps_per_graph(args.steps)
+    graphs = dl.graphs(FUSED, per)
+    n_rep = args.steps // per
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record()
-    for i in range(args.steps):
-        graphs[i % len(graphs)].replay()
-        ev[i + 1].record()
+    replay_steps(graphs, per, args.steps, ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_s, step_mean_s, n_batches = batch_medians(ev, 1, 20)
+    step_s, step_mean_s, n_batches = batch_medians(ev, per, 20)
     value = step_bytes / step_s / 1e9
+    # the same steps with one graph per step: the host's graph launch cost
+    # then sits between consecutive steps (reported for reference)
+    one_per_graph_s = time_graph_steps(dl.graphs(FUSED, 1), 1, args.steps)
 
     # ---- timed region 2: the dominant launch alone, back to back (see
     # dominant_graph); a HIP event on the launch stream after every replay,
@@ -795,8 +852,8 @@ def main():
         calls[name] = {"weights": list(names), "kind": kind, "bytes": b, "avg_eager_event_us": avg * 1e6,
                        "GB/s": b / avg / 1e9}
 
-    # ---- the same layer as seven single-weight launches (one graph per layer)
-    unfused_s = time_graph_steps(dl.graphs(UNFUSED), args.steps)
+    # ---- the same layer as seven single-weight launches (graphs of `per` steps)
+    unfused_s = time_graph_steps(dl.graphs(UNFUSED, per), per, args.steps)
     unfused = {"launches": len(UNFUSED), "ms_per_step": unfused_s * 1e3,
                "GB/s": plan_bytes(UNFUSED) / unfused_s / 1e9, "bytes_per_step": plan_bytes(UNFUSED)}
 
@@ -807,7 +864,9 @@ def main():
         "config": {"workload": "llama3-8b-shaped decode layer at m=1, group_size=64: gemv_multi(q,k,v), gemv(o), "
                                "gemv_multi(gate,up), gemv_silu_gate_resid(down)",
                    "bytes_per_step": step_bytes, "layers_rotated": n_layers, "frac_hbm_peak": value / HBM_PEAK_GBS,
-                   "timing": f"HIP graph per layer, HIP event after every step, median of {n_batches} batches",
+                   "timing": f"HIP graphs of {per} consecutive steps, HIP event after every graph, "
+                             f"median of {n_batches} batches",
+                   "steps_per_graph": per, "ms_per_step_one_graph_per_step": one_per_graph_s * 1e3,
                    "mean_ms_per_step": step_mean_s * 1e3, "wall_s": wall},
         "roofline": roofline,
         "calls": calls,

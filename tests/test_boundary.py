@@ -53,6 +53,11 @@ def test_library_exports_every_declared_symbol():
     (lambda: B.int8w_stream_copy(A16, 0, 1024, 0), B.INT8W_ERR_NULL, "dst is NULL"),
     (lambda: B.int8w_stream_copy(A16, A16 + 512, 1024, 0), B.INT8W_ERR_ALIAS, "overlaps"),
     (lambda: B.int8w_stream_copy(A16, 2 * A16 + 4, 1024, 0), B.INT8W_ERR_ALIGN, "dst is not 16-byte"),
+    (lambda: B.int8w_stream_expand(A16, 0, 1024, 0), B.INT8W_ERR_NULL, "dst is NULL"),
+    # the expand writes 2 * bytes: a dst 1024 bytes below src overlaps it
+    (lambda: B.int8w_stream_expand(A16 + 1024, A16, 1024, 0), B.INT8W_ERR_ALIAS, "overlaps"),
+    (lambda: B.int8w_stream_expand(A16, A16 + 2048 + 8, 1024, 0), B.INT8W_ERR_ALIGN, "dst is not 16-byte"),
+    (lambda: B.int8w_stream_expand(A16, A16 + 4096, 1000, 0), B.INT8W_ERR_SHAPE, "multiple of 1024"),
 ])
 def test_calibration_streams_reject_invalid_calls(call, code, text):
     rc, msg = err(call())

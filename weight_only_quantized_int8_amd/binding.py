@@ -41,7 +41,7 @@ EXPORTED = (
     "int8w_fp8_gemv", "int8w_last_error", "int8_gemm_workspace_bytes", "int8_gemm_ws", "int8_gemm_noalloc",
 )
 # calibration streams declared in include/int8w_measure.h
-EXPORTED_MEASURE = ("int8w_stream_read", "int8w_stream_copy")
+EXPORTED_MEASURE = ("int8w_stream_read", "int8w_stream_copy", "int8w_stream_expand")
 FP8_PER_ROW, FP8_BLOCK_BF16, FP8_BLOCK_F32, FP8_SINGLE = 0, 1, 2, 3  # INT8W_FP8_*
 MAX_MULTI = 4  # INT8W_MAX_MULTI
 MAX_MOE_SLOTS = 65536  # INT8W_MAX_MOE_SLOTS
@@ -131,6 +131,8 @@ def load_library() -> ctypes.CDLL:
     lib.int8w_stream_read.restype = ctypes.c_int
     lib.int8w_stream_copy.argtypes = [P, P, u64, u64]
     lib.int8w_stream_copy.restype = ctypes.c_int
+    lib.int8w_stream_expand.argtypes = [P, P, u64, u64]
+    lib.int8w_stream_expand.restype = ctypes.c_int
     lib.int8w_last_error.argtypes = []
     lib.int8w_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -208,6 +210,10 @@ def int8w_stream_read(src: int, nbytes: int, sink: int, stream: int) -> int:
 
 def int8w_stream_copy(src: int, dst: int, nbytes: int, stream: int) -> int:
     return load_library().int8w_stream_copy(src, dst, nbytes, stream)
+
+
+def int8w_stream_expand(src: int, dst: int, nbytes: int, stream: int) -> int:
+    return load_library().int8w_stream_expand(src, dst, nbytes, stream)
 
 
 def int8_gemv_multi(descs, x: int, ys, stream: int) -> int:

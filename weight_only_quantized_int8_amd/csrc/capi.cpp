@@ -461,4 +461,16 @@ int int8w_stream_copy(const void *src, void *dst, uint64_t bytes, uint64_t strea
   return finish_launch(launch_stream_copy(src, dst, bytes, s), s);
 }
 
+int int8w_stream_expand(const void *src, void *dst, uint64_t bytes, uint64_t stream) {
+  int rc = check_stream_args(src, bytes);
+  if (rc) return rc;
+  if (!dst) return fail(INT8W_ERR_NULL, "dst is NULL");
+  if (!aligned(dst, 16)) return fail(INT8W_ERR_ALIGN, "dst is not 16-byte aligned");
+  if (overlaps(range("dst", dst, 2 * bytes), range("src", src, bytes)))
+    return fail(INT8W_ERR_ALIAS, "dst overlaps src");
+  (void)hipGetLastError();
+  hipStream_t s = as_stream(stream);
+  return finish_launch(launch_stream_expand(src, dst, bytes, s), s);
+}
+
 }  // extern "C"

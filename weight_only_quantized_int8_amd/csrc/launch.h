@@ -79,10 +79,11 @@ hipError_t launch_gemm_smallm32(const WeightView &w, const uint16_t *X, uint16_t
 // when can_split), else 0.
 uint32_t gemm_smallm_slice_rows(const WeightView &w, uint32_t m, bool can_split);
 
-// Calibration streams (not part of the layer path): read `bytes` once, or
-// copy them; bytes a multiple of 1024.
+// Calibration streams (not part of the layer path): read `bytes` once, copy
+// them, or widen each to 16 bits (2 * bytes written); bytes a multiple of 1024.
 hipError_t launch_stream_read(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t stream);
 hipError_t launch_stream_copy(const void *src, void *dst, uint64_t bytes, hipStream_t stream);
+hipError_t launch_stream_expand(const void *src, void *dst, uint64_t bytes, hipStream_t stream);
 
 // ---- C-ABI internals shared by capi.cpp and noalloc.hip
 // Records the calling thread's last error message and returns code.

@@ -1,10 +1,16 @@
 // measure.hip -- calibration kernels for the bandwidth figures: a plain
-// streaming read and a plain streaming copy, built the way the layer kernels
+// streaming read, a plain streaming copy, and a streaming expand (every byte
+// widened to 16 bits: read n bytes, write 2n), built the way the layer kernels
 // stream their weights (contiguous 1 KiB items per wave, 16 bytes per lane,
 // bounded buffer loads, two blocks of loads in flight).  They give the
-// achievable HBM rate on this chip for a read-only and for a read-plus-write
-// stream, the ceilings that the gemv and the dequantize_to / quantize
-// figures are compared with.  Not part of the layer path.
+// achievable HBM rate on this chip for a read-only stream (the gemv's mix),
+// a read-plus-write stream and a one-read-two-writes stream (dequantize_to's
+// mix): the ceilings the layer kernels are compared with.  Not part of the
+// layer path.  Launch shapes and store kinds were swept on MI355X
+// (graph-timed): the read is flat in them (58.7 MB in 10.0-10.4 us); the
+// copy reaches 5.8 TB/s with non-temporal buffer stores at eight
+// workgroups per CU (5.0 with default stores at two, below hipMemcpy's 5.3);
+// the expand 4.7 TB/s with default stores (non-temporal ones: 3.9).
 #include "common.h"
 
 namespace int8w {
@@ -76,7 +82,7 @@ __global__ __launch_bounds__(kMThreads) void k_stream_copy(const uint8_t *__rest
   const uint32_t gw = blockIdx.x * (kMThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const WaveRange wr = wave_range(items, gridDim.x * (kMThreads / 64), gw);
   const auto rs = make_rsrc(src + wr.beg * 1024u, wr.n * 1024u);
-  uint8_t *out = dst + wr.beg * 1024u + ((threadIdx.x & 63u) << 4);
+  const auto rd = make_rsrc(dst + wr.beg * 1024u, wr.n * 1024u);
   const uint32_t vo = (threadIdx.x & 63u) << 4;
   u32x4 A[kMU], B[kMU];
   uint32_t i_item = 0, c_item = 0;
@@ -89,10 +95,70 @@ __global__ __launch_bounds__(kMThreads) void k_stream_copy(const uint8_t *__rest
       ++i_item;
     }
   };
+  // stores past the wave's range fall outside the bounded view: dropped
   auto consume = [&](const u32x4 *blk) {
 #pragma unroll
     for (int u = 0; u < kMU; ++u) {
-      if (c_item < wr.n) *reinterpret_cast<u32x4 *>(out + ((size_t)c_item << 10)) = blk[u];
+      const uint32_t so = __builtin_amdgcn_readfirstlane(c_item << 10);
+      __builtin_amdgcn_raw_buffer_store_b128(blk[u], rd, (int)(c_item < wr.n ? vo : kOutOfRange), (int)so,
+                                             kAuxNontemporal);
+      ++c_item;
+    }
+  };
+  const uint32_t nblk = (wr.n + kMU - 1) / kMU;
+  issue(A);
+  uint32_t b = 0;
+  for (; b + 2u < nblk; b += 2u) {
+    issue(B);
+    consume(A);
+    INT8W_M_VMCNT(kMU);
+    issue(A);
+    consume(B);
+    INT8W_M_VMCNT(kMU);
+  }
+  if (b + 1u < nblk) {
+    issue(B);
+    consume(A);
+    consume(B);
+  } else if (b < nblk) {
+    consume(A);
+  }
+}
+// dst[i] = src[i] as a 16-bit value (zero-extended), i < items * 1024
+__global__ __launch_bounds__(kMThreads) void k_stream_expand(const uint8_t *__restrict__ src,
+                                                             uint16_t *__restrict__ dst, uint64_t items) {
+  const uint32_t gw = blockIdx.x * (kMThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const WaveRange wr = wave_range(items, gridDim.x * (kMThreads / 64), gw);
+  const auto rs = make_rsrc(src + wr.beg * 1024u, wr.n * 1024u);
+  uint16_t *out = dst + wr.beg * 1024u + ((threadIdx.x & 63u) << 4);
+  const uint32_t vo = (threadIdx.x & 63u) << 4;
+  u32x4 A[kMU], B[kMU];
+  uint32_t i_item = 0, c_item = 0;
+  auto issue = [&](u32x4 *blk) {
+#pragma unroll
+    for (int u = 0; u < kMU; ++u) {
+      const uint32_t so = __builtin_amdgcn_readfirstlane(i_item << 10);
+      blk[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(i_item < wr.n ? vo : kOutOfRange), (int)so,
+                                                     kAuxNontemporal);
+      ++i_item;
+    }
+  };
+  // bytes 0, 1 (selector 0x0c010c00) or 2, 3 (0x0c030c02) of a word into the
+  // low halves of two 16-bit lanes, zeros above (selector byte 0x0c)
+  auto widen = [](uint32_t w, uint32_t sel) { return __builtin_amdgcn_perm(0u, w, sel); };
+  auto consume = [&](const u32x4 *blk) {
+#pragma unroll
+    for (int u = 0; u < kMU; ++u) {
+      if (c_item < wr.n) {
+        const u32x4 v = blk[u];
+        const u32x4 lo = {widen(v.x, 0x0c010c00u), widen(v.x, 0x0c030c02u), widen(v.y, 0x0c010c00u),
+                          widen(v.y, 0x0c030c02u)};
+        const u32x4 hi = {widen(v.z, 0x0c010c00u), widen(v.z, 0x0c030c02u), widen(v.w, 0x0c010c00u),
+                          widen(v.w, 0x0c030c02u)};
+        u32x4 *d = reinterpret_cast<u32x4 *>(out + ((size_t)c_item << 10));
+        d[0] = lo;
+        d[1] = hi;
+      }
       ++c_item;
     }
   };
@@ -121,18 +187,26 @@ __global__ __launch_bounds__(kMThreads) void k_stream_copy(const uint8_t *__rest
 
 int device_cu_count();
 
-// two 8-wave workgroups per CU, as the large gemv launches
+// 8-wave workgroups: four per CU for the read, eight for the copy and the
+// expand (each the fastest of 1, 2, 4 or 8 in the sweep above)
 hipError_t launch_stream_read(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t stream) {
-  const uint32_t blocks = 2u * (uint32_t)device_cu_count();
+  const uint32_t blocks = 4u * (uint32_t)device_cu_count();
   hipLaunchKernelGGL(k_stream_read, dim3(blocks), dim3(kMThreads), 0, stream, reinterpret_cast<const uint8_t *>(src),
                      bytes >> 10, sink);
   return hipGetLastError();
 }
 
 hipError_t launch_stream_copy(const void *src, void *dst, uint64_t bytes, hipStream_t stream) {
-  const uint32_t blocks = 2u * (uint32_t)device_cu_count();
+  const uint32_t blocks = 8u * (uint32_t)device_cu_count();
   hipLaunchKernelGGL(k_stream_copy, dim3(blocks), dim3(kMThreads), 0, stream, reinterpret_cast<const uint8_t *>(src),
                      reinterpret_cast<uint8_t *>(dst), bytes >> 10);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_expand(const void *src, void *dst, uint64_t bytes, hipStream_t stream) {
+  const uint32_t blocks = 8u * (uint32_t)device_cu_count();
+  hipLaunchKernelGGL(k_stream_expand, dim3(blocks), dim3(kMThreads), 0, stream,
+                     reinterpret_cast<const uint8_t *>(src), reinterpret_cast<uint16_t *>(dst), bytes >> 10);
   return hipGetLastError();
 }
 
