@@ -475,15 +475,16 @@ hipError_t launch_fp8_sf(const Fp8Cfg &c, const uint8_t *codes, const void *scal
                 : launch_fp8_cfg<SF, 8, 1, false>(c, codes, scale, single, bs_log2, x, y, N, K, stream);
 }
 
-// Launch shape, as for the int8 gemv: short rows (K <= 8192) 8-wave
-// workgroups, two per CU above 16384 rows and one per CU below; long rows
-// one 16-wave workgroup per CU with two rows side by side when every wave
-// owns at least two.
+// Launch shape, as for the int8 gemv: 8-wave workgroups; short rows (K <=
+// 8192) two per CU above 16384 rows and one per CU below; long rows two per
+// CU, one row at a time (4096 x 14336 with 128 x 128 BF16 block scales: 12.0
+// against 12.5 us with one 16-wave workgroup per CU; per-row scales 11.0
+// either way; graph-timed).
 Fp8Cfg choose_fp8_cfg(uint32_t N, uint32_t K, bool block, uint32_t bs_log2) {
   const uint32_t cus = (uint32_t)device_cu_count();
   Fp8Cfg c{};
-  c.waves = K <= 8192u ? 8 : 16;
-  const uint32_t per_cu = c.waves == 8 && N > 16384u ? 2u : 1u;
+  c.waves = 8;
+  const uint32_t per_cu = N > 16384u || K > 8192u ? 2u : 1u;
   const uint32_t W = (uint32_t)c.waves;
   c.blocks = per_cu * cus;
   const uint32_t need = (N + W - 1) / W;
@@ -492,7 +493,7 @@ Fp8Cfg choose_fp8_cfg(uint32_t N, uint32_t K, bool block, uint32_t bs_log2) {
   if (c.blocks < enough) c.blocks = enough;
   const uint32_t tw = c.blocks * W;
   c.max_rows = (N + tw - 1) / tw;
-  c.rp = c.waves == 16 && N / tw >= 2u ? 2 : 1;
+  c.rp = 1;
   const uint32_t cpr = K / 16u;
   const size_t budget = kFp8LdsPerCu / per_cu;
   for (uint32_t ntiles = (cpr + kFp8TileRunsMax - 1) / kFp8TileRunsMax;; ++ntiles) {
