@@ -825,22 +825,20 @@ uint32_t deal_waves(uint32_t tw, const uint32_t *n, uint32_t count, uint32_t *wa
   return max_rows;
 }
 
-// Launch shape (measured on MI355X): 8-wave workgroups; short rows (K <=
-// 8192) two per CU when the launch has more than 16384 rows and one per CU
-// otherwise (a small launch is latency-bound: fewer waves with two rows each
-// beat more waves with one); long rows two per CU, one row at a time.  For
-// long rows, against one 16-wave workgroup per CU (one activation tile for 16
-// waves): the gated 4096 x 14336 gs64 in 12.9 against 13.3 us, 8192 x 28672
-// gs128 in 41.8 against 42.3 us (two rows side by side: 16.2 / 42.8 us;
-// three or four workgroups per CU: 15.1 / 51-55 us), graph-timed.
+// Launch shape (measured on MI355X): short rows (K <= 8192) run 8-wave
+// workgroups, two per CU when the launch has more than 16384 rows and one
+// per CU otherwise (a small launch is latency-bound: fewer waves with two
+// rows each beat more waves with one); long rows one 16-wave workgroup per
+// CU, so one activation tile serves 16 waves, with two rows side by side
+// when every wave owns at least two.
 GemvCfg choose_cfg(const uint32_t *n, uint32_t count, uint32_t K, uint32_t gs, uint32_t *wave_end, int waves = 0,
                    int rp = 0, uint32_t wg_per_cu = 0) {
   const uint32_t cus = (uint32_t)device_cu_count();
   uint32_t N = 0;
   for (uint32_t i = 0; i < count; ++i) N += n[i];
   GemvCfg c{};
-  c.waves = waves ? waves : 8;
-  const uint32_t per_cu = wg_per_cu ? wg_per_cu : (N > 16384u || K > 8192u ? 2u : 1u);
+  c.waves = waves ? waves : (K <= 8192u ? 8 : 16);
+  const uint32_t per_cu = wg_per_cu ? wg_per_cu : (c.waves == 8 && N > 16384u ? 2u : 1u);
   const uint32_t W = (uint32_t)c.waves;
   c.blocks = per_cu * cus;
   const uint32_t need = (N + W - 1) / W;
@@ -853,7 +851,7 @@ GemvCfg choose_cfg(const uint32_t *n, uint32_t count, uint32_t K, uint32_t gs, u
   }
   const uint32_t tw = c.blocks * W;
   c.blocks = (wave_end[count - 1] + W - 1) / W;  // no workgroup of idle waves only
-  c.rp = rp ? rp : 1;
+  c.rp = rp ? rp : (c.waves == 16 && N / tw >= 2u ? 2 : 1);
   const uint32_t cpr = K / 16u;
   const size_t budget = kLdsPerCu / per_cu;
   for (uint32_t ntiles = (cpr + kTileRunsMax - 1) / kTileRunsMax;; ++ntiles) {
@@ -934,7 +932,7 @@ GemvCfg choose_moe_cfg(uint32_t N, uint32_t K, uint32_t gs, uint32_t slots) {
   const uint32_t cus = (uint32_t)device_cu_count();
   GemvCfg c{};
   c.waves = K <= 8192u ? 8 : 16;
-  const uint32_t per_cu = c.waves == 8 && (uint64_t)N * slots > 16384u ? 2u : 1u;
+  const uint32_t per_cu = c.waves == 8 && (uint64_t)N * slots > 16384u ? 2u : 1u;  // as choose_cfg
   const uint32_t W = (uint32_t)c.waves;
   uint32_t per_slot = (per_cu * cus + slots - 1) / slots;
   const uint32_t most = (N + W - 1) / W;                                  // no more waves than rows
