@@ -97,3 +97,37 @@ def test_noalloc_rejects_split_beyond_scratch():
     assert rc == B.INT8W_ERR_SHAPE
     assert b"scratch" in B.load_library().int8w_last_error()
     assert bool((Y.view(torch.int16) == -1).all()), "a rejected call must enqueue nothing"
+
+
+def test_noalloc_inside_a_hip_graph():
+    """The callers it is for: the call captured in a HIP graph (nothing is
+    allocated during capture), replayed three times with new X written
+    eagerly between the replays; every replay against int8_gemm_ws on the
+    same X, bit for bit."""
+    N, K, gs, m = 4096, 14336, 64, 512  # splits K over 4 parts: the scratch is used
+    w, rng = make_weight(7_300, N, K, gs)
+    W = upload(w)
+    assert 0 < B.int8_gemm_workspace_bytes(W.desc, m) <= B.NOALLOC_SCRATCH_BYTES
+    Xd = bits_to_dev(synth.gen_act(rng, (m, K)))
+    Y = _poisoned(m, N)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # one eager call on the capture stream first
+        assert B.int8_gemm_noalloc(W.desc, Xd.data_ptr(), Y.data_ptr(), m, s.cuda_stream) == 0
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rc = B.int8_gemm_noalloc(W.desc, Xd.data_ptr(), Y.data_ptr(), m, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, B.load_library().int8w_last_error()
+    for rep in range(3):
+        log(f"noalloc graph replay {rep}")
+        X = synth.gen_act(rng, (m, K))
+        Xd.copy_(bits_to_dev(X))  # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = dev_to_bits(Y)
+        exp = dev_to_bits(_run_ws(W, Xd, m))
+        torch.cuda.synchronize()
+        assert np.array_equal(got, exp), f"replay {rep}: {np.count_nonzero(got != exp)} outputs differ"
