@@ -131,3 +131,42 @@ def test_noalloc_inside_a_hip_graph():
         exp = dev_to_bits(_run_ws(W, Xd, m))
         torch.cuda.synchronize()
         assert np.array_equal(got, exp), f"replay {rep}: {np.count_nonzero(got != exp)} outputs differ"
+
+
+def test_int8weight_gemm_under_capture_takes_the_static_scratch():
+    """Int8Weight.gemm captured with no cached workspace large enough: it does
+    not allocate during capture (the static scratch serves the split), and
+    every replay equals the eager result."""
+    N, K, gs, m = 4096, 14336, 64, 600  # splits K over 2 parts
+    w, rng = make_weight(7_400, N, K, gs)
+    W = upload(w)
+    need = B.int8_gemm_workspace_bytes(W.desc, m)
+    assert 0 < need <= B.NOALLOC_SCRATCH_BYTES
+    saved = dict(B._workspaces)
+    B._workspaces.clear()  # no cached workspace: it would have to grow
+    try:
+        Xd = bits_to_dev(synth.gen_act(rng, (m, K)))
+        Y = _poisoned(m, N)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            torch.empty(1, device="cuda")  # warm the stream's allocator outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            W.gemm(Xd, Y)
+        assert not B._workspaces, "the workspace grew during capture"
+        for rep in range(2):
+            log(f"Int8Weight.gemm graph replay {rep}")
+            Xd.copy_(bits_to_dev(synth.gen_act(rng, (m, K))))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = dev_to_bits(Y)
+            exp = dev_to_bits(_run_ws(W, Xd, m))
+            torch.cuda.synchronize()
+            assert np.array_equal(got, exp), f"replay {rep}: {np.count_nonzero(got != exp)} outputs differ"
+    finally:
+        B._workspaces.clear()
+        B._workspaces.update(saved)

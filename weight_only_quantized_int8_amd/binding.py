@@ -341,7 +341,8 @@ class Int8Weight:
 
     def gemm(self, x: torch.Tensor, y: torch.Tensor | None = None, split_k: bool = True) -> torch.Tensor:
         """Y = X W^T.  With split_k (the default) a call whose grid has too few
-        tiles runs int8_gemm_ws on a cached per-device workspace; otherwise int8_gemm."""
+        tiles runs int8_gemm_ws on a cached per-device workspace (int8_gemm_noalloc
+        when that would have to grow during graph capture); otherwise int8_gemm."""
         if x.dim() != 2 or x.shape[1] != self.in_features:
             raise ValueError(f"X must be [m, {self.in_features}]")
         m = x.shape[0]
@@ -350,12 +351,16 @@ class Int8Weight:
             y = torch.empty((m, self.out_features), dtype=torch.bfloat16, device=self.device)
         _need_bf16(y, "Y", m * self.out_features, self.device)
         need = int8_gemm_workspace_bytes(self.desc, m) if split_k and m > 16 else 0
-        if need:
-            ws = _workspace(self.device, need)
-            _check(int8_gemm_ws(self.desc, x.data_ptr(), y.data_ptr(), m, ws.data_ptr(), ws.numel(),
-                                _stream_of(self.device)))
+        stream = _stream_of(self.device)
+        ws = _workspace(self.device, need) if need else None
+        if ws is not None:
+            _check(int8_gemm_ws(self.desc, x.data_ptr(), y.data_ptr(), m, ws.data_ptr(), ws.numel(), stream))
+        elif need and need <= NOALLOC_SCRATCH_BYTES:
+            # under graph capture, where the cached workspace may not grow: the
+            # library's static scratch, same kernels and bits
+            _check(int8_gemm_noalloc(self.desc, x.data_ptr(), y.data_ptr(), m, stream))
         else:
-            _check(int8_gemm(self.desc, x.data_ptr(), y.data_ptr(), m, _stream_of(self.device)))
+            _check(int8_gemm(self.desc, x.data_ptr(), y.data_ptr(), m, stream))
         return y
 
 
@@ -365,10 +370,15 @@ class Int8Weight:
 _workspaces: dict = {}
 
 
-def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+def _workspace(device: torch.device, nbytes: int):
+    """The device's cached workspace of at least nbytes, grown if needed; None
+    when it would have to grow while the current stream is being captured into
+    a graph (an allocation made then would come from the graph's pool)."""
     key = device.index if device.index is not None else torch.cuda.current_device()
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            return None
         ws = torch.empty(max(nbytes, 64 << 20), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
