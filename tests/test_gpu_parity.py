@@ -430,6 +430,9 @@ def test_gemm_prefill_full_size_all_rows(m, N, K):
     (257, 1024, 12288, 64),   # 8 parts; the second row tile holds one row
     (128, 4096, 14336, 64),   # the 8B down projection at m = 128: 7 parts
     (1000, 2048, 4096, 64),   # 4 parts
+    (200, 2048, 16384, 128),  # gs 128: blocks of 1024 codes
+    (129, 3000, 12288, 128),  # gs 128, ragged N, one row in the second row tile
+    (1000, 1536, 32768, 32),  # gs 32, 128 scale/bias blocks
 ])
 def test_gemm_split_k(m, N, K, gs):
     from weight_only_quantized_int8_amd import binding as B
