@@ -37,11 +37,9 @@
 //    barrier per step.  With one workgroup per CU the waves of the
 //    single-role design moved in lockstep between an MFMA phase and a
 //    dequantize-and-store phase; here the two phases overlap (measured +10 %
-//    at m = 2048, MFMA busy 30 % before).  k_gemm_prefill_dmx (the usual
+//    at m = 2048, MFMA busy 30 % before).  k_gemm_prefill_dma (the usual
 //    case, K % (8 gs) == 0) stages X and the scales/biases by DMA over three
-//    LDS stages, two steps ahead; k_gemm_prefill_dma does the same for the
-//    128 x 64 tile, one step ahead; k_gemm_prefill_ws (any K) loads through
-//    registers.
+//    LDS stages; k_gemm_prefill_ws (any K) loads through registers.
 #include <type_traits>
 
 #include "common.h"
@@ -414,10 +412,9 @@ struct SplitK {
   float *part;
 };
 
-// The DMA-staged prefill kernel (the 128 x 64 tile; the 256 x 128 tile is
-// k_gemm_prefill_dmx below): wave-specialised like k_gemm_prefill_ws, with
-// the operands staged by DMA (buffer_load_dwordx4 ... lds: memory straight
-// into LDS, no registers, no LDS stores).
+// The main prefill kernel: wave-specialised like k_gemm_prefill_ws, with the
+// operands staged by DMA (buffer_load_dwordx4 ... lds: memory straight into
+// LDS, no registers, no LDS stores).
 //  * LDS holds three K steps.  Between barriers k - 1 and k the producers
 //    request step k + 2's X tile into stage (k + 2) % 3 (it held step k - 1,
 //    whose readers passed barrier k - 1), dequantize step k + 1's weight tile
@@ -437,11 +434,10 @@ struct SplitK {
 //    bytes; gs / 8 steps), double-buffered in LDS: per step a producer reads
 //    one scale and one bias per row it dequantizes from LDS instead of
 //    issuing two 2-byte global loads.  Needs K % (8 gs) == 0.
-//  * Measured on MI355X with the 256 x 128 tile (graph-timed, uniform
-//    activations): one producer role per wave took m = 2048 on 14336 x 4096
-//    from 267 to 249 us and on 4096 x 14336 from 230 to 200 us (every
-//    producer issuing both kinds and waiting for all of its loads at each
-//    barrier before).
+//  * Measured on MI355X (graph-timed): m = 2048 on 14336 x 4096 in 249 us
+//    and on 4096 x 14336 in 200 us (1.2 PFLOP/s); one producer role per
+//    wave took them from 267 / 230 us (every producer issuing both kinds and
+//    waiting for all of its loads at each barrier).
 template <int BM, int BN, int WGM, int WGN, int NP>
 __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
@@ -797,342 +793,6 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
   }
 }
 
-// The 256 x 128 kernel with the MFMA waves staging their own X: each of the
-// four MFMA waves requests its 64 rows of X by DMA and waits for them itself,
-// since no other wave reads those rows, and four dequantizing waves (one per
-// SIMD, next to an MFMA wave) share the weight tile.  Wave 0 also requests
-// the scale/bias blocks.  An MFMA wave issues LDS-DMA loads only, so its
-// partial vmcnt counts those alone, in issue order.
-//  * Everything is staged two steps ahead, so the MFMA waves can read the
-//    next step while they multiply this one: in interval k (between barriers
-//    k - 1 and k) each MFMA wave requests step k + 2's X into stage (k + 2) % 3
-//    and the dequantizing waves store step k + 2's weight tile there (it held
-//    step k - 1, whose reads ended before barrier k - 1); the MFMA wave
-//    multiplies step k, waits for its X of step k + 1 halfway, and requests
-//    step k + 1's first operand fragments before barrier k (step k + 1's
-//    weights were published by barrier k - 1).
-//  * Within a step the operand fragments are read one at a time, three B
-//    fragments ahead of the four MFMAs that use each, and the next half
-//    step's four A fragments in the first four of those slots, so the LDS
-//    latency hides under the MFMAs instead of following each barrier.
-//  * Measured against the same tile with two DMA waves and two dequantizing
-//    waves, everything staged one step ahead and each step's operands read
-//    after its barrier (graph-timed, synthetic N(0,1) activations; same
-//    result bits): m = 2048 on 14336 x 4096 280 -> 258 us and on 4096 x 14336
-//    243 -> 226 us; m = 512 on 4096 x 14336 (K split in 4) 86 -> 78 us and on
-//    14336 x 4096 80 -> 74 us.  Cycle counters in the waves showed where the
-//    step went before: the dequantizing waves' scale/bias reads queued behind
-//    the burst of operand reads that followed each barrier (about 450 cycles
-//    of a 2000-cycle step), and the MFMA waves waited for those operands;
-//    now the dequantizing waves have about 900 cycles to spare per step and
-//    the MFMA waves wait about 100 at the barrier.
-//  * Each output sums the products of each K step in K order, half step 0
-//    then 1, as the other tiled kernels do; the split-K partials have the
-//    layout k_splitk_sum<256, 128, 4, 1> reads.
-template <int NQ>
-__global__ __launch_bounds__(64 * (4 + NQ)) void k_gemm_prefill_dmx(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ X, uint16_t *__restrict__ Y,
-    uint32_t N, uint32_t K, uint32_t m, uint32_t gs_log2, uint32_t mtiles, uint32_t nbig, uint32_t mt_half,
-    uint32_t nt_big, uint32_t nwork, SplitK sk) {
-  constexpr int BM = 256, BN = 128, kMma = 4, WTM = 64;
-  constexpr int TI = 4, TJ = 8;  // 16 x 16 MFMA tiles per wave: 64 x 128
-  constexpr int XJW = WTM / 8;   // X loads per MFMA wave and step (8 rows of 128 B each)
-  constexpr uint32_t kSbW = BN / 64;
-  constexpr int kSbPer = 2 * (int)kSbW;  // scale/bias loads per block
-  constexpr uint32_t kStage = (BM + BN) * BK * 2;
-  constexpr uint32_t kSbBytes = BN * 16u * 2u;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds_pf[];
-  auto stage = [&](uint32_t i) { return lds_pf + i * kStage; };
-  auto sbuf = [&](uint32_t i) { return lds_pf + 3u * kStage + i * kSbBytes; };
-  auto next3 = [](uint32_t i) { return i == 2u ? 0u : i + 1u; };
-  auto barrier = []() { asm volatile("s_barrier" ::: "memory"); };
-
-  uint32_t bid = blockIdx.x;
-  bool half;
-  uint32_t m0, n0, part = 0, tile = 0, kb = 0, kl = K;
-  if (sk.parts > 1u) {
-    if (nwork % kXcds == 0) bid = (bid % kXcds) * (nwork / kXcds) + bid / kXcds;
-    part = bid % sk.parts;
-    tile = bid / sk.parts;
-    half = false;
-    m0 = (tile % mtiles) * BM;
-    n0 = (tile / mtiles) * BN;
-    const uint32_t blo = part * sk.nblk / sk.parts, bhi = (part + 1u) * sk.nblk / sk.parts;
-    kb = blo << (gs_log2 + 3u);
-    kl = (bhi - blo) << (gs_log2 + 3u);
-  } else if (bid < nbig) {
-    if (nbig % kXcds == 0) bid = (bid % kXcds) * (nbig / kXcds) + bid / kXcds;
-    half = false;
-    m0 = (bid % mtiles) * BM;
-    n0 = (bid / mtiles) * BN;
-  } else {
-    uint32_t h = bid - nbig;
-    const uint32_t nh = nwork - nbig;
-    if (nh % kXcds == 0) h = (h % kXcds) * (nh / kXcds) + h / kXcds;
-    half = true;
-    m0 = (h % mt_half) * (BM / 2);
-    n0 = (nt_big + h / mt_half) * BN;
-  }
-  const uint32_t tile_rows = half ? (uint32_t)BM / 2u : (uint32_t)BM;
-  const uint32_t tid = threadIdx.x;
-  const uint32_t lane = tid & 63u, wave = uniform_pf(tid >> 6);
-  const uint32_t ksteps = kl / BK;  // kl is a whole number of scale/bias blocks
-  const uint32_t G = K >> gs_log2;
-  const uint32_t nrows = N - n0 < (uint32_t)BN ? N - n0 : (uint32_t)BN;
-  const uint32_t gb = kb >> gs_log2;
-  const uint32_t sbs_log2 = gs_log2 - 3u;  // steps per scale/bias block, log2
-  const uint32_t nblk = kl >> (gs_log2 + 3u);
-  // Steps 0 .. ksteps - 2 end with barriers 0 .. ksteps - 2; every wave also
-  // passes the two barriers of the prologue.
-  const uint32_t nst = ksteps - 1u;
-
-  if (wave >= (uint32_t)kMma) {
-    // ---------------- dequantizing waves: 16 codes per lane and pass, QWP
-    // passes of QWR rows per step; codes requested three steps ahead
-    constexpr int QWR = 64 * NQ / 4;
-    constexpr int QWP = BN / QWR;
-    static_assert(QWP >= 1 && BN % QWR == 0, "whole weight passes");
-    const uint32_t qtid = tid - 64u * (uint32_t)kMma;
-    const auto rw = make_rsrc(codes + (size_t)n0 * K + kb, nrows * K - kb);
-    const uint32_t wr = qtid >> 2, wp = qtid & 3u;
-    uint32_t vw[QWP];
-#pragma unroll
-    for (int p = 0; p < QWP; ++p) {
-      const uint32_t row = p * QWR + wr;
-      vw[p] = row < nrows ? row * K + wp * 16u : kOutOfRange;
-    }
-    struct Regs {
-      u32x4 w[QWP];
-    };
-    auto issue = [&](Regs &r, uint32_t ks) {
-      const bool live = ks < ksteps;
-#pragma unroll
-      for (int p = 0; p < QWP; ++p)
-        r.w[p] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(live ? vw[p] : kOutOfRange),
-                                                       (int)uniform_pf(live ? ks * BK : 0u), kAuxNontemporal);
-    };
-    auto store = [&](const Regs &r, uint32_t ks, uint8_t *buf) {
-      const uint8_t *sb = sbuf((ks >> sbs_log2) & 1u);
-      const uint32_t g = ((ks * BK + wp * 16u) >> gs_log2) & 7u;
-      float sc[QWP], bi[QWP];
-#pragma unroll
-      for (int p = 0; p < QWP; ++p) {
-        const uint32_t srow = p * QWR + wr;
-        sc[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + srow * 16u + 2u * g));
-        bi[p] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sb + BN * 16u + srow * 16u + 2u * g));
-      }
-      uint8_t *ws = buf + BM * BK * 2;
-#pragma unroll
-      for (int p = 0; p < QWP; ++p) {
-        const uint32_t word[4] = {r.w[p].x, r.w[p].y, r.w[p].z, r.w[p].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[2 * i] = pack_bf16x2(__builtin_fmaf(code_f32(word[i], 0), sc[p], bi[p]),
-                                 __builtin_fmaf(code_f32(word[i], 1), sc[p], bi[p]));
-          o[2 * i + 1] = pack_bf16x2(__builtin_fmaf(code_f32(word[i], 2), sc[p], bi[p]),
-                                     __builtin_fmaf(code_f32(word[i], 3), sc[p], bi[p]));
-        }
-        const uint32_t row = p * QWR + wr;
-        *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp)) = u32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<u32x4 *>(ws + swz(row, 2u * wp + 1u)) = u32x4{o[4], o[5], o[6], o[7]};
-      }
-    };
-    Regs R0, R1, R2;
-    issue(R0, 0u);
-    issue(R1, 1u);
-    issue(R2, 2u);
-    barrier();  // the scale/bias blocks 0 and 1 are in LDS
-    store(R0, 0u, stage(0u));
-    issue(R0, 3u);
-    store(R1, 1u, stage(1u));
-    issue(R1, 4u);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): steps 0 and 1 are stored
-    barrier();                           // steps 0 and 1 are in LDS
-    // interval k: step k + 2 into stage (k + 2) % 3 from codes requested three
-    // intervals earlier, step k + 5's codes requested into the same registers,
-    // barrier k publishes the stores (steps past the last one read zeros and
-    // are stored into a stage nobody reads)
-    auto step = [&](Regs &r, uint32_t k, uint32_t st) {
-      store(r, k + 2u, stage(st));
-      issue(r, k + 5u);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      barrier();
-    };
-    uint32_t k = 0;
-    for (; k + 3u <= nst; k += 3u) {
-      step(R2, k, 2u);
-      step(R0, k + 1u, 0u);
-      step(R1, k + 2u, 1u);
-    }
-    if (k < nst) {
-      step(R2, k, 2u);
-      if (k + 1u < nst) step(R0, k + 1u, 0u);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    return;
-  }
-
-  // ---------------- MFMA waves: wave wm owns rows 64 wm .. 64 wm + 63
-  const uint32_t wm = wave;
-  if (wm * (uint32_t)WTM >= tile_rows) {
-    // a half tile's lower rows: nothing to multiply or stage, but the
-    // barrier count is kept (wave 0 never gets here)
-    for (uint32_t k = 0; k < nst + 2u; ++k) barrier();
-    return;
-  }
-  const uint32_t mrows = m - m0 < tile_rows ? m - m0 : tile_rows;
-  const auto rx = make_rsrc(X + (size_t)m0 * K + kb, mrows * K * 2u - 2u * kb);
-  const uint32_t xchunk = (lane & 7u) ^ (lane >> 3);
-  // this wave's rows 64 wm + 8 j + lane / 8, chunk xchunk, of step ks into
-  // stage st (memory straight into LDS)
-  auto xdma = [&](uint32_t ks, uint32_t st) {
-    const bool live = ks < ksteps;
-    const uint32_t k0 = live ? ks * BK : 0u;
-#pragma unroll
-    for (int j = 0; j < XJW; ++j) {
-      const uint32_t row = wm * WTM + j * 8u + (lane >> 3);
-      const uint32_t off = live && row < mrows ? row * K * 2u + xchunk * 16u : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (__attribute__((address_space(3))) void *)(stage(st) + (wm * WTM + j * 8u) * (BK * 2)), 16, (int)off,
-          (int)uniform_pf(2u * k0), 0, 0);
-    }
-  };
-  const auto rs = make_rsrc(scales + (size_t)n0 * G + gb, nrows * G * 2u - 2u * gb);
-  const auto rb = make_rsrc(biases + (size_t)n0 * G + gb, nrows * G * 2u - 2u * gb);
-  auto sbdma = [&](uint32_t blk) {
-#pragma unroll
-    for (int c = 0; c < kSbPer; ++c) {
-      const uint32_t sbrow = (c % kSbW) * 64u + lane;
-      const uint32_t vsbd = sbrow < nrows ? sbrow * G * 2u : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          c >= (int)kSbW ? rb : rs,
-          (__attribute__((address_space(3))) void *)(sbuf(blk & 1u) + (c / kSbW) * (BN * 16u) + (c % kSbW) * 1024u),
-          16, (int)vsbd, (int)uniform_pf(blk * 16u), 0, 0);
-    }
-  };
-#define INT8W_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
-  static_assert(2 * XJW + kSbPer < 64, "vmcnt range");
-  if (wm == 0u) {
-    sbdma(0u);
-    if (1u < nblk) sbdma(1u);
-  }
-  xdma(0u, 0u);
-  xdma(1u, 1u);
-  INT8W_VMCNT(2 * XJW);  // wave 0: the scale/bias blocks 0 and 1 have landed
-  barrier();             // ... published for the dequantizing waves
-  INT8W_VMCNT(XJW);      // this wave's X of step 0 has landed
-  barrier();             // the weight tiles of steps 0 and 1 are in LDS
-
-  f32x4 acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint32_t lr = lane & 15u, lg = lane >> 4;
-  // A fragment i (this wave's rows 16 i ..) and B fragment j (weight rows
-  // 16 j ..) of half step kh of the step in stage buf
-  auto read_a = [&](bf16x8 &dst, const uint8_t *buf, uint32_t i, uint32_t kh) {
-    dst = *reinterpret_cast<const bf16x8 *>(buf + swz(wm * WTM + 16u * i + lr, 4u * kh + lg));
-  };
-  auto read_b = [&](bf16x8 &dst, const uint8_t *buf, uint32_t j, uint32_t kh) {
-    dst = *reinterpret_cast<const bf16x8 *>(buf + BM * BK * 2 + swz(16u * j + lr, 4u * kh + lg));
-  };
-  bf16x8 af[2][TI], bf[4];
-  // half step kh of the step in cur: B fragment j + 3 (or the next half
-  // step's fragment j - 5, from nxt when kh = 1) is requested before the
-  // MFMAs of fragment j, and the next half step's A fragment j for j < 4
-  auto halfstep = [&](auto khc, const uint8_t *cur, const uint8_t *nxt) {
-    constexpr int kh = decltype(khc)::value;
-    const uint8_t *nb = kh == 0 ? cur : nxt;
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      if (j + 3 < TJ)
-        read_b(bf[(j + 3) & 3], cur, j + 3, kh);
-      else
-        read_b(bf[(j + 3) & 3], nb, j + 3 - TJ, kh ^ 1);
-      if (j < TI) read_a(af[kh ^ 1][j], nb, j, kh ^ 1);
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kh][i], bf[j & 3], acc[i][j], 0, 0, 0);
-    }
-  };
-  // the order the scheduler keeps (left to itself it read each fragment
-  // just before its MFMAs)
-  auto pin_order = [] {
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      if (j < TI)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads: B fragment, A fragment
-      else
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read: B fragment
-      __builtin_amdgcn_sched_group_barrier(0x008, TI, 0);   // MFMAs
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < TI; ++i) read_a(af[0][i], stage(0u), i, 0u);
-#pragma unroll
-  for (int j = 0; j < 3; ++j) read_b(bf[j], stage(0u), j, 0u);
-  // interval k: step k + 2's X requested, step k multiplied (step k + 1's X
-  // awaited between its halves: only step k + 2's, and for wave 0 a
-  // scale/bias block, may still be in flight), step k + 1's first fragments
-  // requested; barrier k: this wave's reads of stage k % 3 are done
-  // (lgkmcnt(3): only step k + 1's B fragments 0 .. 2 may be in flight; its A
-  // fragments were requested before B fragment 7 of step k)
-  uint32_t s = 0;
-  for (uint32_t k = 0;; ++k) {
-    const uint8_t *cur = stage(s);
-    s = next3(s);
-    const uint8_t *nxt = stage(s);
-    xdma(k + 2u, next3(s));
-    halfstep(std::integral_constant<int, 0>{}, cur, nxt);
-    pin_order();
-    // vmcnt(XJW) as a memory barrier for the compiler: the reads of step
-    // k + 1's X below must stay after it
-    static_assert(XJW == 8, "the wait below counts 8 loads");
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    halfstep(std::integral_constant<int, 1>{}, cur, nxt);
-    pin_order();
-    if (k + 1u >= ksteps) break;
-    if (wm == 0u) {
-      // the block after the one step k + 2 opens, into the buffer of the
-      // block before it (its last step was stored in interval k - 1)
-      const uint32_t n2 = k + 2u;
-      if ((n2 & ((1u << sbs_log2) - 1u)) == 0u && (n2 >> sbs_log2) + 1u < nblk) sbdma((n2 >> sbs_log2) + 1u);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC37F);  // lgkmcnt(3)
-    barrier();
-  }
-#undef INT8W_VMCNT
-  // the X requested past the last step (zeros into LDS): an LDS-DMA write
-  // still in flight when the workgroup ends would land in the LDS of the next
-  // workgroup on the CU
-  __builtin_amdgcn_s_waitcnt(0);
-  if (sk.parts > 1u) {
-    constexpr uint32_t kVals = TI * TJ;  // float4s per lane
-    float *mine = sk.part + (((size_t)part * sk.ntiles + tile) * kMma + wave) * kVals * 256u + lane * 4u;
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) *reinterpret_cast<f32x4 *>(mine + (i * TJ + j) * 256u) = acc[i][j];
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const uint32_t n = n0 + 16u * j + lr;
-      if (n >= N) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t row = m0 + wm * WTM + 16u * i + 4u * lg + r;
-        if (row < m) Y[(size_t)row * N + n] = to_bf16_bits(acc[i][j][r]);
-      }
-    }
-  }
-}
-
 // The sum of a split launch's parts: thread t adds float4 t of every part
 // (part[0] + part[1] + ... in that order), rounds to BF16 and writes the
 // four outputs it holds (rows 4 lg .. 4 lg + 3 of a 16 x 16 MFMA tile, one
@@ -1167,19 +827,10 @@ uint64_t split_bytes(uint32_t tiles, uint32_t parts) {
   return (uint64_t)parts * tiles * (WGM * WGN) * kSub;
 }
 
-// XQ > 0: k_gemm_prefill_dmx<XQ> (256 x 128 only) in place of
-// k_gemm_prefill_dma: the same work items, LDS size and split-K partials.
-template <int BM, int BN, int WGM, int WGN, int NP, int XQ = 0>
+template <int BM, int BN, int WGM, int WGN, int NP>
 hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream,
                            uint32_t parts = 1, void *ws = nullptr) {
-  static_assert(XQ == 0 || (BM == 256 && BN == 128 && WGM == 4 && WGN == 1), "256 x 128 only");
-  const auto kern = [] {
-    if constexpr (XQ > 0)
-      return k_gemm_prefill_dmx<XQ>;
-    else
-      return k_gemm_prefill_dma<BM, BN, WGM, WGN, NP>;
-  }();
-  constexpr uint32_t kThreads = XQ > 0 ? 64u * (4u + XQ) : 64u * (WGM * WGN + NP);
+  auto kern = k_gemm_prefill_dma<BM, BN, WGM, WGN, NP>;
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -1196,7 +847,7 @@ hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, 
     if (ws == nullptr) return hipErrorInvalidValue;
     SplitK sk{parts, w.K >> (gs_log2 + 3u), tiles, static_cast<float *>(ws)};
     const uint32_t nwork = tiles * parts;
-    hipLaunchKernelGGL(kern, dim3(nwork), dim3(kThreads), lds, stream,
+    hipLaunchKernelGGL(kern, dim3(nwork), dim3(64 * (WGM * WGN + NP)), lds, stream,
                        reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m, gs_log2,
                        mtiles, 0u, 0u, 0u, nwork, sk);
     hipError_t e = hipGetLastError();
@@ -1224,7 +875,7 @@ hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, 
   const uint32_t nbig = mtiles * nt_big;
   const uint32_t nwork = nbig + mt_half * nt_half;
   const SplitK none{1u, 0u, 0u, nullptr};
-  hipLaunchKernelGGL(kern, dim3(nwork), dim3(kThreads), lds, stream,
+  hipLaunchKernelGGL(kern, dim3(nwork), dim3(64 * (WGM * WGN + NP)), lds, stream,
                      reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m, gs_log2,
                      mtiles, nbig, mt_half, nt_big, nwork, none);
   return hipGetLastError();
@@ -1273,9 +924,9 @@ hipError_t launch_tile(const WeightView &w, const uint16_t *X, uint16_t *Y, uint
 
 // Tile shapes (BM x BN, waves): 0 = 128 x 128 (2 x 2), 1 = 128 x 64 (2 x 2),
 // 2 = 256 x 128 (4 x 2 MFMA waves + 8 producer waves), 3 = 256 x 128 staged
-// by DMA (4 x 1 MFMA waves of 64 x 128 staging their own X + 4 dequantizing
-// waves; K % (8 gs) == 0), 4 = 128 x 64 staged by DMA (2 x 2 MFMA waves + 4
-// producer waves; K % (8 gs) == 0).
+// by DMA (4 x 1 MFMA waves of 64 x 128 + 4 producer waves; K % (8 gs) == 0),
+// 4 = 128 x 64 staged by DMA (2 x 2 MFMA waves + 4 producer waves;
+// K % (8 gs) == 0).
 hipError_t launch_gemm_prefill_tile(int t, const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
                                     hipStream_t stream) {
   switch (t) {
@@ -1283,7 +934,7 @@ hipError_t launch_gemm_prefill_tile(int t, const WeightView &w, const uint16_t *
     case 2: return launch_tile_ws<256, 128, 4, 2, 8>(w, X, Y, m, stream);
     case 3:
       if (w.K % (8u * w.gs) != 0u) return hipErrorInvalidValue;
-      return launch_tile_dma<256, 128, 4, 1, 4, 4>(w, X, Y, m, stream);
+      return launch_tile_dma<256, 128, 4, 1, 4>(w, X, Y, m, stream);
     case 4:
       if (w.K % (8u * w.gs) != 0u) return hipErrorInvalidValue;
       return launch_tile_dma<128, 64, 2, 2, 4>(w, X, Y, m, stream);
@@ -1350,7 +1001,7 @@ uint64_t gemm_prefill_workspace_bytes(const WeightView &w, uint32_t m) {
 hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, void *ws,
                                hipStream_t stream) {
   const PrefillPick pick = prefill_pick(w, m, (uint32_t)device_cu_count(), ws != nullptr);
-  if (pick.parts > 1u) return launch_tile_dma<256, 128, 4, 1, 4, 4>(w, X, Y, m, stream, pick.parts, ws);
+  if (pick.parts > 1u) return launch_tile_dma<256, 128, 4, 1, 4>(w, X, Y, m, stream, pick.parts, ws);
   return launch_gemm_prefill_tile(pick.shape, w, X, Y, m, stream);
 }
 
