@@ -537,13 +537,26 @@ def secondary(dev, quick):
                     res[f"gemm_m{m}_{N}x{K}_gs64"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
                                                       "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
                                                       "TFLOP/s": 2.0 * m * N * K / t / 1e12}
+                # the library's dense BF16 GEMM (torch.matmul, hipBLASLt) on the
+                # same activations and the dequantized weight: a practical
+                # ceiling for the matrix cores under this load, measured
+                # beside the fused kernel (it reads 2 bytes per weight and
+                # does no dequantization)
+                wdq = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+                for j in range(2):
+                    ws[j].dequantize_to(wdq[j])
                 for m in (512, 2048):
                     X = bits_dev(synth.gen_act(rng, (m, K)), dev)
                     Y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
                     t = time_batches(lambda i: ws[i % len(ws)].gemm(X, Y), 10)
+                    tl = time_batches(lambda i: torch.matmul(X, wdq[i % 2].t(), out=Y), 10)
                     fl = 2.0 * m * N * K
                     res[f"gemm_m{m}_{N}x{K}_gs64"] = {"us": t * 1e6, "TFLOP/s": fl / t / 1e12,
-                                                      "frac_mfma_bf16": fl / t / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+                                                      "frac_mfma_bf16": fl / t / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                                                      "library_bf16_us": tl * 1e6,
+                                                      "library_bf16_TFLOP/s": fl / tl / 1e12,
+                                                      "frac_of_library_bf16": tl / t}
+                del wdq
             del ws
             torch.cuda.empty_cache()
     # a weight whose one round of 256 x 128 tiles walks all of K: m = 32 goes
