@@ -310,6 +310,32 @@ def test_gemm_small_m_ragged(m, N, K, gs):
 
 
 @pytest.mark.parametrize("m,N,K,gs", [
+    (2, 777, 1024, 32), (3, 777, 1024, 128), (4, 777, 1024, 64),
+    (2, 777, 3072, 128), (3, 777, 3072, 32), (4, 777, 3072, 32),
+    (2, 1000, 2048, 64), (3, 333, 4096, 64), (4, 513, 4096, 128),
+    (2, 5, 4096, 64),        # fewer rows than the workgroup has waves
+    (3, 28672, 2048, 32),    # 14 rows per wave
+    (4, 8192, 2048, 64),     # the largest weight that takes this form at m = 4
+    (4, 8200, 2048, 64),     # one above: the small-m kernel
+    (2, 6144, 4096, 128),
+])
+def test_gemm_few_rows_register_form(m, N, K, gs):
+    """m = 2..4 on in_features 1024..4096: every code converted once to BF16
+    and multiplied into each row with v_dot2c_f32_bf16; repeated calls give
+    the same bits."""
+    log(f"gemm few rows m={m} N={N} K={K} gs={gs}")
+    w, rng = make_weight(2700 + m + N + K + gs, N, K, gs)
+    X = synth.gen_act(rng, (m, K))
+    W = upload(w)
+    Xd = bits_to_dev(X)
+    Y = dev_to_bits(W.gemm(Xd))
+    Y2 = dev_to_bits(W.gemm(Xd))
+    Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
+    assert_close(Y, Y_ref, A, f"gemm m={m} {N}x{K} gs{gs}")
+    assert np.array_equal(Y, Y2), "repeated call differs"
+
+
+@pytest.mark.parametrize("m,N,K,gs", [
     (17, 200, 512, 64),
     (64, 128, 256, 64),
     (129, 130, 96, 32),

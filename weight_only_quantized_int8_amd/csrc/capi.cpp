@@ -357,10 +357,14 @@ int gemm_common(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t 
   // 16 < m <= 128 on a small grid: passes of the small-m kernel over slices of
   // 32 (or 16) rows
   const bool sm_ok = smallm_supported(w->in_features, w->group_size);
+  // 2 or 3 rows (4 on weights of at most 8192 rows) on in_features 1024..4096:
+  // the register-resident gemv form with several rows, measured faster there
+  // than the small-m kernel (14336 x 4096, m = 2: 12.8 against 15.0 us)
+  const bool rows = gemv_rows_supported(w->in_features, m) && (m <= 3u || N <= 8192u);
   const uint32_t slice = m > 16u ? gemm_smallm_slice_rows(view(w), m, ws != nullptr) : 0u;
   const bool passes = slice != 0u;
   // the tiled kernel addresses a 256-row X tile with 32-bit byte offsets
-  const bool tiled = !passes && (m > 16u || (m > 1u && !sm_ok));
+  const bool tiled = !passes && !rows && (m > 16u || (m > 1u && !sm_ok));
   if (tiled && K * 2u * 256u > 0xFFFFFFFFull)
     return fail(INT8W_ERR_SHAPE, "in_features=%u above 2^23 - 1 needs m = 1 or a small-m shape (m=%u)",
                 w->in_features, m);
@@ -388,6 +392,8 @@ int gemm_common(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t 
   hipError_t e;
   if (m == 1) {
     e = launch_gemv(view(w), kEpiNone, x, nullptr, nullptr, y, s);
+  } else if (rows) {
+    e = launch_gemv_rows(view(w), x, y, m, s);
   } else if (m <= 16 && sm_ok) {
     e = launch_gemm_smallm(view(w), x, y, m, s);
   } else if (passes) {

@@ -483,6 +483,145 @@ __device__ __forceinline__ void gemv_wave_rx(const uint8_t *__restrict__ codes, 
   }
 }
 
+// MR = 2..4 rows of X (gemm with a few rows) on the register-resident
+// shapes: the m = 1 form above, with each run of 16 codes converted once to
+// BF16 pairs (exact: a code has at most 8 significant bits) and multiplied
+// into every row's activations, which the lane holds as the BF16 pairs it
+// loaded, by v_dot2c_f32_bf16 (two exact products per operation).  The affine
+// terms factor out of the run as in gemv_wave: s * sum q x + b * sum x, per
+// row.  Per code: 1.5 operations to convert, 0.5 per row to multiply.
+template <int NS, int MR>
+__device__ __forceinline__ void gemv_wave_rxm(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+                                              const uint16_t *__restrict__ biases, uint16_t *Y, uint32_t N,
+                                              uint32_t lw, uint32_t TW, const uint16_t *__restrict__ X,
+                                              uint32_t gs_log2) {
+  constexpr uint32_t K = NS * 1024u;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t rq = N / TW, rr = N % TW;
+  const uint32_t rbeg = lw * rq + (lw < rr ? lw : rr);
+  const uint32_t nr = lw < TW ? rq + (lw < rr ? 1u : 0u) : 0u;
+  const uint32_t G = K >> gs_log2;
+  const uint32_t seg_sb = (1024u >> gs_log2) << 1;      // scale bytes per segment
+  const auto rw = make_rsrc(codes + (size_t)rbeg * K, nr * K);
+  const auto rx = make_rsrc(X, MR * K * 2u);
+  const auto rsc = make_rsrc(scales + (size_t)rbeg * G, nr * G * 2u);
+  const auto rbi = make_rsrc(biases + (size_t)rbeg * G, nr * G * 2u);
+  const uint32_t vo_w = lane << 4;
+  const uint32_t v_sg = ((lane << 4) >> gs_log2) << 1;  // the lane's group in a segment, bytes
+
+  struct RowBlock {
+    u32x4 q[NS];
+    uint16_t s[NS], b[NS];  // BF16 bits of the lane's group scale and bias
+  };
+  // the activation loads go out first: waiting for them never waits for codes
+  u32x4 xw[MR][NS][2];
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      xw[r][u][0] = buf_load_b128(rx, r * (K * 2u) + (u << 11) + (lane << 5));
+      xw[r][u][1] = buf_load_b128(rx, r * (K * 2u) + (u << 11) + (lane << 5) + 16u);
+    }
+  uint32_t i_row = 0;
+  auto issue = [&](RowBlock &blk) {
+    // past the wave's rows a block re-reads its last row
+    const uint32_t row = i_row < nr ? i_row : (nr ? nr - 1u : 0u);
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const uint32_t sw = uniform(row * K + (u << 10));
+      const uint32_t ss = uniform(row * G * 2u + u * seg_sb);
+      blk.q[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vo_w, (int)sw, kAuxNontemporal);
+      blk.s[u] = __builtin_amdgcn_raw_buffer_load_b16(rsc, (int)v_sg, (int)ss, 0);
+      blk.b[u] = __builtin_amdgcn_raw_buffer_load_b16(rbi, (int)v_sg, (int)ss, 0);
+    }
+    ++i_row;
+  };
+  RowBlock A, B;
+  issue(A);
+  float S[MR][NS];  // the sum of the lane's 16 activations of each row and segment
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const uint32_t wv[8] = {xw[r][u][0].x, xw[r][u][0].y, xw[r][u][0].z, xw[r][u][0].w,
+                              xw[r][u][1].x, xw[r][u][1].y, xw[r][u][1].z, xw[r][u][1].w};
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sum += bf16_lo(wv[i]);
+        sum += bf16_hi(wv[i]);
+      }
+      S[r][u] = sum;
+    }
+  uint32_t c_row = 0;
+  auto consume = [&](const RowBlock &blk) {
+    float acc[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const float sc = bf16_bits_to_f32(blk.s[u]);
+      const float bi = bf16_bits_to_f32(blk.b[u]);
+      // codes 2i, 2i + 1 of the run as a BF16 pair (the fp32 value of a code
+      // has zero low halves, so its high half is the BF16 value)
+      const uint32_t words[4] = {blk.q[u].x, blk.q[u].y, blk.q[u].z, blk.q[u].w};
+      uint32_t cb[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t f0 = __builtin_bit_cast(uint32_t, code_f32(words[j], 0));
+        const uint32_t f1 = __builtin_bit_cast(uint32_t, code_f32(words[j], 1));
+        const uint32_t f2 = __builtin_bit_cast(uint32_t, code_f32(words[j], 2));
+        const uint32_t f3 = __builtin_bit_cast(uint32_t, code_f32(words[j], 3));
+        cb[2 * j] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+        cb[2 * j + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+      }
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        const uint32_t xv[8] = {xw[r][u][0].x, xw[r][u][0].y, xw[r][u][0].z, xw[r][u][0].w,
+                                xw[r][u][1].x, xw[r][u][1].y, xw[r][u][1].z, xw[r][u][1].w};
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cb[i]), __builtin_bit_cast(bf16x2, xv[i]), p,
+                                              false);
+        acc[r] = __builtin_fmaf(sc, p, __builtin_fmaf(bi, S[r][u], acc[r]));
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      const float tot = wave_sum_lane63(acc[r]);
+      if (lane == 63u) Y[(size_t)r * N + rbeg + c_row] = to_bf16_bits(tot);
+    }
+    ++c_row;
+  };
+  // the same two-stage pipeline as gemv_wave_rx
+  uint32_t b = 0;
+  for (; b + 2u < nr; b += 2u) {
+    issue(B);
+    consume(A);
+    issue(A);
+    consume(B);
+  }
+  if (b + 1u < nr) {
+    issue(B);
+    consume(A);
+    consume(B);
+  } else if (b < nr) {
+    consume(A);
+  }
+}
+
+// gemm for m = MR rows on the register-resident shapes: one 8-wave workgroup
+// per CU (the activations of four rows take up to 128 registers a lane).
+template <int NS, int MR>
+__global__ __launch_bounds__(512) void k_gemv_rows(const uint8_t *__restrict__ codes,
+                                                    const uint16_t *__restrict__ scales,
+                                                    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ X,
+                                                    uint16_t *Y, uint32_t N, uint32_t gs_log2) {
+  const uint32_t gw = blockIdx.x * 8u + uniform(threadIdx.x >> 6);
+  gemv_wave_rxm<NS, MR>(codes, scales, biases, Y, N, gw, gridDim.x * 8u, X, gs_log2);
+}
+
 // The wave body of a launch: the register-resident form (NS > 0) or the
 // LDS-tiled one (NS == 0).
 template <int NS, int EPI, int W, int RP, int U, bool TAIL>
@@ -959,6 +1098,44 @@ hipError_t launch_gemv(const WeightView &w, GemvEpilogue epi, const uint16_t *x_
                        const uint16_t *up, const uint16_t *x_resid, uint16_t *y,
                        hipStream_t stream) {
   return launch_gemv_list(&w, &y, 1, epi, x_or_gate, up, x_resid, stream);
+}
+
+bool gemv_rows_supported(uint32_t K, uint32_t m) {
+  return m >= 2u && m <= 4u && K % 1024u == 0 && K >= 1024u && K <= 4096u;
+}
+
+namespace {
+
+template <int NS, int MR>
+void launch_rows_cfg(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemv_rows<NS, MR>), dim3(blocks), dim3(512), 0, stream,
+                     reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N,
+                     (uint32_t)__builtin_ctz(w.gs));
+}
+
+template <int MR>
+void launch_rows_ns(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t blocks, hipStream_t stream) {
+  switch (w.K / 1024u) {
+    case 1: launch_rows_cfg<1, MR>(w, X, Y, blocks, stream); break;
+    case 2: launch_rows_cfg<2, MR>(w, X, Y, blocks, stream); break;
+    case 3: launch_rows_cfg<3, MR>(w, X, Y, blocks, stream); break;
+    default: launch_rows_cfg<4, MR>(w, X, Y, blocks, stream); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_rows(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream) {
+  if (!gemv_rows_supported(w.K, m)) return hipErrorInvalidValue;
+  uint32_t blocks = (uint32_t)device_cu_count();
+  const uint32_t need = (w.N + 7u) / 8u;  // no workgroup without rows
+  if (blocks > need) blocks = need;
+  switch (m) {
+    case 2: launch_rows_ns<2>(w, X, Y, blocks, stream); break;
+    case 3: launch_rows_ns<3>(w, X, Y, blocks, stream); break;
+    default: launch_rows_ns<4>(w, X, Y, blocks, stream); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_multi(const WeightView *w, uint16_t *const *y, uint32_t count, const uint16_t *x,

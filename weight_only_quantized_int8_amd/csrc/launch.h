@@ -25,6 +25,10 @@ hipError_t launch_dequant(const WeightView &w, uint16_t *out, hipStream_t stream
 enum GemvEpilogue { kEpiNone = 0, kEpiSiluGate = 1, kEpiSiluGateResid = 2 };
 
 // y = W a, with a = x (kEpiNone) or silu(gate)*up; plus x_resid for kEpiSiluGateResid.
+// gemm with 2 <= m <= 4 rows of X on in_features 1024..4096 (a multiple of
+// 1024): the register-resident gemv with several rows (gemv.hip).
+bool gemv_rows_supported(uint32_t K, uint32_t m);
+hipError_t launch_gemv_rows(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream);
 hipError_t launch_gemv(const WeightView &w, GemvEpilogue epi, const uint16_t *x_or_gate,
                        const uint16_t *up, const uint16_t *x_resid, uint16_t *y, hipStream_t stream);
 
