@@ -450,7 +450,7 @@ def test_gemm_prefill_full_size_all_rows(m, N, K):
 # cases run back to back on one workspace, so stale partials of an earlier
 # shape would show.
 @pytest.mark.parametrize("m,N,K,gs", [
-    (90, 1500, 16384, 64),    # 8 parts of 4 scale/bias blocks, ragged rows and columns
+    (150, 1500, 16384, 64),   # 8 parts of 4 scale/bias blocks, ragged rows and columns
     (300, 2000, 8192, 32),    # 8 parts of 4 blocks
     (600, 3000, 16384, 64),   # 7 parts of 4 or 5 blocks
     (257, 1024, 12288, 64),   # 8 parts; the second row tile holds one row
@@ -480,6 +480,39 @@ def test_gemm_split_k(m, N, K, gs):
     assert B.int8_gemm(W.desc, Xd.data_ptr(), Y3.data_ptr(), m, torch.cuda.current_stream().cuda_stream) == 0
     _sync()
     assert_close(dev_to_bits(Y3), Y_ref, A, f"unsplit gemm m={m} {N}x{K} gs{gs}")
+
+
+# Grids of 256 x 128 tiles a few tiles past a whole round over the CUs: only
+# the last tiles have K split (the tail), the whole rounds' tiles write Y
+# directly; sampled rows over every column (the split tiles are the last
+# column tiles), a repeat call bit-identical, and the unsplit int8_gemm within
+# the same bound.
+@pytest.mark.parametrize("m,N,K,gs", [
+    (300, 16640, 4096, 64),    # 260 tiles: 4 split in 4 parts
+    (520, 11008, 2048, 32),    # 258 tiles, ragged rows: 2 split in 4 parts
+    (256, 32946, 4096, 128),   # 258 tiles, the last column tile 50 wide: 2 split in 2 parts
+])
+def test_gemm_split_k_tail(m, N, K, gs):
+    from weight_only_quantized_int8_amd import binding as B
+    log(f"gemm tail split m={m} N={N} K={K} gs={gs}")
+    w, rng = make_weight(3_900 + m + N + K, N, K, gs)
+    X = synth.gen_act(rng, (m, K))
+    W = upload(w)
+    tiles = -(-m // 256) * -(-N // 128)
+    need = B.int8_gemm_workspace_bytes(W.desc, m)
+    assert 0 < need < tiles * 2 * 256 * 128 * 4, f"expected a split of the last tiles only ({need} bytes)"
+    Xd = bits_to_dev(X)
+    got = dev_to_bits(W.gemm(Xd))
+    rows = np.unique(np.concatenate([[0, 1, 127, 255, m - 1], np.arange(256, m, 37),
+                                     np.random.default_rng(m + N).choice(m, 12, replace=False)]))
+    rows = rows[rows < m]
+    Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X[rows])
+    assert_close(got[rows], Y_ref, A, f"tail split gemm m={m} {N}x{K} gs{gs}")
+    assert np.array_equal(dev_to_bits(W.gemm(Xd)), got)
+    Y3 = torch.empty((m, N), dtype=torch.bfloat16, device="cuda")
+    assert B.int8_gemm(W.desc, Xd.data_ptr(), Y3.data_ptr(), m, torch.cuda.current_stream().cuda_stream) == 0
+    _sync()
+    assert_close(dev_to_bits(Y3)[rows], Y_ref, A, f"unsplit gemm m={m} {N}x{K} gs{gs}")
 
 
 def test_gemm_m1_is_gemv_bit_exact():

@@ -81,8 +81,8 @@ def test_noalloc_unsplit_matches_int8_gemm(m, N, K, gs):
 
 
 def test_noalloc_rejects_split_beyond_scratch():
-    # 28672 x 28672 at m = 256 splits over 224 MiB of partials
-    N, K, gs, m = 28672, 28672, 64, 256
+    # 4096 x 14336 gs32 at m = 768: 96 tiles split 8 ways, 96 MiB of partials
+    N, K, gs, m = 4096, 14336, 32, 768
     packed = torch.empty(N * K // 4, dtype=torch.int32, device="cuda")
     scales = torch.empty(N * (K // gs), dtype=torch.int16, device="cuda")
     biases = torch.empty(N * (K // gs), dtype=torch.int16, device="cuda")
@@ -137,7 +137,7 @@ def test_int8weight_gemm_under_capture_takes_the_static_scratch():
     """Int8Weight.gemm captured with no cached workspace large enough: it does
     not allocate during capture (the static scratch serves the split), and
     every replay equals the eager result."""
-    N, K, gs, m = 4096, 14336, 64, 600  # splits K over 2 parts
+    N, K, gs, m = 4096, 14336, 64, 600  # splits K over 5 parts
     w, rng = make_weight(7_400, N, K, gs)
     W = upload(w)
     need = B.int8_gemm_workspace_bytes(W.desc, m)

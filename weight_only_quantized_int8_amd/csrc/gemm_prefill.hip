@@ -404,12 +404,15 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_ws(
 // per store instruction); k_splitk_sum, launched next on the same stream,
 // adds the parts in the order 0 .. parts - 1 and writes the BF16 outputs.  The
 // kernel boundary orders the two: no atomics, no flags, deterministic sums.
-// parts == 1: no split, no workspace.
+// parts == 1: no split, no workspace.  The split may cover only the tiles
+// from tile0 on (the last, partial round of a grid): the work items before
+// them (nbig) are whole tiles that write Y directly.
 struct SplitK {
   uint32_t parts;
   uint32_t nblk;
-  uint32_t ntiles;
+  uint32_t ntiles;  // split tiles
   float *part;
+  uint32_t tile0;   // first split tile
 };
 
 // The main prefill kernel: wave-specialised like k_gemm_prefill_ws, with the
@@ -460,19 +463,24 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
   // so that a grid of 3.5 rounds of full tiles ends in one round of half tiles
   // instead of half a round of full ones.  Within each kind, consecutive
   // items (the M tiles of one N tile) stay on one XCD.
-  // With a split of K (sk.parts > 1) the items are (tile, part) pairs, the
-  // parts of a tile consecutive, and there are no half tiles; the item's K
-  // range is kb .. kb + kl - 1, a whole number of scale/bias blocks.
+  // With a split of K (sk.parts > 1) the items from nbig on are (tile, part)
+  // pairs over the tiles from sk.tile0 on, the parts of a tile consecutive,
+  // and there are no half tiles; the item's K range is kb .. kb + kl - 1, a
+  // whole number of scale/bias blocks.
   uint32_t bid = blockIdx.x;
-  bool half;
+  bool half, split = false;
   uint32_t m0, n0, part = 0, tile = 0, kb = 0, kl = K;
-  if (sk.parts > 1u) {
-    if (nwork % kXcds == 0) bid = (bid % kXcds) * (nwork / kXcds) + bid / kXcds;
-    part = bid % sk.parts;
-    tile = bid / sk.parts;
+  if (sk.parts > 1u && bid >= nbig) {
+    uint32_t h = bid - nbig;
+    const uint32_t nh = nwork - nbig;
+    if (nh % kXcds == 0) h = (h % kXcds) * (nh / kXcds) + h / kXcds;
+    part = h % sk.parts;
+    tile = h / sk.parts;
     half = false;
-    m0 = (tile % mtiles) * BM;
-    n0 = (tile / mtiles) * BN;
+    split = true;
+    const uint32_t gt = sk.tile0 + tile;
+    m0 = (gt % mtiles) * BM;
+    n0 = (gt / mtiles) * BN;
     const uint32_t blo = part * sk.nblk / sk.parts, bhi = (part + 1u) * sk.nblk / sk.parts;
     kb = blo << (gs_log2 + 3u);
     kl = (bhi - blo) << (gs_log2 + 3u);
@@ -768,7 +776,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
       ++k;
     }
   }
-  if (sk.parts > 1u) {
+  if (split) {
     // this wave's fp32 partial of its sub-tile, lane-major float4s
     constexpr uint32_t kVals = TI * TJ;  // float4s per lane
     float *mine = sk.part + (((size_t)part * sk.ntiles + tile) * kMma + wave) * kVals * 256u + lane * 4u;
@@ -800,7 +808,8 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NP)) void k_gemm_prefill_dma(
 // tiles of 16 x 16 per wave.
 template <int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(256) void k_splitk_sum(const float *__restrict__ part, uint32_t parts, uint32_t ntiles,
-                                                    uint32_t mtiles, uint16_t *__restrict__ Y, uint32_t m, uint32_t N) {
+                                                    uint32_t tile0, uint32_t mtiles, uint16_t *__restrict__ Y,
+                                                    uint32_t m, uint32_t N) {
   constexpr uint32_t WTM = BM / WGM, WTN = BN / WGN, TI = WTM / 16, TJ = WTN / 16, kMma = WGM * WGN;
   constexpr uint32_t kVals = TI * TJ;
   const uint32_t t = blockIdx.x * 256u + threadIdx.x;
@@ -811,7 +820,8 @@ __global__ __launch_bounds__(256) void k_splitk_sum(const float *__restrict__ pa
   f32x4 sum = *reinterpret_cast<const f32x4 *>(p0);
   for (uint32_t q = 1; q < parts; ++q) sum += *reinterpret_cast<const f32x4 *>(p0 + q * stride);
   const uint32_t wm = wave / WGN, wn = wave % WGN, i = e / TJ, j = e % TJ;
-  const uint32_t m0 = (tile % mtiles) * BM, n0 = (tile / mtiles) * BN;
+  const uint32_t gt = tile0 + tile;
+  const uint32_t m0 = (gt % mtiles) * BM, n0 = (gt / mtiles) * BN;
   const uint32_t n = n0 + wn * WTN + 16u * j + (lane & 15u);
   if (n >= N) return;
 #pragma unroll
@@ -827,9 +837,13 @@ uint64_t split_bytes(uint32_t tiles, uint32_t parts) {
   return (uint64_t)parts * tiles * (WGM * WGN) * kSub;
 }
 
+// The number of tiles whose K is split when only the last, partial round is
+// split (tail): the tiles past the last whole round over the CUs.
+uint32_t tail_tiles(uint32_t tiles, uint32_t cus) { return tiles > cus ? tiles % cus : tiles; }
+
 template <int BM, int BN, int WGM, int WGN, int NP>
 hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream,
-                           uint32_t parts = 1, void *ws = nullptr) {
+                           uint32_t parts = 1, void *ws = nullptr, bool tail = false) {
   auto kern = k_gemm_prefill_dma<BM, BN, WGM, WGN, NP>;
   static bool configured = false;
   if (!configured) {
@@ -843,19 +857,23 @@ hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, 
   const size_t lds = 3u * (BM + BN) * BK * 2u + BN * 16u * 2u * 2u;
   const uint32_t gs_log2 = (uint32_t)__builtin_ctz(w.gs);
   if (parts > 1u) {
+    // every tile split, or (tail) only the tiles past the last whole round,
+    // the whole rounds' tiles first and unsplit
     const uint32_t tiles = mtiles * ntiles;
-    if (ws == nullptr) return hipErrorInvalidValue;
-    SplitK sk{parts, w.K >> (gs_log2 + 3u), tiles, static_cast<float *>(ws)};
-    const uint32_t nwork = tiles * parts;
+    const uint32_t nsplit = tail ? tail_tiles(tiles, (uint32_t)device_cu_count()) : tiles;
+    if (ws == nullptr || nsplit == 0u) return hipErrorInvalidValue;
+    const uint32_t nbig = tiles - nsplit;
+    SplitK sk{parts, w.K >> (gs_log2 + 3u), nsplit, static_cast<float *>(ws), nbig};
+    const uint32_t nwork = nbig + nsplit * parts;
     hipLaunchKernelGGL(kern, dim3(nwork), dim3(64 * (WGM * WGN + NP)), lds, stream,
                        reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m, gs_log2,
-                       mtiles, 0u, 0u, 0u, nwork, sk);
+                       mtiles, nbig, 0u, 0u, nwork, sk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr uint32_t kThreadsPerTile = (uint32_t)(BM * BN) / 4u;  // one float4 of outputs each
-    const uint32_t blocks = (uint32_t)(((uint64_t)tiles * kThreadsPerTile + 255u) / 256u);
+    const uint32_t blocks = (uint32_t)(((uint64_t)nsplit * kThreadsPerTile + 255u) / 256u);
     hipLaunchKernelGGL((k_splitk_sum<BM, BN, WGM, WGN>), dim3(blocks), dim3(256), 0, stream,
-                       static_cast<const float *>(ws), parts, tiles, mtiles, Y, m, w.N);
+                       static_cast<const float *>(ws), parts, nsplit, nbig, mtiles, Y, m, w.N);
     return hipGetLastError();
   }
   // When the full tiles leave a last round at most half full, the N tiles of
@@ -874,7 +892,7 @@ hipError_t launch_tile_dma(const WeightView &w, const uint16_t *X, uint16_t *Y, 
   const uint32_t mt_half = (m + BM / 2 - 1) / (BM / 2);
   const uint32_t nbig = mtiles * nt_big;
   const uint32_t nwork = nbig + mt_half * nt_half;
-  const SplitK none{1u, 0u, 0u, nullptr};
+  const SplitK none{1u, 0u, 0u, nullptr, 0u};
   hipLaunchKernelGGL(kern, dim3(nwork), dim3(64 * (WGM * WGN + NP)), lds, stream,
                      reinterpret_cast<const uint8_t *>(w.packed), w.scales, w.biases, X, Y, w.N, w.K, m, gs_log2,
                      mtiles, nbig, mt_half, nt_big, nwork, none);
@@ -958,11 +976,21 @@ struct PrefillPick {
   int shape;        // launch_gemm_prefill_tile's shape number
   uint32_t parts;   // K parts per tile (shape 3 only; 1 = no split)
   double est_us;    // estimated kernel time, or a negative value when no estimate is calibrated
+  bool tail;        // split only the tiles past the last whole round
 };
 
 // A split of K into `parts` (shape 3, a workspace given): (tile, part) items,
-// one round per ceil(items / CUs), each walking about 1 / parts of K, plus
-// ~5 us for storing the fp32 partials and the launch that sums them.
+// one round per ceil(items / CUs), each walking about 1 / parts of K and
+// costing ~8 us more per round (partial stores, a short pipeline), plus ~5 us
+// for the launch that sums the partials.  With a workspace the last, partial
+// round of 256 x 128 tiles can also be split on its own (tail): a partial
+// last round takes as long as a whole one, so the estimates count it whole
+// when that is an option.  Measured (graph-timed, interleaved) on 14336 x
+// 4096: m = 1536 (3 rounds) 195 us, m = 2048 (3.5) 258 us, m = 1792 (3 rounds
+// and 16 tiles) 272 us, 223 us with the 16 tiles split in 4; splitting a
+// larger tail was no faster (m = 2048: 255 us) or slower (m = 1024, 192 tiles:
+// 146-156 against 130 us), and splitting every tile slower still (m = 2048:
+// 315 us in 2 parts).
 PrefillPick prefill_pick(const WeightView &w, uint32_t m, uint32_t cus, bool can_split) {
   const double ksteps = (double)((w.K + 63u) / 64u);
   const uint32_t t256 = ((m + 255u) / 256u) * ((w.N + 127u) / 128u);
@@ -970,38 +998,47 @@ PrefillPick prefill_pick(const WeightView &w, uint32_t m, uint32_t cus, bool can
   const double r12864 = (double)((t12864 + cus - 1u) / cus);
   if (w.K % (8u * w.gs) == 0u) {
     const uint32_t rem = t256 % cus;
-    const double r256 = t256 <= cus ? 1.0 : (double)(t256 / cus) + (rem == 0u ? 0.0 : 2u * rem <= cus ? 0.5 : 1.0);
-    PrefillPick best{3, 1u, r256 * 0.85 * ksteps};
+    const double part_round = can_split ? 1.0 : 2u * rem <= cus ? 0.5 : 1.0;
+    const double r256 = t256 <= cus ? 1.0 : (double)(t256 / cus) + (rem == 0u ? 0.0 : part_round);
+    PrefillPick best{3, 1u, r256 * 0.85 * ksteps, false};
     const uint32_t nblk = w.K / (8u * w.gs);
     const double steps_per_blk = (double)(8u * w.gs) / 64.0;
     if (can_split) {
       for (uint32_t parts = 2; parts <= 8u && 2u * parts <= nblk; ++parts) {
+        const double per = 0.85 * steps_per_blk * (double)((nblk + parts - 1u) / parts) + 8.0;  // a round of parts
         const double rounds = (double)((t256 * parts + cus - 1u) / cus);
-        const double est = rounds * 0.85 * steps_per_blk * (double)((nblk + parts - 1u) / parts) + 5.0;
-        if (est < best.est_us) best = PrefillPick{3, parts, est};
+        const double est = rounds * per + 5.0;
+        if (est < best.est_us) best = PrefillPick{3, parts, est, false};
+        if (t256 > cus && rem != 0u) {
+          const double est_tail =
+              (double)(t256 / cus) * 0.85 * ksteps + (double)((rem * parts + cus - 1u) / cus) * per + 5.0;
+          if (est_tail < best.est_us) best = PrefillPick{3, parts, est_tail, true};
+        }
       }
     }
     const double e12864 = r12864 * 0.45 * ksteps;
-    return best.est_us <= e12864 ? best : PrefillPick{4, 1u, e12864};
+    return best.est_us <= e12864 ? best : PrefillPick{4, 1u, e12864, false};
   }
   const uint32_t t128 = ((m + 127u) / 128u) * ((w.N + 127u) / 128u);
-  if (4u * t256 >= 3u * cus) return {2, 1u, -1.0};
-  if (4u * t128 >= 3u * cus) return {0, 1u, -1.0};
-  return {1, 1u, r12864 * 0.42 * ksteps};
+  if (4u * t256 >= 3u * cus) return {2, 1u, -1.0, false};
+  if (4u * t128 >= 3u * cus) return {0, 1u, -1.0, false};
+  return {1, 1u, r12864 * 0.42 * ksteps, false};
 }
 
 }  // namespace
 
 uint64_t gemm_prefill_workspace_bytes(const WeightView &w, uint32_t m) {
-  const PrefillPick pick = prefill_pick(w, m, (uint32_t)device_cu_count(), true);
+  const uint32_t cus = (uint32_t)device_cu_count();
+  const PrefillPick pick = prefill_pick(w, m, cus, true);
   if (pick.parts <= 1u) return 0;
-  return split_bytes<256, 128, 4, 1, 4>(((m + 255u) / 256u) * ((w.N + 127u) / 128u), pick.parts);
+  const uint32_t tiles = ((m + 255u) / 256u) * ((w.N + 127u) / 128u);
+  return split_bytes<256, 128, 4, 1, 4>(pick.tail ? tail_tiles(tiles, cus) : tiles, pick.parts);
 }
 
 hipError_t launch_gemm_prefill(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, void *ws,
                                hipStream_t stream) {
   const PrefillPick pick = prefill_pick(w, m, (uint32_t)device_cu_count(), ws != nullptr);
-  if (pick.parts > 1u) return launch_tile_dma<256, 128, 4, 1, 4>(w, X, Y, m, stream, pick.parts, ws);
+  if (pick.parts > 1u) return launch_tile_dma<256, 128, 4, 1, 4>(w, X, Y, m, stream, pick.parts, ws, pick.tail);
   return launch_gemm_prefill_tile(pick.shape, w, X, Y, m, stream);
 }
 
