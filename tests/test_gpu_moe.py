@@ -44,6 +44,7 @@ def run_case(seed, E, N, K, gs, T, topk, per_slot_rows, ids=None):
     (8, 1024, 4096, 64, 4, 2, False),
     (3, 200, 16384, 128, 2, 2, True),    # 16-wave workgroups
     (2, 4096, 16384, 128, 1, 2, False),  # 16-wave workgroups, two rows side by side
+    (2, 300, 20480, 64, 1, 2, False),    # one tile with per-item scales (K over 16384)
     (16, 64, 1024, 32, 16, 4, True),     # many slots, few rows each
 ])
 def test_moe_gemv_matches_oracle(E, N, K, gs, T, topk, per_slot):

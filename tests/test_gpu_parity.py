@@ -83,7 +83,9 @@ GEMV_SHAPES = [
     (1024, 4096, 64),     # 8B k/v
     (1000, 4096, 64),     # ragged rows
     (33, 96, 32),         # ragged everything
-    (7, 20480, 128),      # K over one LDS tile (two tiles)
+    (7, 20480, 128),      # K over one staged tile: one tile, scales loaded per item
+    (9, 20512, 32),       # the same with a partial last segment: two staged tiles
+    (5000, 32768, 64),    # the largest K of one tile with per-item scales, two rows per wave
     (3000, 40960, 32),    # three LDS tiles, many rows
     (1, 32, 32),          # degenerate: one row, one group
     (5, 4128, 32),        # rows split over waves, partial last segment
@@ -144,7 +146,8 @@ MULTI_CASES = [
     ([4096, 1024, 1024], 4096, 64),   # q, k, v of an 8B layer
     ([14336, 14336], 4096, 64),       # gate and up
     ([33, 7, 100, 1], 96, 32),        # four ragged weights
-    ([300, 5], 20480, 128),           # two LDS tiles
+    ([300, 5], 20480, 128),           # one tile with per-item scales
+    ([40, 90], 33792, 64),            # over 32768: several staged tiles
     ([77, 3000], 4128, 32),           # partial last segment
     ([1], 32, 32),
     ([700, 300], 2048, 32),           # register-resident form, two weights
@@ -176,8 +179,10 @@ def test_gemv_multi(ns, K, gs):
 GATED_SHAPES = [
     (256, 512, 64),
     (4096, 14336, 64),    # 8B down projection
-    (8192, 28672, 128),   # 70B down projection
+    (8192, 28672, 128),   # 70B down projection (one tile, scales loaded per item)
     (1000, 3072, 32),
+    (600, 17408, 32),     # one tile with per-item scales, one row per wave
+    (50, 17440, 32),      # partial last segment over 16384: two staged tiles
     (33, 96, 32),
     (5, 36864, 64),       # K over one LDS tile
     (77, 4128, 32),       # rows split over waves, partial last segment

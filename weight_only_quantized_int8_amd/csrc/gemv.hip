@@ -47,7 +47,8 @@ namespace int8w {
 
 namespace {
 
-constexpr uint32_t kTileRunsMax = 1024;    // 16384 activations per LDS tile
+constexpr uint32_t kTileRunsMax = 1024;    // 16384 activations per LDS tile (staged scales)
+constexpr uint32_t kTileRunsInline = 2048; // 32768 per tile when the scales come with the codes
 constexpr int kLoadsPerBlock = 4;          // 1 KiB wave loads per pipeline block (U items x RP rows)
 constexpr uint32_t kMaxRowsPerWave = 16;   // rows a wave may own
 constexpr size_t kLdsPerCu = 156 * 1024;   // dynamic LDS budget of one CU
@@ -60,11 +61,12 @@ struct GemvCfg {
   uint32_t ct;         // 16-code runs per LDS tile (multiple of 64)
   uint32_t max_rows;   // most rows any wave owns
   bool tail;           // in_features not a multiple of 1024
+  bool sbi;            // scales and biases loaded with the codes, not staged in LDS
 };
 
-// LDS bytes of one workgroup (layout in k_gemv).
+// LDS bytes of one workgroup (layout in gemv_wave).
 size_t lds_bytes(const GemvCfg &c, uint32_t gs) {
-  const size_t tg = (size_t)c.ct * 16u / gs;
+  const size_t tg = c.sbi ? 0u : (size_t)c.ct * 16u / gs;
   return (size_t)c.ct * 68u + (size_t)c.waves * c.max_rows * tg * 8u + (size_t)c.waves * c.max_rows * 4u;
 }
 
@@ -125,14 +127,21 @@ struct GemvTargets {
 template <int U, int RP>
 struct Block {
   u32x4 q[U][RP];
+  uint16_t s[U][RP], b[U][RP];  // BF16 bits of the lane's group scale and bias (SBI only)
 };
 
 // LDS layout of one workgroup (dynamic):
 //   act   [NSEG][4][64] float4   activation of lane l's 16 codes in segment s
 //   ssum  [NSEG][64] float       their sum
-//   sb    [W][max_rows][TG] float2   each wave's (scale, bias - 1024 scale)
+//   sb    [W][max_rows][TG] float2   each wave's (scale, bias - 1024 scale); not with SBI
 //   part  [W][max_rows] float        row partial sums across K-tiles
-template <int EPI, int W, int RP, int U, bool TAIL>
+// SBI: each item's scale and bias (of the lane's group) are loaded with its
+// codes instead of being staged per tile, which frees the LDS for a tile of
+// up to 32768 activations: the long rows of a 16-wave workgroup (in_features
+// 16385..32768) then run as one tile, with no drain and second prologue in
+// the middle of the stream.  Same arithmetic per run; for shapes the staged
+// form also covers in one tile, the same bits.
+template <int EPI, int W, int RP, int U, bool TAIL, bool SBI>
 __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                                           const uint16_t *__restrict__ biases, uint16_t *y, uint32_t N,
                                           uint32_t lw, uint32_t TW, const uint16_t *__restrict__ xg,
@@ -142,11 +151,12 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
   // weight.  y may be resid itself (in-place residual): each output element
   // reads its own residual before it is written, by the same lane.
   constexpr int kThreads = 64 * W;
-  constexpr int kStage = (int)(kTileRunsMax + kThreads - 1) / kThreads;  // runs staged per thread
+  constexpr uint32_t kRunsMax = SBI ? kTileRunsInline : kTileRunsMax;
+  constexpr int kStage = (int)(kRunsMax + kThreads - 1) / kThreads;  // runs staged per thread
   extern __shared__ float4 lds4[];
   const uint32_t CT = tile_runs;
   const uint32_t NSEG = CT >> 6;
-  const uint32_t TG = (CT << 4) >> gs_log2;
+  const uint32_t TG = SBI ? 0u : (CT << 4) >> gs_log2;
   float4 *act = lds4;
   float *ssum = reinterpret_cast<float *>(lds4 + NSEG * 256);
   float2 *sb_all = reinterpret_cast<float2 *>(ssum + NSEG * 64);
@@ -162,6 +172,7 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
   const uint32_t cpr = K >> 4;
   const uint32_t G = K >> gs_log2;
   const uint32_t gps = 1024u >> gs_log2;  // groups per segment
+  const uint32_t seg_sb = gps << 1;         // scale bytes per segment (SBI)
 
   const auto rw = make_rsrc(codes + (size_t)rbeg * K, nr * K);
   const auto rx = make_rsrc(xg, K * 2u);
@@ -170,6 +181,9 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
   // them at the weight's first row
   const uint16_t *srow = scales + (size_t)(nr ? rbeg : 0u) * G;
   const uint16_t *brow = biases + (size_t)(nr ? rbeg : 0u) * G;
+  const auto rsc = make_rsrc(scales + (size_t)rbeg * G, SBI ? nr * G * 2u : 0u);
+  const auto rbi = make_rsrc(biases + (size_t)rbeg * G, SBI ? nr * G * 2u : 0u);
+  const uint32_t v_sg = ((lane << 4) >> gs_log2) << 1;  // the lane's group in a segment, bytes (SBI)
   float2 *sb = sb_all + wave * max_rows * TG;
   float *part = part_all + wave * max_rows;
 
@@ -198,15 +212,21 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
     // staged (finite) scale/bias entry; their activations are zero
     const uint32_t vo_w_last = TAIL && lane >= last_lanes ? kOutOfRange : vo_w;
     const uint32_t v_sb_last = TAIL && lane >= last_lanes ? 0u : v_sb;
+    const uint32_t v_sg_last = TAIL && lane >= last_lanes ? kOutOfRange : v_sg;  // reads zero
     const uint32_t grp_skip = RP * K - (nseg << 10);  // to the next row group (mod 2^32)
+    const uint32_t grp_skip_s = RP * G * 2u - nseg * seg_sb;
     const uint32_t last_off = (nr ? nr - 1u : 0u) * K + (t0 << 4) + ((nseg - 1u) << 10);
+    const uint32_t last_soff = (nr ? nr - 1u : 0u) * G * 2u + (g0 << 1) + (nseg - 1u) * seg_sb;
 
-    uint32_t i_off = t0 << 4, i_seg = 0, i_grp = 0;
+    uint32_t i_off = t0 << 4, i_soff = g0 << 1, i_seg = 0, i_grp = 0;
     auto issue = [&](Block<U, RP> &blk) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        uint32_t vw = vo_w;
-        if constexpr (TAIL) vw = (i_seg == nseg - 1u) ? vo_w_last : vo_w;
+        uint32_t vw = vo_w, vs = v_sg;
+        if constexpr (TAIL) {
+          vw = (i_seg == nseg - 1u) ? vo_w_last : vo_w;
+          vs = (i_seg == nseg - 1u) ? v_sg_last : v_sg;
+        }
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
           // past the wave's rows a load re-reads the last segment of its last
@@ -215,9 +235,21 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
           const uint32_t sw = uniform(live ? i_off + r * K : last_off);
           const uint32_t vwr = live ? vw : vo_w_last;
           blk.q[u][r] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vwr, (int)sw, kAuxNontemporal);
+          if constexpr (SBI) {
+            const uint32_t ss = uniform(live ? i_soff + r * G * 2u : last_soff);
+            const uint32_t vsr = live ? vs : v_sg_last;
+            blk.s[u][r] = __builtin_amdgcn_raw_buffer_load_b16(rsc, (int)vsr, (int)ss, 0);
+            blk.b[u][r] = __builtin_amdgcn_raw_buffer_load_b16(rbi, (int)vsr, (int)ss, 0);
+          }
         }
         i_off += 1024u;
-        if (++i_seg == nseg) { i_seg = 0; ++i_grp; i_off += grp_skip; }
+        if constexpr (SBI) i_soff += seg_sb;
+        if (++i_seg == nseg) {
+          i_seg = 0;
+          ++i_grp;
+          i_off += grp_skip;
+          if constexpr (SBI) i_soff += grp_skip_s;
+        }
       }
     };
     uint32_t c_grp = 0, c_seg = 0;
@@ -231,13 +263,19 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
           const float S = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(ssum) +
                                                            uniform(c_seg << 8) + v_s);
           uint32_t vs = v_sb;
-          if constexpr (TAIL) vs = (c_seg == nseg - 1u) ? v_sb_last : v_sb;
+          if constexpr (TAIL && !SBI) vs = (c_seg == nseg - 1u) ? v_sb_last : v_sb;
 #pragma unroll
           for (int r = 0; r < RP; ++r) {
-            const uint32_t row = c_grp * RP + r;
-            const uint32_t rs = row < nr ? row : 0u;
-            const float2 sbv = *reinterpret_cast<const float2 *>(
-                reinterpret_cast<const char *>(sb) + uniform((rs * tg + c_seg * gps) << 3) + vs);
+            float2 sbv;
+            if constexpr (SBI) {
+              sbv.x = bf16_bits_to_f32(blk.s[u][r]);
+              sbv.y = __builtin_fmaf(-1024.f, sbv.x, bf16_bits_to_f32(blk.b[u][r]));
+            } else {
+              const uint32_t row = c_grp * RP + r;
+              const uint32_t rs = row < nr ? row : 0u;
+              sbv = *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(sb) +
+                                                      uniform((rs * tg + c_seg * gps) << 3) + vs);
+            }
             const float p = run_dot(blk.q[u][r], a0, a1, a2, a3);
             acc[r] = __builtin_fmaf(sbv.x, p, __builtin_fmaf(sbv.y, S, acc[r]));
           }
@@ -265,8 +303,8 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
       }
     };
 
-    // 1. activation loads, the first weight block, then this wave's scales
-    //    and biases for the tile: all in flight together
+    // 1. activation loads, then this wave's scales and biases for the tile
+    //    (staged form), then the first weight block: all in flight together
     u32x4 xv[kStage][2], uv[kStage][2];
 #pragma unroll
     for (int s = 0; s < kStage; ++s) {
@@ -282,13 +320,15 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
     const uint32_t nsb = nr * tg;
     const uint32_t tg_inv = (uint32_t)(0xFFFFFFFFu / tg) + 1u;  // e / tg == umulhi(e, tg_inv) for e < 2^16
     uint16_t sv[kSbPerLane], bv[kSbPerLane];
+    if constexpr (!SBI) {
 #pragma unroll
-    for (int j = 0; j < kSbPerLane; ++j) {
-      const uint32_t e = lane + 64u * j;
-      const uint32_t r = __umulhi(e, tg_inv), g = e - r * tg;
-      const uint32_t src = e < nsb ? r * G + g0 + g : 0u;
-      sv[j] = srow[src];
-      bv[j] = brow[src];
+      for (int j = 0; j < kSbPerLane; ++j) {
+        const uint32_t e = lane + 64u * j;
+        const uint32_t r = __umulhi(e, tg_inv), g = e - r * tg;
+        const uint32_t src = e < nsb ? r * G + g0 + g : 0u;
+        sv[j] = srow[src];
+        bv[j] = brow[src];
+      }
     }
     // the first weight block goes out after the small loads and unconditionally
     // (a wave without items loads out of range): vmcnt counts in order, so
@@ -326,31 +366,33 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
       }
     }
     __syncthreads();
-    // this wave's private (scale, bias - 1024 scale) slice: only this wave
-    // reads it, after writing it, and its previous tile is consumed
-#pragma unroll
-    for (int j = 0; j < kSbPerLane; ++j) {
-      const uint32_t e = lane + 64u * j;
-      if (e < nsb) {
-        const float sc = bf16_bits_to_f32(sv[j]);
-        sb[e] = make_float2(sc, __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32(bv[j])));
-      }
-    }
-    for (uint32_t e0 = 64u * kSbPerLane; e0 < nsb; e0 += 64u * kSbPerLane) {  // rows beyond the prefetch
+    if constexpr (!SBI) {
+      // this wave's private (scale, bias - 1024 scale) slice: only this wave
+      // reads it, after writing it, and its previous tile is consumed
 #pragma unroll
       for (int j = 0; j < kSbPerLane; ++j) {
-        const uint32_t e = e0 + lane + 64u * j;
-        const uint32_t r = __umulhi(e, tg_inv), g = e - r * tg;
-        const uint32_t src = e < nsb ? r * G + g0 + g : 0u;
-        sv[j] = srow[src];
-        bv[j] = brow[src];
-      }
-#pragma unroll
-      for (int j = 0; j < kSbPerLane; ++j) {
-        const uint32_t e = e0 + lane + 64u * j;
+        const uint32_t e = lane + 64u * j;
         if (e < nsb) {
           const float sc = bf16_bits_to_f32(sv[j]);
           sb[e] = make_float2(sc, __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32(bv[j])));
+        }
+      }
+      for (uint32_t e0 = 64u * kSbPerLane; e0 < nsb; e0 += 64u * kSbPerLane) {  // rows beyond the prefetch
+#pragma unroll
+        for (int j = 0; j < kSbPerLane; ++j) {
+          const uint32_t e = e0 + lane + 64u * j;
+          const uint32_t r = __umulhi(e, tg_inv), g = e - r * tg;
+          const uint32_t src = e < nsb ? r * G + g0 + g : 0u;
+          sv[j] = srow[src];
+          bv[j] = brow[src];
+        }
+#pragma unroll
+        for (int j = 0; j < kSbPerLane; ++j) {
+          const uint32_t e = e0 + lane + 64u * j;
+          if (e < nsb) {
+            const float sc = bf16_bits_to_f32(sv[j]);
+            sb[e] = make_float2(sc, __builtin_fmaf(-1024.f, sc, bf16_bits_to_f32(bv[j])));
+          }
         }
       }
     }
@@ -358,12 +400,13 @@ __device__ __forceinline__ void gemv_wave(const uint8_t *__restrict__ codes, con
     //    the loop.  The loop has a single exit: with an exit after every
     //    block, the compiler's wait counts at the loop head also covered the
     //    paths that leave, and it waited there for the block just issued.
-    //    After each consume the other block's U RP loads may still be in
-    //    flight, and nothing older: said explicitly, because a consume whose
-    //    items are past the wave's rows reads nothing and so waits for
-    //    nothing, and the compiler would otherwise wait for every load
-    //    before reusing the consumed block's registers.
-    constexpr int kBlk = U * RP;
+    //    After each consume the other block's loads (U RP items, each its
+    //    codes, and with SBI its scale and bias) may still be in flight, and
+    //    nothing older: said explicitly, because a consume whose items are
+    //    past the wave's rows reads nothing and so waits for nothing, and the
+    //    compiler would otherwise wait for every load before reusing the
+    //    consumed block's registers.
+    constexpr int kBlk = (SBI ? 3 : 1) * U * RP;
     uint32_t b = 0;
     for (; b + 2u < nblk; b += 2u) {
       issue(B);
@@ -624,7 +667,7 @@ __global__ __launch_bounds__(512) void k_gemv_rows(const uint8_t *__restrict__ c
 
 // The wave body of a launch: the register-resident form (NS > 0) or the
 // LDS-tiled one (NS == 0).
-template <int NS, int EPI, int W, int RP, int U, bool TAIL>
+template <int NS, int EPI, int W, int RP, int U, bool TAIL, bool SBI>
 __device__ __forceinline__ void gemv_body(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
                                           uint16_t *y, uint32_t N, uint32_t lw, uint32_t TW, const uint16_t *xg,
                                           const uint16_t *up, const uint16_t *resid, uint32_t K, uint32_t gs_log2,
@@ -632,12 +675,12 @@ __device__ __forceinline__ void gemv_body(const uint8_t *codes, const uint16_t *
   if constexpr (NS > 0)
     gemv_wave_rx<NS>(codes, scales, biases, y, N, lw, TW, xg, gs_log2);
   else
-    gemv_wave<EPI, W, RP, U, TAIL>(codes, scales, biases, y, N, lw, TW, xg, up, resid, K, gs_log2, tile_runs,
+    gemv_wave<EPI, W, RP, U, TAIL, SBI>(codes, scales, biases, y, N, lw, TW, xg, up, resid, K, gs_log2, tile_runs,
                                    max_rows);
 }
 
 // gemv, gemv_silu_gate, gemv_silu_gate_resid: one weight, all waves.
-template <int NS, int EPI, int W, int RP, int U, bool TAIL>
+template <int NS, int EPI, int W, int RP, int U, bool TAIL, bool SBI>
 __global__ __launch_bounds__(64 * W) void k_gemv(const uint8_t *__restrict__ codes,
                                                  const uint16_t *__restrict__ scales,
                                                  const uint16_t *__restrict__ biases, const uint16_t *__restrict__ xg,
@@ -645,13 +688,13 @@ __global__ __launch_bounds__(64 * W) void k_gemv(const uint8_t *__restrict__ cod
                                                  uint32_t N, uint32_t K, uint32_t gs_log2, uint32_t tile_runs,
                                                  uint32_t max_rows) {
   const uint32_t gw = blockIdx.x * W + uniform(threadIdx.x >> 6);
-  gemv_body<NS, EPI, W, RP, U, TAIL>(codes, scales, biases, y, N, gw, gridDim.x * W, xg, up, resid, K, gs_log2,
+  gemv_body<NS, EPI, W, RP, U, TAIL, SBI>(codes, scales, biases, y, N, gw, gridDim.x * W, xg, up, resid, K, gs_log2,
                                      tile_runs, max_rows);
 }
 
 // gemv_multi: the waves are dealt to the weights of the launch in proportion
 // to their rows; each wave streams its share of one weight.
-template <int NS, int W, int RP, int U, bool TAIL>
+template <int NS, int W, int RP, int U, bool TAIL, bool SBI>
 __global__ __launch_bounds__(64 * W) void k_gemv_multi(GemvTargets t, const uint16_t *__restrict__ xg, uint32_t K,
                                                        uint32_t gs_log2, uint32_t tile_runs, uint32_t max_rows) {
   const uint32_t gw = blockIdx.x * W + uniform(threadIdx.x >> 6);
@@ -670,7 +713,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_multi(GemvTargets t, const uint
     }
   }
   // waves past the last weight's share (the grid is whole workgroups) own no rows
-  gemv_body<NS, kEpiNone, W, RP, U, TAIL>(codes, scales, biases, y, N, gw - wb, we - wb, xg, xg, nullptr, K,
+  gemv_body<NS, kEpiNone, W, RP, U, TAIL, SBI>(codes, scales, biases, y, N, gw - wb, we - wb, xg, xg, nullptr, K,
                                           gs_log2, tile_runs, max_rows);
 }
 
@@ -682,7 +725,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_multi(GemvTargets t, const uint
 // and each slot streams its expert once, so an expert named by several slots
 // is streamed once per slot.  A slot whose id is not below E writes NaN and
 // reads no weight.
-template <int NS, int W, int RP, int U, bool TAIL>
+template <int NS, int W, int RP, int U, bool TAIL, bool SBI>
 __global__ __launch_bounds__(64 * W) void k_moe_gemv(const uint8_t *__restrict__ codes,
                                                      const uint16_t *__restrict__ scales,
                                                      const uint16_t *__restrict__ biases,
@@ -706,7 +749,7 @@ __global__ __launch_bounds__(64 * W) void k_moe_gemv(const uint8_t *__restrict__
   const uint32_t t = p / topk, j = p - t * topk;
   const uint16_t *xp = x + ((size_t)t * x_rows + (x_rows == 1u ? 0u : j)) * K;
   const size_t G = K >> gs_log2;
-  gemv_body<NS, kEpiNone, W, RP, U, TAIL>(codes + (size_t)e * N * K, scales + (size_t)e * N * G,
+  gemv_body<NS, kEpiNone, W, RP, U, TAIL, SBI>(codes + (size_t)e * N * K, scales + (size_t)e * N * G,
                                           biases + (size_t)e * N * G, yp, N, lw, TW, xp, xp, nullptr, K, gs_log2,
                                           tile_runs, max_rows);
 }
@@ -894,21 +937,21 @@ hipError_t raise_lds_cap(Kern kern, bool &configured, int bytes = 160 * 1024) {
   return e;
 }
 
-template <int EPI, int W, int RP, bool TAIL, int NS = 0>
+template <int EPI, int W, int RP, bool TAIL, int NS = 0, bool SBI = false>
 hipError_t launch_cfg(const GemvCfg &cfg, const GemvTargets &t, uint32_t K, uint32_t gs, const uint16_t *xg,
                       const uint16_t *up, const uint16_t *resid, hipStream_t stream) {
   static bool configured = false;  // raise the dynamic-LDS cap once per instantiation
   const uint32_t gs_log2 = (uint32_t)__builtin_ctz(gs);
   const size_t lds = NS ? 0u : lds_bytes(cfg, gs);  // the register-resident form uses no LDS
   if (t.count == 1) {
-    auto kern = k_gemv<NS, EPI, W, RP, kLoadsPerBlock / RP, TAIL>;
+    auto kern = k_gemv<NS, EPI, W, RP, kLoadsPerBlock / RP, TAIL, SBI>;
     hipError_t e = raise_lds_cap(kern, configured);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(cfg.blocks), dim3(64 * W), lds, stream, t.codes[0], t.scales[0], t.biases[0], xg,
                        up, resid, t.y[0], t.n[0], K, gs_log2, cfg.ct, cfg.max_rows);
   } else {
     static bool configured_multi = false;
-    auto kern = k_gemv_multi<NS, W, RP, kLoadsPerBlock / RP, TAIL>;
+    auto kern = k_gemv_multi<NS, W, RP, kLoadsPerBlock / RP, TAIL, SBI>;
     hipError_t e = raise_lds_cap(kern, configured_multi);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(cfg.blocks), dim3(64 * W), lds, stream, t, xg, K, gs_log2, cfg.ct, cfg.max_rows);
@@ -926,11 +969,41 @@ template <int EPI, bool TAIL>
 hipError_t launch_shape(const GemvCfg &cfg, const GemvTargets &t, uint32_t K, uint32_t gs, const uint16_t *xg,
                         const uint16_t *up, const uint16_t *resid, hipStream_t stream) {
   if (cfg.waves == 16) {
+    if constexpr (!TAIL) {
+      if (cfg.sbi)
+        return cfg.rp == 2 ? launch_cfg<EPI, 16, 2, false, 0, true>(cfg, t, K, gs, xg, up, resid, stream)
+                           : launch_cfg<EPI, 16, 1, false, 0, true>(cfg, t, K, gs, xg, up, resid, stream);
+    }
     return cfg.rp == 2 ? launch_cfg<EPI, 16, 2, TAIL>(cfg, t, K, gs, xg, up, resid, stream)
                        : launch_cfg<EPI, 16, 1, TAIL>(cfg, t, K, gs, xg, up, resid, stream);
   }
   return cfg.rp == 2 ? launch_cfg<EPI, 8, 2, TAIL>(cfg, t, K, gs, xg, up, resid, stream)
                      : launch_cfg<EPI, 8, 1, TAIL>(cfg, t, K, gs, xg, up, resid, stream);
+}
+
+// The activation tile of the LDS form: the whole row in one tile with
+// staged scales when that fits the LDS budget; else, for 16-wave workgroups
+// and in_features a multiple of 1024 up to 32768, one tile with the scales
+// loaded per item (sbi); else several staged tiles.  One tile saves a drain
+// of the stream, a barrier and a second prologue per extra tile: 8192 x 28672
+// gs128 silu_gate_resid 41.9 -> 40.3 us (graph-timed, interleaved).  Where
+// one staged tile fits, the staged form stays (per-item scale loads measured
+// 0-4 % slower on 4096 x 14336).
+void pick_tile(GemvCfg &c, uint32_t K, uint32_t gs, size_t budget) {
+  const uint32_t cpr = K / 16u;
+  c.tail = (cpr % 64u) != 0;
+  c.sbi = false;
+  uint32_t ntiles = (cpr + kTileRunsMax - 1) / kTileRunsMax;
+  for (;; ++ntiles) {
+    c.ct = ((cpr + ntiles - 1) / ntiles + 63u) / 64u * 64u;
+    if (lds_bytes(c, gs) <= budget || c.ct == 64u) break;
+  }
+  if (ntiles > 1u && c.waves == 16 && !c.tail && cpr <= kTileRunsInline) {
+    GemvCfg one = c;
+    one.sbi = true;
+    one.ct = cpr;  // a multiple of 64 runs: in_features is a multiple of 1024
+    if (lds_bytes(one, gs) <= budget) c = one;
+  }
 }
 
 // Deal the launch's waves to its weights in proportion to their rows (every
@@ -991,13 +1064,7 @@ GemvCfg choose_cfg(const uint32_t *n, uint32_t count, uint32_t K, uint32_t gs, u
   const uint32_t tw = c.blocks * W;
   c.blocks = (wave_end[count - 1] + W - 1) / W;  // no workgroup of idle waves only
   c.rp = rp ? rp : (c.waves == 16 && N / tw >= 2u ? 2 : 1);
-  const uint32_t cpr = K / 16u;
-  const size_t budget = kLdsPerCu / per_cu;
-  for (uint32_t ntiles = (cpr + kTileRunsMax - 1) / kTileRunsMax;; ++ntiles) {
-    c.ct = ((cpr + ntiles - 1) / ntiles + 63u) / 64u * 64u;
-    if (lds_bytes(c, gs) <= budget || c.ct == 64u) break;
-  }
-  c.tail = (cpr % 64u) != 0;
+  pick_tile(c, K, gs, kLdsPerCu / per_cu);
   return c;
 }
 
@@ -1049,11 +1116,11 @@ hipError_t launch_gemv_list(const WeightView *w, uint16_t *const *y, uint32_t co
   return launch_targets(cfg, t, w[0].K, w[0].gs, epi, x_or_gate, up, x_resid, stream);
 }
 
-template <int W, int RP, bool TAIL, int NS = 0>
+template <int W, int RP, bool TAIL, int NS = 0, bool SBI = false>
 hipError_t launch_moe_cfg(const GemvCfg &cfg, const WeightView &w, uint32_t E, const uint16_t *x, uint32_t x_rows,
                           const uint32_t *ids, uint32_t topk, uint32_t slots, uint16_t *y, hipStream_t stream) {
   static bool configured = false;
-  auto kern = k_moe_gemv<NS, W, RP, kLoadsPerBlock / RP, TAIL>;
+  auto kern = k_moe_gemv<NS, W, RP, kLoadsPerBlock / RP, TAIL, SBI>;
   hipError_t e = raise_lds_cap(kern, configured);
   if (e != hipSuccess) return e;
   const uint32_t gs_log2 = (uint32_t)__builtin_ctz(w.gs);
@@ -1082,13 +1149,7 @@ GemvCfg choose_moe_cfg(uint32_t N, uint32_t K, uint32_t gs, uint32_t slots) {
   c.blocks = per_slot * slots;
   c.max_rows = (N + tw - 1) / tw;
   c.rp = c.waves == 16 && N / tw >= 2u ? 2 : 1;
-  const uint32_t cpr = K / 16u;
-  const size_t budget = kLdsPerCu / per_cu;
-  for (uint32_t ntiles = (cpr + kTileRunsMax - 1) / kTileRunsMax;; ++ntiles) {
-    c.ct = ((cpr + ntiles - 1) / ntiles + 63u) / 64u * 64u;
-    if (lds_bytes(c, gs) <= budget || c.ct == 64u) break;
-  }
-  c.tail = (cpr % 64u) != 0;
+  pick_tile(c, K, gs, kLdsPerCu / per_cu);
   return c;
 }
 
@@ -1188,6 +1249,9 @@ hipError_t launch_moe_gemv(const WeightView &w, uint32_t E, const uint16_t *x, u
     }
   }
   if (cfg.waves == 16) {
+    if (cfg.sbi)
+      return cfg.rp == 2 ? launch_moe_cfg<16, 2, false, 0, true>(cfg, w, E, x, x_rows, ids, topk, slots, y, stream)
+                         : launch_moe_cfg<16, 1, false, 0, true>(cfg, w, E, x, x_rows, ids, topk, slots, y, stream);
     if (cfg.rp == 2)
       return cfg.tail ? launch_moe_cfg<16, 2, true>(cfg, w, E, x, x_rows, ids, topk, slots, y, stream)
                       : launch_moe_cfg<16, 2, false>(cfg, w, E, x, x_rows, ids, topk, slots, y, stream);
