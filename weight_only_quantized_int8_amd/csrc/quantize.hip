@@ -46,25 +46,49 @@ __device__ __forceinline__ uint32_t quant_code(float v, float b, float s) {
 // t = (v - b) * rcp(s) serves where it is clearly on one side of one: rcp is
 // within 1 ulp and the product within half an ulp, so for quotients below 256
 // t is within 2^-14 of the correctly rounded quotient, and a t farther than
-// 2^-13 from every half-integer gives the same code.  Returns a mask of the
-// codes (bit i for code i) that need the IEEE division (t near a
-// half-integer, or not finite).  v - b >= 0 (b is the group's minimum), so
-// codes are only clamped at 255.
-__device__ __forceinline__ uint32_t quant_codes_fast(const float (&f)[8], float b, float s, uint32_t &q0,
-                                                     uint32_t &q1) {
+// 2^-13 from every half-integer gives the same code.  near[i] is set for the
+// codes that need the IEEE division (t near a half-integer, or not finite);
+// as booleans they stay lane masks in scalar registers.  v - b >= 0 (b is
+// the group's minimum), so codes are only clamped at 255.
+__device__ __forceinline__ void quant_codes_fast(const float (&f)[8], float b, float s, uint32_t &q0, uint32_t &q1,
+                                                 bool (&near)[8]) {
   const float rs = __builtin_amdgcn_rcpf(s);
-  uint32_t near = 0u;
+  const bool live = s != 0.0f;
   uint32_t w[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float t = (f[i] - b) * rs;
     const float r = __builtin_rintf(t);
-    near |= __builtin_fabsf(t - r) < 0.5f - 0x1p-13f ? 0u : (1u << i);
+    near[i] = live && !(__builtin_fabsf(t - r) < 0.5f - 0x1p-13f);
     w[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fminf(r, 255.0f), i & 3, w[i >> 2]);
   }
   q0 = w[0];
   q1 = w[1];
-  return s != 0.0f ? near : 0u;
+}
+
+// Cross-lane min / max over the LPG lanes of a group (aligned runs of 4, 8 or
+// 16 lanes) by row-local DPP moves: swap neighbours, swap pairs, then mirror
+// the half row and the row.  Each step combines two disjoint halves of the
+// lanes seen so far, so every lane ends with the group's extreme; min and max
+// do not depend on the order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int LPG>
+__device__ __forceinline__ void group_min_max(float &lo, float &hi) {
+  lo = fminf(lo, dpp_mov<0xB1>(lo));  // quad_perm [1,0,3,2]
+  hi = fmaxf(hi, dpp_mov<0xB1>(hi));
+  lo = fminf(lo, dpp_mov<0x4E>(lo));  // quad_perm [2,3,0,1]
+  hi = fmaxf(hi, dpp_mov<0x4E>(hi));
+  if constexpr (LPG >= 8) {
+    lo = fminf(lo, dpp_mov<0x141>(lo));  // row_half_mirror
+    hi = fmaxf(hi, dpp_mov<0x141>(hi));
+  }
+  if constexpr (LPG >= 16) {
+    lo = fminf(lo, dpp_mov<0x140>(lo));  // row_mirror
+    hi = fmaxf(hi, dpp_mov<0x140>(hi));
+  }
 }
 
 template <int U>
@@ -126,11 +150,7 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(const uint16_t *__restri
         }
         // lanes past the end hold zeros; they sit in their own (unwritten)
         // groups, since chunks is a whole number of groups
-#pragma unroll
-        for (int off = 1; off < LPG; off <<= 1) {
-          lo = fminf(lo, __shfl_xor(lo, off, 64));
-          hi = fmaxf(hi, __shfl_xor(hi, off, 64));
-        }
+        group_min_max<LPG>(lo, hi);
         // A zero extreme is +0: the cross-lane min/max do not follow element
         // order, so which signed zero survives is arbitrary; normalising both
         // makes an all-zero group's scale and bias +0 whatever the order.
@@ -141,15 +161,17 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(const uint16_t *__restri
         const uint16_t b_bits = to_bf16_bits(lo);  // exact
         const float s = bf16_bits_to_f32(s_bits), b = bf16_bits_to_f32(b_bits);
         uint32_t q0, q1;
-        const uint32_t near = quant_codes_fast(f, b, s, q0, q1);
+        bool near[8];
+        quant_codes_fast(f, b, s, q0, q1, near);
         if (s == 0.0f) q0 = q1 = 0u;
         // The IEEE division, per code position, only where some lane of the
         // wave needs it there (each test is wave-uniform; usually none does,
         // and when one does it is usually one position of one lane).
-        if (__builtin_amdgcn_ballot_w64(near != 0u) != 0u) {
+        if (__builtin_amdgcn_ballot_w64(near[0] || near[1] || near[2] || near[3] || near[4] || near[5] ||
+                                        near[6] || near[7]) != 0u) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const bool here = (near >> i) & 1u;
+            const bool here = near[i];
             if (__builtin_amdgcn_ballot_w64(here) != 0u) {
               if (here) {
                 const uint32_t c = quant_code(f[i], b, s) << (8 * (i & 3));
