@@ -49,7 +49,11 @@ __device__ __forceinline__ uint32_t quant_code(float v, float b, float s) {
 // 2^-13 from every half-integer gives the same code.  near[i] is set for the
 // codes that need the IEEE division (t near a half-integer, or not finite);
 // as booleans they stay lane masks in scalar registers.  v - b >= 0 (b is
-// the group's minimum), so codes are only clamped at 255.
+// the group's minimum), so codes are only clamped at 255: v_cvt_pk_u8_f32
+// saturates to 0..255 (measured on gfx950: 256, 300 and +inf give 255;
+// it rounds to nearest even, so on the integer-valued r it is exact), which
+// is the clamp.  A NaN quotient (only with s == 0) gives 0, and those codes
+// are zeroed by the caller anyway.
 __device__ __forceinline__ void quant_codes_fast(const float (&f)[8], float b, float s, uint32_t &q0, uint32_t &q1,
                                                  bool (&near)[8]) {
   const float rs = __builtin_amdgcn_rcpf(s);
@@ -60,7 +64,7 @@ __device__ __forceinline__ void quant_codes_fast(const float (&f)[8], float b, f
     const float t = (f[i] - b) * rs;
     const float r = __builtin_rintf(t);
     near[i] = live && !(__builtin_fabsf(t - r) < 0.5f - 0x1p-13f);
-    w[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fminf(r, 255.0f), i & 3, w[i >> 2]);
+    w[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r, i & 3, w[i >> 2]);
   }
   q0 = w[0];
   q1 = w[1];
