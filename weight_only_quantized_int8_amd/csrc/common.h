@@ -38,11 +38,14 @@ __device__ __forceinline__ float code_f32(uint32_t word, int b) {
   return (float)((word >> (8 * b)) & 0xFFu);
 }
 
-// silu(g) * u in fp32; silu(g) = g / (1 + e^-g).  For g -> -inf the
-// quotient is -0 (e^-g overflows to +inf), the limit of silu there.
+// silu(g) * u in fp32; silu(g) = g / (1 + e^-g), with the hardware
+// reciprocal of 1 + e^-g (within 1 ulp) instead of an IEEE division, whose
+// scale-and-fixup sequence cost about nine more operations per value.  For
+// g -> -inf, e^-g overflows to +inf, its reciprocal is +0 and the product
+// -0, the limit of silu there; for g -> +inf it is g.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  float e = __expf(-g);
-  return __fdividef(g, 1.0f + e) * u;
+  const float e = __expf(-g);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // Sum over the 64 lanes of a wave; every lane receives the total.
