@@ -31,6 +31,18 @@ constexpr int kQU = 4;          // items per pipeline block
 
 __device__ __forceinline__ uint32_t uniform_q(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// (hi - lo) / 255 correctly rounded without the division sequence: the
+// product with RN(1/255), then one FMA correction from the exact residual.
+// Equal to the IEEE quotient for every non-negative finite fp32 (denormals
+// included, which these kernels keep), checked exhaustively on the host by
+// tests/test_div255.py.
+__device__ __forceinline__ float div255(float x) {
+  constexpr float r = 1.0f / 255.0f;
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, 255.0f, x);
+  return __builtin_fmaf(e, r, q0);
+}
+
 // one code, in the order of the definition above
 __device__ __forceinline__ uint32_t quant_code(float v, float b, float s) {
   if (s == 0.0f) return 0u;
@@ -160,7 +172,7 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(const uint16_t *__restri
         // makes an all-zero group's scale and bias +0 whatever the order.
         if (lo == 0.0f) lo = 0.0f;
         if (hi == 0.0f) hi = 0.0f;
-        const float sf = __fdiv_rn(hi - lo, 255.0f);
+        const float sf = div255(hi - lo);
         const uint16_t s_bits = to_bf16_bits(sf);
         const uint16_t b_bits = to_bf16_bits(lo);  // exact
         const float s = bf16_bits_to_f32(s_bits), b = bf16_bits_to_f32(b_bits);
