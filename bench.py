@@ -571,6 +571,17 @@ def secondary(dev, quick):
                 del wdq
             del ws
             torch.cuda.empty_cache()
+    # two rows on long in_features where X's rows are kept in LDS (group size
+    # 32 at 14336, and the 70B-shaped down projection)
+    for N, K, gs in ((4096, 14336, 32), (8192, 28672, 128)):
+        ws = make_weights(2200 + N + gs, N, K, gs, copies_for(N * K), dev)
+        X = bits_dev(synth.gen_act(np.random.default_rng(2201 + N), (2, K)), dev)
+        Y = torch.empty((2, N), dtype=torch.bfloat16, device=dev)
+        t = time_batches(lambda i: ws[i % len(ws)].gemm(X, Y), 30)
+        b = gemm_bytes(N, K, gs, 2)
+        res[f"gemm_m2_{N}x{K}_gs{gs}"] = {"us": t * 1e6, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
+        del ws
+        torch.cuda.empty_cache()
     # a weight whose one round of 256 x 128 tiles walks all of K: m = 32 goes
     # through one 32-row small-m pass
     N, K, gs, m = 18944, 3584, 64, 32

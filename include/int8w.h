@@ -208,7 +208,10 @@ int int8_gemv_silu_gate_resid(const int8w_weight *w, const uint16_t *gate, const
  * both contiguous row-major.  Y[i,n] = RNE_bf16(sum_k w[n,k] * X[i,k]) with fp32
  * accumulation.  m = 1 runs the gemv; 2 <= m <= 16 the small-m kernel, which
  * multiplies the raw codes and applies each group's scale and bias to the
- * group's partial sums; larger m the tiled kernel, where the weight enters the
+ * group's partial sums (except a few rows on some shapes: 2..4 rows on
+ * in_features 1024..4096, and 2 rows on longer in_features at group size 32 or
+ * above 16384, take the gemv's weight stream with each code converted once and
+ * multiplied into every row); larger m the tiled kernel, where the weight enters the
  * matrix cores as RNE_bf16(w[n,k]) (the dequantize_to value).  For
  * 16 < m <= 128 on a weight that gives the tiled kernel few tiles per CU (so
  * that its time is set by walking all of in_features, whatever m), the rows

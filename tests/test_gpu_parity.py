@@ -341,6 +341,33 @@ def test_gemm_few_rows_register_form(m, N, K, gs):
 
 
 @pytest.mark.parametrize("m,N,K,gs", [
+    (2, 4096, 14336, 32),    # the 8B down projection at group size 32
+    (2, 8192, 28672, 128),   # the 70B down projection
+    (2, 1000, 32768, 32),    # m * in_features at the LDS limit (65536)
+    (2, 14336, 8192, 32),    # several rows per wave
+    (2, 77, 5120, 32),       # fewer rows than the workgroup has waves
+    (2, 5, 20480, 64),
+    (2, 4096, 14336, 64),    # group size 64 at 14336: the small-m kernel
+    (3, 4096, 14336, 32),    # three rows: the small-m kernel
+    (2, 300, 33792, 32),     # m * in_features above the limit: the small-m kernel
+])
+def test_gemm_few_rows_lds_form(m, N, K, gs):
+    """m = 2 on in_features above 4096 (group size 32, or above 16384): the
+    few-rows arithmetic with X's rows kept in LDS, and the shapes around it
+    that stay with the small-m kernel; repeated calls give the same bits."""
+    log(f"gemm few rows (LDS) m={m} N={N} K={K} gs={gs}")
+    w, rng = make_weight(2800 + m + N + K + gs, N, K, gs)
+    X = synth.gen_act(rng, (m, K))
+    W = upload(w)
+    Xd = bits_to_dev(X)
+    Y = dev_to_bits(W.gemm(Xd))
+    Y2 = dev_to_bits(W.gemm(Xd))
+    Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
+    assert_close(Y, Y_ref, A, f"gemm m={m} {N}x{K} gs{gs}")
+    assert np.array_equal(Y, Y2), "repeated call differs"
+
+
+@pytest.mark.parametrize("m,N,K,gs", [
     (17, 200, 512, 64),
     (64, 128, 256, 64),
     (129, 130, 96, 32),

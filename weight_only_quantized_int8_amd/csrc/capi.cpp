@@ -361,10 +361,13 @@ int gemm_common(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t 
   // the register-resident gemv form with several rows, measured faster there
   // than the small-m kernel (14336 x 4096, m = 2: 12.8 against 15.0 us)
   const bool rows = gemv_rows_supported(w->in_features, m) && (m <= 3u || N <= 8192u);
+  // 2 rows on longer in_features at group size 32 or above 16384: the same
+  // arithmetic with X's rows in LDS (4096 x 14336 gs32: 16.5 against 18.5 us)
+  const bool lrows = !rows && gemv_rows_lds_supported(w->in_features, w->group_size, m);
   const uint32_t slice = m > 16u ? gemm_smallm_slice_rows(view(w), m, ws != nullptr) : 0u;
   const bool passes = slice != 0u;
   // the tiled kernel addresses a 256-row X tile with 32-bit byte offsets
-  const bool tiled = !passes && !rows && (m > 16u || (m > 1u && !sm_ok));
+  const bool tiled = !passes && !rows && !lrows && (m > 16u || (m > 1u && !sm_ok));
   if (tiled && K * 2u * 256u > 0xFFFFFFFFull)
     return fail(INT8W_ERR_SHAPE, "in_features=%u above 2^23 - 1 needs m = 1 or a small-m shape (m=%u)",
                 w->in_features, m);
@@ -394,6 +397,8 @@ int gemm_common(const int8w_weight *w, const uint16_t *x, uint16_t *y, uint32_t 
     e = launch_gemv(view(w), kEpiNone, x, nullptr, nullptr, y, s);
   } else if (rows) {
     e = launch_gemv_rows(view(w), x, y, m, s);
+  } else if (lrows) {
+    e = launch_gemv_rows_lds(view(w), x, y, m, s);
   } else if (m <= 16 && sm_ok) {
     e = launch_gemm_smallm(view(w), x, y, m, s);
   } else if (passes) {

@@ -665,6 +665,179 @@ __global__ __launch_bounds__(512) void k_gemv_rows(const uint8_t *__restrict__ c
   gemv_wave_rxm<NS, MR>(codes, scales, biases, Y, N, gw, gridDim.x * 8u, X, gs_log2);
 }
 
+// gemm with MR rows of X (two, where it is used) on long rows (in_features
+// above 4096, a multiple of 1024): the arithmetic of gemv_wave_rxm (codes converted once
+// per run to BF16 pairs, v_dot2c_f32_bf16 into every row, s * sum q x +
+// b * sum x per run, the same reduction), with X kept in LDS instead of
+// registers.  The workgroup copies X's BF16 rows into LDS once (exact: no
+// conversion), each run's two 16-byte halves placed 1 KiB apart so that a
+// wave's reads of one half are contiguous, with the fp32 sum of each run's
+// 16 activations beside them; the waves then stream their rows in blocks of U
+// segments, scale and bias loaded with each segment's codes, two blocks in
+// flight.
+// LDS: xt [MR][K] BF16 (segment s of row r at r*2K + 2048 s: lane l's first
+// half at + 16 l, its second at + 1024 + 16 l), then ssum [MR][K/16] fp32.
+constexpr uint32_t kRowsLdsMaxMK = 65536;  // MR * in_features: 147 KiB of LDS
+
+template <int MR>
+__global__ __launch_bounds__(1024) void k_gemv_rows_lds(const uint8_t *__restrict__ codes,
+                                                        const uint16_t *__restrict__ scales,
+                                                        const uint16_t *__restrict__ biases,
+                                                        const uint16_t *__restrict__ X, uint16_t *Y, uint32_t N,
+                                                        uint32_t K, uint32_t gs_log2) {
+  constexpr int W = 16, U = 4;
+  constexpr uint32_t kThreads = 64u * W;
+  constexpr int kXRuns = (int)((kRowsLdsMaxMK / 16u + kThreads - 1u) / kThreads);  // X runs per thread
+  extern __shared__ u32x4 ldsx[];
+  uint8_t *xt = reinterpret_cast<uint8_t *>(ldsx);
+  const uint32_t runs = K >> 4;  // runs of 16 codes per row
+  float *ssum = reinterpret_cast<float *>(xt + MR * K * 2u);
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t lw = blockIdx.x * W + uniform(tid >> 6);
+  const uint32_t TW = gridDim.x * W;
+  const uint32_t rq = N / TW, rr = N % TW;
+  const uint32_t rbeg = lw * rq + (lw < rr ? lw : rr);
+  const uint32_t nr = lw < TW ? rq + (lw < rr ? 1u : 0u) : 0u;
+  const uint32_t nseg = K >> 10;
+  const uint32_t G = K >> gs_log2;
+  const uint32_t seg_sb = (1024u >> gs_log2) << 1;  // scale bytes per segment
+  const auto rw = make_rsrc(codes + (size_t)rbeg * K, nr * K);
+  const auto rsc = make_rsrc(scales + (size_t)rbeg * G, nr * G * 2u);
+  const auto rbi = make_rsrc(biases + (size_t)rbeg * G, nr * G * 2u);
+  const auto rx = make_rsrc(X, MR * K * 2u);
+  const uint32_t vo_w = lane << 4;
+  const uint32_t v_sg = ((lane << 4) >> gs_log2) << 1;  // the lane's group in a segment, bytes
+  const uint32_t last_off = (nr ? nr - 1u : 0u) * K + ((nseg - 1u) << 10);
+  const uint32_t last_soff = (nr ? nr - 1u : 0u) * G * 2u + (nseg - 1u) * seg_sb;
+
+  // 1. X's runs (32 bytes each), then the first code block: waiting for the
+  //    former never waits for the latter
+  const uint32_t xruns = MR * runs;
+  u32x4 xv[kXRuns][2];
+#pragma unroll
+  for (int j = 0; j < kXRuns; ++j) {
+    const uint32_t e = tid + (uint32_t)j * kThreads;
+    const uint32_t off = e < xruns ? e * 32u : kOutOfRange;
+    xv[j][0] = buf_load_b128(rx, off);
+    xv[j][1] = buf_load_b128(rx, off + 16u);
+  }
+  Block<U, 1> A, B;
+  uint32_t i_off = 0, i_soff = 0, i_seg = 0, i_grp = 0;
+  auto issue = [&](Block<U, 1> &blk) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // past the wave's rows a load re-reads the last segment of its last row
+      const bool live = i_grp < nr;
+      const uint32_t sw = uniform(live ? i_off : last_off);
+      const uint32_t ss = uniform(live ? i_soff : last_soff);
+      blk.q[u][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vo_w, (int)sw, kAuxNontemporal);
+      blk.s[u][0] = __builtin_amdgcn_raw_buffer_load_b16(rsc, (int)v_sg, (int)ss, 0);
+      blk.b[u][0] = __builtin_amdgcn_raw_buffer_load_b16(rbi, (int)v_sg, (int)ss, 0);
+      i_off += 1024u;
+      i_soff += seg_sb;
+      if (++i_seg == nseg) {
+        i_seg = 0;
+        ++i_grp;
+      }
+    }
+  };
+  issue(A);
+
+  // 2. X into LDS, with each run's sum (in the order gemv_wave_rxm sums)
+#pragma unroll
+  for (int j = 0; j < kXRuns; ++j) {
+    const uint32_t e = tid + (uint32_t)j * kThreads;
+    if (e < xruns) {
+      const uint32_t r = e / runs, t = e - r * runs;  // row, run within the row
+      uint8_t *dst = xt + r * K * 2u + ((t >> 6) << 11) + ((t & 63u) << 4);
+      *reinterpret_cast<u32x4 *>(dst) = xv[j][0];
+      *reinterpret_cast<u32x4 *>(dst + 1024u) = xv[j][1];
+      const uint32_t wv[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
+                              xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sum += bf16_lo(wv[i]);
+        sum += bf16_hi(wv[i]);
+      }
+      ssum[e] = sum;
+    }
+  }
+  __syncthreads();
+
+  float acc[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) acc[r] = 0.f;
+  uint32_t c_grp = 0, c_seg = 0;
+  auto consume = [&](const Block<U, 1> &blk) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c_grp < nr) {
+        const float sc = bf16_bits_to_f32(blk.s[u][0]);
+        const float bi = bf16_bits_to_f32(blk.b[u][0]);
+        const uint32_t words[4] = {blk.q[u][0].x, blk.q[u][0].y, blk.q[u][0].z, blk.q[u][0].w};
+        uint32_t cb[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t f0 = __builtin_bit_cast(uint32_t, code_f32(words[j], 0));
+          const uint32_t f1 = __builtin_bit_cast(uint32_t, code_f32(words[j], 1));
+          const uint32_t f2 = __builtin_bit_cast(uint32_t, code_f32(words[j], 2));
+          const uint32_t f3 = __builtin_bit_cast(uint32_t, code_f32(words[j], 3));
+          cb[2 * j] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+          cb[2 * j + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+        }
+        const uint32_t seg_off = uniform(c_seg << 11) + (lane << 4);
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+          const uint8_t *src = xt + r * K * 2u + seg_off;
+          const u32x4 h0 = *reinterpret_cast<const u32x4 *>(src);
+          const u32x4 h1 = *reinterpret_cast<const u32x4 *>(src + 1024u);
+          const uint32_t xw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+          const float S = ssum[r * runs + (c_seg << 6) + lane];
+          float p = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cb[i]), __builtin_bit_cast(bf16x2, xw[i]),
+                                                p, false);
+          acc[r] = __builtin_fmaf(sc, p, __builtin_fmaf(bi, S, acc[r]));
+        }
+        if (c_seg == nseg - 1u) {  // the row's last segment
+#pragma unroll
+          for (int r = 0; r < MR; ++r) {
+            const float tot = wave_sum_lane63(acc[r]);
+            if (lane == 63u) Y[(size_t)r * N + rbeg + c_grp] = to_bf16_bits(tot);
+            acc[r] = 0.f;
+          }
+        }
+      }
+      if (++c_seg == nseg) { c_seg = 0; ++c_grp; }
+    }
+  };
+  // 3. the pipeline of gemv_wave (two blocks in flight, a single exit); after
+  //    each consume only the other block's loads (codes, scale and bias of U
+  //    items) may still be in flight
+  const uint32_t nblk = (nr * nseg + U - 1u) / U;
+  constexpr int kBlk = 3 * U;
+  uint32_t b = 0;
+  for (; b + 2u < nblk; b += 2u) {
+    issue(B);
+    consume(A);
+    __builtin_amdgcn_s_waitcnt(((kBlk >> 4) << 14) | 0x0F70 | (kBlk & 15));
+    issue(A);
+    consume(B);
+    __builtin_amdgcn_s_waitcnt(((kBlk >> 4) << 14) | 0x0F70 | (kBlk & 15));
+  }
+  if (b + 1u < nblk) {
+    issue(B);
+    consume(A);
+    consume(B);
+  } else if (b < nblk) {
+    consume(A);
+  }
+}
+
 // The wave body of a launch: the register-resident form (NS > 0) or the
 // LDS-tiled one (NS == 0).
 template <int NS, int EPI, int W, int RP, int U, bool TAIL, bool SBI>
@@ -1197,6 +1370,42 @@ hipError_t launch_gemv_rows(const WeightView &w, const uint16_t *X, uint16_t *Y,
     default: launch_rows_ns<4>(w, X, Y, blocks, stream); break;
   }
   return hipGetLastError();
+}
+
+// Measured against the small-m matrix-core kernel (graph-timed, rotated
+// weights): m = 2 on 4096 x 14336 gs32 16.5 against 18.5 us, on 8192 x 28672
+// gs128 45.3 against 53.3 us; but 4096 x 14336 gs64 m = 2 16.5 against 14.6
+// us, and m = 3 or 4 slower on every shape tried (up to 20.6 against 14.7 us):
+// the dot products of several rows cost more vector work per code than the
+// stream hides.  So two rows, where the small-m kernel is weakest: group size
+// 32 (a rescale every 32 codes) or rows longer than 16384.
+bool gemv_rows_lds_supported(uint32_t K, uint32_t gs, uint32_t m) {
+  return m == 2u && K > 4096u && K % 1024u == 0 && (uint64_t)m * K <= kRowsLdsMaxMK && (gs == 32u || K > 16384u);
+}
+
+namespace {
+
+template <int MR>
+hipError_t launch_rows_lds_cfg(const WeightView &w, const uint16_t *X, uint16_t *Y, hipStream_t stream) {
+  static bool configured = false;
+  auto kern = k_gemv_rows_lds<MR>;
+  hipError_t e = raise_lds_cap(kern, configured);
+  if (e != hipSuccess) return e;
+  uint32_t blocks = (uint32_t)device_cu_count();
+  const uint32_t need = (w.N + 15u) / 16u;  // no workgroup without rows
+  if (blocks > need) blocks = need;
+  const size_t lds = (size_t)MR * w.K * 2u + (size_t)MR * (w.K / 16u) * 4u;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(1024), lds, stream, reinterpret_cast<const uint8_t *>(w.packed),
+                     w.scales, w.biases, X, Y, w.N, w.K, (uint32_t)__builtin_ctz(w.gs));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_rows_lds(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m,
+                                hipStream_t stream) {
+  if (!gemv_rows_lds_supported(w.K, w.gs, m)) return hipErrorInvalidValue;
+  return launch_rows_lds_cfg<2>(w, X, Y, stream);
 }
 
 hipError_t launch_gemv_multi(const WeightView *w, uint16_t *const *y, uint32_t count, const uint16_t *x,

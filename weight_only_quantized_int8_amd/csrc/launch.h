@@ -29,6 +29,11 @@ enum GemvEpilogue { kEpiNone = 0, kEpiSiluGate = 1, kEpiSiluGateResid = 2 };
 // 1024): the register-resident gemv with several rows (gemv.hip).
 bool gemv_rows_supported(uint32_t K, uint32_t m);
 hipError_t launch_gemv_rows(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream);
+// gemm with m = 2 rows on in_features above 4096 (a multiple of 1024, up to
+// 32768) where the small-m kernel is weakest (group size 32, or in_features
+// above 16384): the same arithmetic with X's rows in LDS.
+bool gemv_rows_lds_supported(uint32_t K, uint32_t gs, uint32_t m);
+hipError_t launch_gemv_rows_lds(const WeightView &w, const uint16_t *X, uint16_t *Y, uint32_t m, hipStream_t stream);
 hipError_t launch_gemv(const WeightView &w, GemvEpilogue epi, const uint16_t *x_or_gate,
                        const uint16_t *up, const uint16_t *x_resid, uint16_t *y, hipStream_t stream);
 
