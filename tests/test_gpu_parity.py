@@ -302,6 +302,9 @@ def test_gemm_small_batch_decode(m, N, K, gs):
     (4, 300, 14336, 32),    # 16-wave workgroups, long scale/bias rows
     (16, 520, 12288, 128),
     (3, 64, 131072, 32),    # scale/bias rows too long to stage: routed to the tiled kernel
+    (4, 1024, 20480, 32),   # 16 waves with 8 staged X rows (long gs32 scale/bias rows)
+    (8, 77, 12288, 32),     # the same, ragged rows, m at the 8-row limit
+    (9, 77, 12288, 32),     # one row more: the 8-wave shape
 ])
 def test_gemm_small_m_ragged(m, N, K, gs):
     log(f"gemm ragged m={m} N={N} K={K} gs={gs}")
