@@ -54,6 +54,8 @@ def upload(codes, scale, fmt, bs, single=2.5e-4):
     (1000, 3072, 128),     # register-resident form, three segments
     (600, 2048, 64),       # two segments, several row blocks per wave
     (65, 1024, 128),       # one segment, ragged rows
+    (40, 20000, 64),       # two K-tiles, the last segment partial, block scales loaded per item
+    (3000, 8192, 512),     # LDS form with one row at a time, several row blocks
 ])
 def test_fp8_gemv_matches_oracle(fmt, N, K, bs):
     log(f"fp8_gemv {fmt} N={N} K={K} bs={bs}")

@@ -38,8 +38,6 @@ constexpr uint32_t kFp8TileRunsMax = 1024;  // 16384 activations per LDS tile
 constexpr int kFp8LoadsPerBlock = 4;        // 1 KiB wave loads per pipeline block
 constexpr uint32_t kFp8MaxRowsPerWave = 16;
 constexpr size_t kFp8LdsPerCu = 156 * 1024;
-constexpr uint32_t kFp8MinBlock = 64;  // smallest block size: 2 row blocks x 16384/64 k-blocks per tile
-constexpr int kSbkPerLane = (int)(2u * (kFp8TileRunsMax * 16u / kFp8MinBlock) / 64u);
 
 enum Fp8Scale { kSfRow = 0, kSfBlockBf16 = 1, kSfBlockF32 = 2 };
 
@@ -77,9 +75,11 @@ __device__ __forceinline__ float sum_lane63(float v) {
   return v;
 }
 
-template <int U, int RP>
+template <int U, int RP, int SF = 0>
 struct Fp8Block {
   u32x4 q[U][RP];
+  // block scales: the entry of each item's lane (its row block, its run's k-block)
+  std::conditional_t<SF == 1, uint16_t, uint32_t> s[SF != 0 ? U : 1][SF != 0 ? RP : 1];
 };
 
 struct Fp8Cfg {
@@ -91,15 +91,11 @@ struct Fp8Cfg {
   bool tail;          // k not a multiple of 1024
 };
 
-// k-blocks of one tile, and the LDS bytes of one workgroup:
+// The LDS bytes of one workgroup:
 //   act  [NSEG][4][64] float4   activations of lane l's 16 codes in segment s
-//   sbk  [W][2][TB] float       each wave's block scales (two row blocks)
 //   part [W][max_rows] float    row partials across K-tiles
-__host__ __device__ inline uint32_t tile_blocks(uint32_t ct, uint32_t bs_log2) { return ((ct << 4) + (1u << bs_log2) - 1u) >> bs_log2; }
-size_t fp8_lds_bytes(const Fp8Cfg &c, bool block, uint32_t bs_log2) {
-  return (size_t)c.ct * 64u + (block ? (size_t)c.waves * 2u * tile_blocks(c.ct, bs_log2) * 4u : 0u) +
-         (size_t)c.waves * c.max_rows * 4u;
-}
+// (block scales are loaded with the codes: each item's lane needs one entry)
+size_t fp8_lds_bytes(const Fp8Cfg &c) { return (size_t)c.ct * 64u + (size_t)c.waves * c.max_rows * 4u; }
 
 template <int SF, int W, int RP, int U, bool TAIL>
 __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__ codes, const void *__restrict__ scale,
@@ -112,10 +108,8 @@ __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__
   extern __shared__ float4 lds4[];
   const uint32_t CT = tile_runs;
   const uint32_t NSEG = CT >> 6;
-  const uint32_t TB = tile_blocks(CT, bs_log2);
   float4 *act = lds4;
-  float *sbk_all = reinterpret_cast<float *>(lds4 + NSEG * 256);
-  float *part_all = sbk_all + (kBlock ? W * 2u * TB : 0u);
+  float *part_all = reinterpret_cast<float *>(lds4 + NSEG * 256);
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
@@ -129,21 +123,21 @@ __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__
   const uint32_t cpr = K >> 4;
   const uint32_t KB = (K + (1u << bs_log2) - 1u) >> bs_log2;  // scale blocks along k
   const uint32_t NB = (N + (1u << bs_log2) - 1u) >> bs_log2;  // and along n
-  const uint32_t rb0 = rbeg >> bs_log2;
+  constexpr uint32_t kEl = SF == kSfBlockBf16 ? 2u : 4u;  // block scale entry bytes
 
   const auto rw = make_rsrc(codes + (size_t)rbeg * K, nr * K);
   const auto rx = make_rsrc(xg, K * 2u);
-  float *sbk = sbk_all + wave * 2u * TB;
+  const auto rsc = make_rsrc(scale, kBlock ? NB * KB * kEl : 0u);
   float *part = part_all + wave * max_rows;
 
   const uint32_t vo_w = lane << 4;
   const uint32_t v_act = lane << 4;
-  const uint32_t v_kb = kBlock ? (((lane << 4) >> bs_log2) << 2) : 0u;  // this lane's k-block in a segment, bytes
+  const uint32_t v_kb = kBlock ? (((lane << 4) >> bs_log2) * kEl) : 0u;  // this lane's k-block in a segment, bytes
 
   float acc[RP];
 #pragma unroll
   for (int r = 0; r < RP; ++r) acc[r] = 0.f;
-  Fp8Block<U, RP> A, B;
+  Fp8Block<U, RP, SF> A, B;
 
   for (uint32_t t0 = 0; t0 < cpr; t0 += CT) {
     const uint32_t ct = (cpr - t0) < CT ? (cpr - t0) : CT;
@@ -153,49 +147,57 @@ __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__
     const uint32_t nblk = (nitems + U - 1) / U;
     const uint32_t last_lanes = ct - ((nseg - 1u) << 6);
     const uint32_t vo_w_last = TAIL && lane >= last_lanes ? kOutOfRange : vo_w;
-    // lanes past the end of the last segment read a staged (finite) scale
-    const uint32_t v_kb_last = TAIL && lane >= last_lanes ? 0u : v_kb;
+    // lanes past the end of the last segment load no scale (their codes are zero)
+    const uint32_t v_kb_last = TAIL && lane >= last_lanes ? kOutOfRange : v_kb;
     const uint32_t grp_skip = RP * K - (nseg << 10);
     const uint32_t last_off = (nr ? nr - 1u : 0u) * K + (t0 << 4) + ((nseg - 1u) << 10);
     const uint32_t kb0 = (t0 << 4) >> bs_log2;
     const uint32_t seg_kb = kBlock ? (1024u >> bs_log2) : 0u;  // k-blocks per segment
 
     uint32_t i_off = t0 << 4, i_seg = 0, i_grp = 0;
-    auto issue = [&](Fp8Block<U, RP> &blk) {
+    auto issue = [&](Fp8Block<U, RP, SF> &blk) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        uint32_t vw = vo_w;
-        if constexpr (TAIL) vw = (i_seg == nseg - 1u) ? vo_w_last : vo_w;
+        uint32_t vw = vo_w, vk = v_kb;
+        if constexpr (TAIL) {
+          vw = (i_seg == nseg - 1u) ? vo_w_last : vo_w;
+          vk = (i_seg == nseg - 1u) ? v_kb_last : v_kb;
+        }
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
           const bool live = i_grp < ngrp && i_grp * RP + r < nr;
           const uint32_t sw = uni(live ? i_off + r * K : last_off);
           const uint32_t vwr = live ? vw : vo_w_last;
           blk.q[u][r] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vwr, (int)sw, kAuxNontemporal);
+          if constexpr (kBlock) {
+            // the entry of (row block, k-block of the lane's run); past the
+            // wave's rows, the last row's (any finite value: not used)
+            const uint32_t row = rbeg + (live ? i_grp * RP + r : (nr ? nr - 1u : 0u));
+            const uint32_t ss = uni(((row >> bs_log2) * KB + kb0 + i_seg * seg_kb) * kEl);
+            if constexpr (SF == kSfBlockBf16)
+              blk.s[u][r] = __builtin_amdgcn_raw_buffer_load_b16(rsc, (int)vk, (int)ss, 0);
+            else
+              blk.s[u][r] = __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)vk, (int)ss, 0);
+          }
         }
         i_off += 1024u;
         if (++i_seg == nseg) { i_seg = 0; ++i_grp; i_off += grp_skip; }
       }
     };
     uint32_t c_grp = 0, c_seg = 0;
-    auto consume = [&](const Fp8Block<U, RP> &blk) {
+    auto consume = [&](const Fp8Block<U, RP, SF> &blk) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (c_grp < ngrp) {
           const float4 *ap = reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(act) +
                                                               uni(c_seg << 12) + v_act);
           const float4 a0 = ap[0], a1 = ap[64], a2 = ap[128], a3 = ap[192];
-          uint32_t vk = v_kb;
-          if constexpr (TAIL) vk = (c_seg == nseg - 1u) ? v_kb_last : v_kb;
 #pragma unroll
           for (int r = 0; r < RP; ++r) {
             const float p = fp8_run_dot(blk.q[u][r], a0, a1, a2, a3);
             if constexpr (kBlock) {
-              const uint32_t row = c_grp * RP + r;
-              const uint32_t rs = row < nr ? row : 0u;
-              const uint32_t rbi = ((rbeg + rs) >> bs_log2) - rb0;
-              const float s = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(sbk) +
-                                                               uni((rbi * TB + c_seg * seg_kb) << 2) + vk);
+              const float s = SF == kSfBlockBf16 ? bf16_bits_to_f32((uint16_t)blk.s[u][r])
+                                                 : __uint_as_float((uint32_t)blk.s[u][r]);
               acc[r] = __builtin_fmaf(s, p, acc[r]);
             } else {
               acc[r] += p;
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__
       }
     };
 
-    // 1. activation loads, the first weight block and the tile's block scales
+    // 1. activation loads, then the first weight block
     u32x4 xv[kStage][2];
 #pragma unroll
     for (int s = 0; s < kStage; ++s) {
@@ -233,23 +235,6 @@ __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__
       const uint32_t off = e < ct ? (t0 + e) * 32u : kOutOfRange;
       xv[s][0] = buf_load_b128(rx, off);
       xv[s][1] = buf_load_b128(rx, off + 16u);
-    }
-    // this wave's block scales: row blocks rb0 and rb0 + 1 (a wave owns at
-    // most 16 <= BS rows), k-blocks kb0 .. kb0 + TB - 1; missing ones are 0
-    float sv[kBlock ? kSbkPerLane : 1];
-    if constexpr (kBlock) {
-#pragma unroll
-      for (int j = 0; j < kSbkPerLane; ++j) {
-        const uint32_t e = lane + 64u * j;
-        const uint32_t rbi = e >= TB ? 1u : 0u;
-        const uint32_t rb = rb0 + rbi, kb = kb0 + e - rbi * TB;
-        sv[j] = 0.f;
-        if (e < 2u * TB && rb < NB && kb < KB) {
-          const size_t idx = (size_t)rb * KB + kb;
-          sv[j] = SF == kSfBlockBf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(scale)[idx])
-                                     : reinterpret_cast<const float *>(scale)[idx];
-        }
-      }
     }
     // the first weight block goes out after the small loads and
     // unconditionally, so that waiting for them never waits for it
@@ -269,13 +254,6 @@ __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__
                                     bf16_hi(wv[2 * f + 1]));
       }
     }
-    if constexpr (kBlock) {
-#pragma unroll
-      for (int j = 0; j < kSbkPerLane; ++j) {
-        const uint32_t e = lane + 64u * j;
-        if (e < 2u * TB) sbk[e] = sv[j];
-      }
-    }
     __syncthreads();
     // 3. two-stage pipeline in a loop with a single exit, two blocks per
     //    iteration and the rest after it (an exit after every block made the
@@ -283,7 +261,7 @@ __global__ __launch_bounds__(64 * W) void k_fp8_gemv(const uint8_t *__restrict__
     //    each consume only the other block's U RP loads may be in flight,
     //    said explicitly because a consume past the wave's rows waits for
     //    nothing
-    constexpr int kBlk = U * RP;
+    constexpr int kBlk = (kBlock ? 2 : 1) * U * RP;  // codes (and block scales) of U RP items
     uint32_t b = 0;
     for (; b + 2u < nblk; b += 2u) {
       issue(B);
@@ -453,7 +431,7 @@ hipError_t launch_fp8_cfg(const Fp8Cfg &c, const uint8_t *codes, const void *sca
   auto kern = k_fp8_gemv<SF, W, RP, kFp8LoadsPerBlock / RP, TAIL>;
   hipError_t e = lds_cap(kern, configured);
   if (e != hipSuccess) return e;
-  const size_t lds = fp8_lds_bytes(c, SF != kSfRow, bs_log2);
+  const size_t lds = fp8_lds_bytes(c);
   hipLaunchKernelGGL(kern, dim3(c.blocks), dim3(64 * W), lds, stream, codes, scale, single, x, y, N, K, bs_log2,
                      c.ct, c.max_rows);
   return hipGetLastError();
@@ -498,7 +476,7 @@ Fp8Cfg choose_fp8_cfg(uint32_t N, uint32_t K, bool block, uint32_t bs_log2) {
   const size_t budget = kFp8LdsPerCu / per_cu;
   for (uint32_t ntiles = (cpr + kFp8TileRunsMax - 1) / kFp8TileRunsMax;; ++ntiles) {
     c.ct = ((cpr + ntiles - 1) / ntiles + 63u) / 64u * 64u;
-    if (fp8_lds_bytes(c, block, bs_log2) <= budget || c.ct == 64u) break;
+    if (fp8_lds_bytes(c) <= budget || c.ct == 64u) break;
   }
   c.tail = (cpr % 64u) != 0;
   return c;
