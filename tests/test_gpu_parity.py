@@ -478,6 +478,28 @@ def test_gemm_prefill_full_size_all_rows(m, N, K):
     assert_close(Yb, Y_ref, A, f"gemm m={m} {N}x{K}")
 
 
+@pytest.mark.parametrize("m,N,K,gs", [
+    (2048, 14336, 4096, 64),  # 3.5 rounds of 256 x 128 tiles: the last 16 column tiles as half-height tiles
+    (1000, 9000, 1024, 64),   # ragged rows, 28 tiles past one round, ragged last column tile
+    (700, 12000, 1024, 128),  # gs 128
+])
+def test_gemm_prefill_column_tail(m, N, K, gs):
+    """int8_gemm without a workspace on grids whose 256 x 128 tiles leave a
+    last round at most half full: that round's column tiles run as
+    half-height tiles.  Every output against the oracle; a repeat call
+    bit-identical."""
+    log(f"gemm prefill column tail m={m} N={N} K={K} gs={gs}")
+    w, rng = make_weight(3_700 + m + N + gs, N, K, gs)
+    X = synth.gen_act(rng, (m, K))
+    W = upload(w)
+    Xd = bits_to_dev(X)
+    Yb = dev_to_bits(W.gemm(Xd, split_k=False))
+    Yb2 = dev_to_bits(W.gemm(Xd, split_k=False))
+    Y_ref, A = oracle.gemm(w.packed, w.scales, w.biases, gs, X)
+    assert_close(Yb, Y_ref, A, f"gemm m={m} {N}x{K} gs{gs}")
+    assert np.array_equal(Yb, Yb2), "repeated call differs"
+
+
 # A grid with too few tiles splits K over several work items per tile (the
 # workspace form, int8_gemm_ws, which Int8Weight.gemm uses when the call
 # needs one): every output against the oracle, a repeat call bit-identical,
