@@ -109,3 +109,26 @@ def test_traffic_record_needs_one_kernel_and_one_calibration_copy(tmp_path, monk
     _counter_csv(write, [("k_other", 1, 5.0)])
     with pytest.raises(SystemExit):
         bench.write_traffic_record("quantize", str(fetch), str(write))
+
+
+def test_traffic_record_skips_other_copies_with_the_calibration_grid(tmp_path, monkeypatch):
+    # a target whose rotated buffers are cloned by the same copy kernel, with
+    # the same grid size as the 256 MiB calibration copy: only the calibration
+    # dispatches (about 128 MiB read and 256 MiB written in the counters'
+    # units) set the factors, however many smaller copies share the key
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "traffic_file", lambda name: str(out))
+    kern = "void int8w::(anonymous namespace)::k_fp8_gemv<1, 8, 1, 4, false>(unsigned char const*)"
+    copy = "__amd_rocclr_copyBuffer"
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    clones_f = [(copy, 4096, 28672.0)] * 20   # 56 MiB clones: half read ...
+    clones_w = [(copy, 4096, 57344.0)] * 20   # ... all written
+    _counter_csv(fetch, [(kern, 9, 28941.0)] * 3 + clones_f + [(copy, 4096, 131072.0)] * 5)
+    _counter_csv(write, [(kern, 9, 16.0)] * 3 + clones_w + [(copy, 4096, 262144.0)] * 5)
+    bench.write_traffic_record("fp8_block_4096x14336", str(fetch), str(write))
+    rec = json.loads(out.read_text())
+    assert rec["fetch_factor"] == pytest.approx(2.0)
+    assert rec["write_factor"] == pytest.approx(1.0)
+    assert rec["calibration_fetch_size_kib"] == 131072.0
+    assert rec["calibration_write_size_kib"] == 262144.0
+    assert rec["hbm_bytes_per_launch"] == round(28941 * 1024 * 2 + 16 * 1024)
