@@ -338,9 +338,10 @@ class QuantizeTarget(Target):
 
 
 class GemmTarget(Target):
-    def __init__(self, name, m, N, K, gs, kernel, iters):
+    def __init__(self, name, m, N, K, gs, kernel, iters, source=None):
         fl = 2 * m * N * K
-        super().__init__(name, kernel, _src("gemm_prefill.hip" if m > 16 else "gemm_smallm.hip"), iters,
+        source = source or ("gemm_prefill.hip" if m > 16 else "gemm_smallm.hip")
+        super().__init__(name, kernel, _src(source), iters,
                          bytes_=gemm_bytes(N, K, gs, m), flops=fl, note=f"gemm m={m} {N}x{K} gs{gs}")
         self.m, self.N, self.K, self.gs = m, N, K, gs
 
@@ -430,6 +431,7 @@ TARGETS = {t.name: t for t in [
     DequantTarget(),
     QuantizeTarget(),
     Fp8Target("fp8_block_4096x14336", 4096, 14336),
+    GemmTarget("rows2_70b", 2, 8192, 28672, 128, "k_gemv_rows_lds", 30, source="gemv.hip"),
     GemmTarget("smallm16", 16, 4096, 14336, 64, "k_gemm_smallm", 30),
     GemmTarget("prefill512", 512, 4096, 14336, 64, "k_gemm_prefill", 10),
     GemmTarget("prefill2048", 2048, 14336, 4096, 64, "k_gemm_prefill", 10),
